@@ -1,0 +1,478 @@
+"""Oracle: a plain, slow, CPU reference of the packed KV cache and its decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import or run this module.  The product path (the HIP
+library and its Python binding) never calls it, and it shares no code with the
+product: the two meet only through the synthetic-input generator in
+``kvq_synth`` and through the packed layouts documented in ``include/kvq.h``.
+
+Sources (cited by short name below):
+  [GEOM] "The KV cache has a geometry problem, not a bits problem" (unite.ai)
+  [KIVI] "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+         (Telegram post on tgoop.com, sections "Method" and "Experiments")
+  [KVQ]  "KVQuant: Towards 10 Million Context Length LLM Inference with KV
+         Cache Quantization" (paper review on nubint.ai: abstract items (i)-(iv),
+         "Proposed method", results table)
+  [AXIS] "Why KV cache quantization fails without axis-specific geometry"
+         (dothoosh.com; restates [GEOM])
+
+Precision: the quantizer is float32 (IEEE round-to-nearest-even, one rounding
+per operation, no fused multiply-add) because codes and metadata must be
+bit-exact against the device; numpy ufuncs apply exactly one rounding per
+operation.  Attention is float64.  fp16 values travel as uint16 bit patterns.
+
+Parity pins for every function live in tests/test_oracle_*.py.  The one part
+with no pin is the choice of the nuq code book itself (an input here): "parity
+unpinned" for whether it resembles KVQuant's learned datatype.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 32
+
+
+# --------------------------------------------------------------------------
+# fp16 <-> fp32 (IEEE binary16; numpy's conversion rounds to nearest even and
+# keeps subnormals)
+# --------------------------------------------------------------------------
+def f16_to_f32(bits) -> np.ndarray:
+    """Exact widening of fp16 bit patterns to float32."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_bits(x) -> np.ndarray:
+    """float32 -> fp16 bit pattern, round to nearest even."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# O1: uniform asymmetric B-bit quantizer on groups ([GEOM] "Quantization error
+# in practice": the group minimum is the zero point, the step is the range
+# divided by 2^B - 1, each element goes to the nearest step; [KIVI]
+# "Experiments": group 32 with a floating-point zero point).
+# --------------------------------------------------------------------------
+def uniform_quantize_groups(x_bits: np.ndarray, bits: int):
+    """Quantize groups that run along the LAST axis of ``x_bits`` (fp16 bits).
+
+    Returns (codes uint8 same shape, scale fp16 bits, min fp16 bits), the
+    metadata with the group axis removed.
+
+    Readings: rounding is half-to-even; the code is (x - min) times the
+    reciprocal of the stored fp16 scale (one reciprocal per group); a zero
+    scale gives all-zero codes; -0 is stored as +0.
+    """
+    x = f16_to_f32(x_bits)
+    levels = np.float32(2 ** bits - 1)
+    mn = x.min(axis=-1) + np.float32(0.0)     # + 0 turns -0 into +0
+    mx = x.max(axis=-1) + np.float32(0.0)
+    min_h = f32_to_f16_bits(mn)                # exact: mn is an fp16 value
+    scale_h = f32_to_f16_bits((mx - mn) / levels)
+    s = f16_to_f32(scale_h)
+    with np.errstate(divide="ignore"):
+        inv = np.where(s == 0, np.float32(0.0), np.float32(1.0) / s).astype(np.float32)
+    q = np.rint((x - mn[..., None]) * inv[..., None])
+    q = np.clip(q, np.float32(0.0), levels)
+    q = np.where(s[..., None] == 0, np.float32(0.0), q)
+    return q.astype(np.uint8), scale_h, min_h
+
+
+def uniform_dequant(codes: np.ndarray, scale_h: np.ndarray, min_h: np.ndarray) -> np.ndarray:
+    """x_hat = code * scale + min, two float32 roundings (metadata broadcast on the last axis)."""
+    s = f16_to_f32(scale_h)[..., None]
+    m = f16_to_f32(min_h)[..., None]
+    return codes.astype(np.float32) * s + m
+
+
+# --------------------------------------------------------------------------
+# O2: grouping axes.  Keys per channel: a group is one channel over 32
+# consecutive tokens ([GEOM] "Keys: outliers in fixed channels"; [KIVI]
+# "Method").  Values per token: a group is 32 consecutive channels of one token
+# ([GEOM] "Values: where intuition breaks").
+# --------------------------------------------------------------------------
+def quantize_keys_per_channel(k_bits: np.ndarray, bits: int):
+    """k_bits [..., N, D] (N % 32 == 0) -> codes [..., N, D], scale/min [..., N/32, D]."""
+    *lead, n, d = k_bits.shape
+    assert n % GROUP == 0
+    blk = k_bits.reshape(*lead, n // GROUP, GROUP, d)
+    blk = np.swapaxes(blk, -1, -2)                         # [..., nb, D, 32]
+    c, s, m = uniform_quantize_groups(blk, bits)
+    c = np.swapaxes(c, -1, -2).reshape(*lead, n, d)
+    return c, s, m
+
+
+def quantize_values_per_token(v_bits: np.ndarray, bits: int):
+    """v_bits [..., N, D] (D % 32 == 0) -> codes [..., N, D], scale/min [..., N, D/32]."""
+    *lead, n, d = v_bits.shape
+    assert d % GROUP == 0
+    grp = v_bits.reshape(*lead, n, d // GROUP, GROUP)
+    c, s, m = uniform_quantize_groups(grp, bits)
+    return c.reshape(*lead, n, d), s, m
+
+
+def quantize_keys_per_token(k_bits: np.ndarray, bits: int):
+    """The swapped axis for keys (ablation only): groups of 32 channels per token."""
+    return quantize_values_per_token(k_bits, bits)
+
+
+def quantize_values_per_channel(v_bits: np.ndarray, bits: int):
+    """The swapped axis for values (ablation only): groups of 32 tokens per channel."""
+    return quantize_keys_per_channel(v_bits, bits)
+
+
+def dequant_keys_per_channel(codes, scale_h, min_h):
+    *lead, n, d = codes.shape
+    c = np.swapaxes(codes.reshape(*lead, n // GROUP, GROUP, d), -1, -2)
+    x = uniform_dequant(c, scale_h, min_h)
+    return np.swapaxes(x, -1, -2).reshape(*lead, n, d)
+
+
+def dequant_values_per_token(codes, scale_h, min_h):
+    *lead, n, d = codes.shape
+    c = codes.reshape(*lead, n, d // GROUP, GROUP)
+    return uniform_dequant(c, scale_h, min_h).reshape(*lead, n, d)
+
+
+# --------------------------------------------------------------------------
+# O3: packing into the library's layouts (the pages give bit budgets, not bit
+# layouts; the layouts are the ones include/kvq.h documents).  Codes are
+# packed least-significant-bit first into little-endian 32-bit words.
+# --------------------------------------------------------------------------
+def _pack_fields(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack the last axis (length L, L*bits % 32 == 0) into L*bits/32 uint32 words."""
+    per = 32 // bits
+    *lead, n = codes.shape
+    c = codes.astype(np.uint64).reshape(*lead, n // per, per)
+    sh = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
+    return np.bitwise_or.reduce(c << sh, axis=-1).astype(np.uint32)
+
+
+def _unpack_fields(words: np.ndarray, bits: int, n: int) -> np.ndarray:
+    per = 32 // bits
+    w = words.astype(np.uint64)[..., None]
+    sh = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
+    c = (w >> sh) & np.uint64((1 << bits) - 1)
+    return c.reshape(*words.shape[:-1], n).astype(np.uint8)
+
+
+def pack_meta(scale_h: np.ndarray, min_h: np.ndarray) -> np.ndarray:
+    """Metadata word: fp16 scale in bits 0..15, fp16 min in bits 16..31."""
+    return (scale_h.astype(np.uint32) | (min_h.astype(np.uint32) << np.uint32(16)))
+
+
+def unpack_meta(words: np.ndarray):
+    return (words & 0xFFFF).astype(np.uint16), (words >> 16).astype(np.uint16)
+
+
+def pack_k_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[..., N, D] -> [..., N/32, 32 tokens, D*bits/32 words]: token-major rows; channel d
+    of a token sits at bit (bits*d) % 32 of word (bits*d) // 32."""
+    *lead, n, d = codes.shape
+    w = _pack_fields(codes, bits)                          # [..., N, D*bits/32]
+    return w.reshape(*lead, n // GROUP, GROUP, d * bits // 32)
+
+
+def unpack_k_codes(words: np.ndarray, bits: int, d: int) -> np.ndarray:
+    *lead, nb, g, _ = words.shape
+    return _unpack_fields(words, bits, d).reshape(*lead, nb * g, d)
+
+
+def pack_v_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[..., N, D] -> [..., N/32, D, bits words]: channel-major within a block; token j of
+    the block sits at bit (bits*j) % 32 of word (bits*j) // 32 of its channel."""
+    *lead, n, d = codes.shape
+    blk = codes.reshape(*lead, n // GROUP, GROUP, d)
+    blk = np.swapaxes(blk, -1, -2)                         # [..., nb, D, 32]
+    return _pack_fields(blk, bits)                          # [..., nb, D, bits]
+
+
+def unpack_v_codes(words: np.ndarray, bits: int) -> np.ndarray:
+    *lead, nb, d, _ = words.shape
+    c = _unpack_fields(words, bits, GROUP)                 # [..., nb, D, 32]
+    return np.swapaxes(c, -1, -2).reshape(*lead, nb * GROUP, d)
+
+
+def pack_nuq3_k(codes: np.ndarray) -> np.ndarray:
+    """nuq3 key codes [..., N, D] -> [..., N/32, 32, 3*D/32 words]: per token, the low two
+    bits of every channel as in the 2-bit layout (D/16 words), then the high bit of
+    every channel, channel d at bit d % 32 of word D/16 + d // 32."""
+    lo = pack_k_codes(codes & 3, 2)
+    hi = pack_k_codes(codes >> 2, 1)
+    return np.concatenate([lo, hi], axis=-1)
+
+
+def unpack_nuq3_k(words: np.ndarray, d: int) -> np.ndarray:
+    nlo = d // 16
+    lo = unpack_k_codes(words[..., :nlo], 2, d)
+    hi = unpack_k_codes(words[..., nlo:], 1, d)
+    return (lo | (hi << 2)).astype(np.uint8)
+
+
+def pack_nuq3_v(codes: np.ndarray) -> np.ndarray:
+    """nuq3 value codes [..., N, D] -> [..., N/32, D, 3 words]: per channel, words 0-1 hold the
+    low two bits of the block's 32 tokens (2-bit layout) and word 2 their high bits."""
+    lo = pack_v_codes(codes & 3, 2)
+    hi = pack_v_codes(codes >> 2, 1)
+    return np.concatenate([lo, hi], axis=-1)
+
+
+def unpack_nuq3_v(words: np.ndarray) -> np.ndarray:
+    lo = unpack_v_codes(words[..., :2], 2)
+    hi = unpack_v_codes(words[..., 2:], 1)
+    return (lo | (hi << 2)).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Byte accounting ([KVQ] results table, KV-cache GB column).
+# --------------------------------------------------------------------------
+def kv_cache_bytes(layers: int, hidden: int, tokens: int, bits_per_elem: float,
+                   outlier_frac: float = 0.0, outlier_bits: int = 32) -> float:
+    """Bytes of K plus V for ``tokens`` tokens: 2 * layers * hidden * tokens elements at
+    ``bits_per_elem``, plus ``outlier_frac`` of the elements kept as sparse entries of
+    ``outlier_bits`` each (value and index; row pointers not counted)."""
+    elems = 2 * layers * hidden * tokens
+    return elems * bits_per_elem / 8.0 + elems * outlier_frac * outlier_bits / 8.0
+
+
+# --------------------------------------------------------------------------
+# O4: streaming cache with an fp16 residual window ([GEOM] "The systems tax";
+# [KIVI] "Method": keep up to R recent tokens in full precision and quantize
+# them as a group once enough have accumulated).  Reading: the flush is lazy
+# (it happens when a token arrives and the window is already full).
+# --------------------------------------------------------------------------
+class StreamingCache:
+    """Per-channel keys / per-token values, one window shared by K and V."""
+
+    def __init__(self, batch, heads, head_dim, k_bits, v_bits, residual_len=128):
+        assert residual_len % GROUP == 0
+        self.B, self.H, self.D = batch, heads, head_dim
+        self.kb, self.vb, self.R = k_bits, v_bits, residual_len
+        self.k_res = np.zeros((batch, heads, residual_len, head_dim), np.uint16)
+        self.v_res = np.zeros((batch, heads, residual_len, head_dim), np.uint16)
+        self.k_codes = np.zeros((batch, heads, 0, head_dim), np.uint8)
+        self.v_codes = np.zeros((batch, heads, 0, head_dim), np.uint8)
+        self.k_scale = np.zeros((batch, heads, 0, head_dim), np.uint16)
+        self.k_min = np.zeros((batch, heads, 0, head_dim), np.uint16)
+        self.v_scale = np.zeros((batch, heads, 0, head_dim // GROUP), np.uint16)
+        self.v_min = np.zeros((batch, heads, 0, head_dim // GROUP), np.uint16)
+        self.n_packed = 0
+        self.n_resid = 0
+
+    def _flush(self):
+        kc, ks, km = quantize_keys_per_channel(self.k_res, self.kb)
+        vc, vs, vm = quantize_values_per_token(self.v_res, self.vb)
+        self.k_codes = np.concatenate([self.k_codes, kc], axis=2)
+        self.v_codes = np.concatenate([self.v_codes, vc], axis=2)
+        self.k_scale = np.concatenate([self.k_scale, ks], axis=2)
+        self.k_min = np.concatenate([self.k_min, km], axis=2)
+        self.v_scale = np.concatenate([self.v_scale, vs], axis=2)
+        self.v_min = np.concatenate([self.v_min, vm], axis=2)
+        self.n_packed += self.R
+        self.n_resid = 0
+
+    def append(self, k_new: np.ndarray, v_new: np.ndarray):
+        """k_new, v_new: fp16 bits [B][H][D] for one new token."""
+        if self.R == 0:
+            raise ValueError("streaming needs a residual window")
+        if self.n_resid == self.R:
+            self._flush()
+        self.k_res[:, :, self.n_resid] = k_new
+        self.v_res[:, :, self.n_resid] = v_new
+        self.n_resid += 1
+
+    def dequant(self):
+        """(K_hat, V_hat) float32 [B][H][N + r][D]: packed part dequantized, window as fp16."""
+        kd = dequant_keys_per_channel(self.k_codes, self.k_scale, self.k_min)
+        vd = dequant_values_per_token(self.v_codes, self.v_scale, self.v_min)
+        r = self.n_resid
+        kd = np.concatenate([kd, f16_to_f32(self.k_res[:, :, :r])], axis=2)
+        vd = np.concatenate([vd, f16_to_f32(self.v_res[:, :, :r])], axis=2)
+        return kd, vd
+
+
+# --------------------------------------------------------------------------
+# O5/O6: non-uniform datatype with per-vector dense-and-sparse outliers
+# ([KVQ] abstract (iii) non-uniform datatype nuqX, (iv) per-vector
+# dense-and-sparse quantization; "Proposed method").
+# Readings: the code book is given in level units [0, 2^B - 1] with the same
+# (min, scale) normalization as the uniform quantizer, so the identity code
+# book reproduces the uniform quantizer; each element goes to the nearest code
+# book level (ties to the even index); outliers are the ceil(n * bp / 10000)
+# largest magnitudes of the vector (ties: lower index first), kept exactly and
+# excluded from the min/max; codes are still stored at outlier positions.
+# --------------------------------------------------------------------------
+def outlier_count(n: int, bp: int) -> int:
+    """ceil(n * bp / 10000) in integer arithmetic."""
+    return (n * bp + 9999) // 10000
+
+
+def select_outliers(x_bits: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest |x| of a 1-D vector of fp16 bits (ties: lower index first)."""
+    if k <= 0:
+        return np.zeros(0, dtype=np.int64)
+    mag = (np.asarray(x_bits, dtype=np.uint16) & 0x7FFF).astype(np.int64)
+    order = np.argsort(-mag, kind="stable")
+    return np.sort(order[:k])
+
+
+def nuq_code(xn: np.ndarray, lut_f32: np.ndarray) -> np.ndarray:
+    """Index of the nearest code-book level for normalized values (ties: even index)."""
+    mid = (lut_f32[:-1] + lut_f32[1:]) * np.float32(0.5)
+    c = (xn[..., None] > mid).sum(axis=-1)
+    cc = np.minimum(c, len(mid) - 1)
+    tie = (c < len(mid)) & (xn == mid[cc]) & (c % 2 == 1)
+    return (c + tie).astype(np.uint8)
+
+
+def nuq_quantize_vector(x_bits: np.ndarray, lut_bits: np.ndarray, n_outliers: int = 0):
+    """One vector (fp16 bits, 1-D).  Returns (codes, scale_h, min_h, outlier_idx, x_hat)."""
+    lut = f16_to_f32(lut_bits)
+    bits = int(round(math.log2(len(lut))))
+    x = f16_to_f32(x_bits)
+    out_idx = select_outliers(x_bits, n_outliers)
+    dense = np.ones(x.shape[0], dtype=bool)
+    dense[out_idx] = False
+    if dense.any():
+        mn = x[dense].min() + np.float32(0.0)
+        mx = x[dense].max() + np.float32(0.0)
+    else:
+        mn = mx = np.float32(0.0)
+    min_h = f32_to_f16_bits(mn)
+    scale_h = f32_to_f16_bits((mx - mn) / np.float32(2 ** bits - 1))
+    s = f16_to_f32(scale_h)
+    if s == 0:
+        codes = np.zeros(x.shape[0], dtype=np.uint8)
+    else:
+        inv = np.float32(1.0) / s
+        xn = (x - mn) * inv
+        codes = nuq_code(xn, lut)
+    xhat = lut[codes] * s + mn
+    xhat[out_idx] = x[out_idx]
+    return codes, scale_h, min_h, out_idx, xhat
+
+
+def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int):
+    """Keys of one head [N][D]: per channel over the whole context, with outliers.
+
+    Returns codes [N][D], scale/min [D], CSR (row_ptr int32 [N+1], entries uint32: column in
+    bits 0..15 and the fp16 value in bits 16..31, rows = tokens, columns ascending), and
+    the dequantized keys x_hat float32 [N][D] (pre-RoPE)."""
+    n, d = k_bits.shape
+    k = outlier_count(n, outlier_bp)
+    codes = np.zeros((n, d), np.uint8)
+    scale = np.zeros(d, np.uint16)
+    mins = np.zeros(d, np.uint16)
+    xhat = np.zeros((n, d), np.float32)
+    is_out = np.zeros((n, d), bool)
+    for ch in range(d):
+        c, s, m, oi, xh = nuq_quantize_vector(k_bits[:, ch], lut_bits, k)
+        codes[:, ch], scale[ch], mins[ch], xhat[:, ch] = c, s, m, xh
+        is_out[oi, ch] = True
+    counts = is_out.sum(axis=1)
+    row_ptr = np.zeros(n + 1, np.int32)
+    row_ptr[1:] = np.cumsum(counts)
+    tt, cc = np.nonzero(is_out)                   # row-major: tokens, then channels ascending
+    ent = cc.astype(np.uint32) | (k_bits[tt, cc].astype(np.uint32) << np.uint32(16))
+    return codes, scale, mins, row_ptr, ent.astype(np.uint32), xhat
+
+
+def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray):
+    """Values of one head [N][D]: per token over all D channels, no outliers.
+    Returns codes [N][D], scale/min [N], x_hat float32 [N][D]."""
+    n, d = v_bits.shape
+    codes = np.zeros((n, d), np.uint8)
+    scale = np.zeros(n, np.uint16)
+    mins = np.zeros(n, np.uint16)
+    lut = f16_to_f32(lut_bits)
+    x = f16_to_f32(v_bits)
+    mn = x.min(axis=1) + np.float32(0.0)
+    mx = x.max(axis=1) + np.float32(0.0)
+    mins[:] = f32_to_f16_bits(mn)
+    scale[:] = f32_to_f16_bits((mx - mn) / np.float32(len(lut) - 1))
+    s = f16_to_f32(scale)
+    with np.errstate(divide="ignore"):
+        inv = np.where(s == 0, np.float32(0.0), np.float32(1.0) / s).astype(np.float32)
+    xn = (x - mn[:, None]) * inv[:, None]
+    codes[:] = nuq_code(xn, lut)
+    codes[s == 0] = 0
+    xhat = lut[codes] * s[:, None] + mn[:, None]
+    return codes, scale, mins, xhat
+
+
+# --------------------------------------------------------------------------
+# O7: rotary position embedding applied after dequantization ([GEOM] "Rotary
+# embeddings complicate keys": quantize keys before the rotation and apply it
+# after; [KVQ] abstract (ii)).  Readings: interleaved pairs (2i, 2i+1),
+# frequency theta^(-2i/D), angle t * freq, all in float64.
+# --------------------------------------------------------------------------
+def rope_f64(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate x [..., T, D] (float64) at integer positions [T]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    i = np.arange(d // 2, dtype=np.float64)
+    freq = np.power(np.float64(theta), -2.0 * i / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+# --------------------------------------------------------------------------
+# O8: decode attention over the dequantized cache, float64 ([GEOM] "Why the KV
+# cache is a problem": every generated token reads the whole cache; the score,
+# softmax and weighted sum are textbook attention).  GQA: query head h reads kv
+# head h // (Hq / Hkv).
+# --------------------------------------------------------------------------
+def decode_attention_f64(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
+                         sm_scale: float) -> np.ndarray:
+    """q [B][Hq][D]; k_hat, v_hat [B][Hkv][T][D] (any float) -> out float32 [B][Hq][D]."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, hq, d = q.shape
+    hkv = k_hat.shape[1]
+    g = hq // hkv
+    out = np.zeros((bsz, hq, d), np.float64)
+    for b in range(bsz):
+        for h in range(hq):
+            kh = np.asarray(k_hat[b, h // g], dtype=np.float64)
+            vh = np.asarray(v_hat[b, h // g], dtype=np.float64)
+            if kh.shape[0] == 0:
+                continue
+            s = (kh @ q[b, h]) * sm_scale
+            p = np.exp(s - s.max())
+            out[b, h] = (p @ vh) / p.sum()
+    return out.astype(np.float32)
+
+
+def default_sm_scale(head_dim: int) -> float:
+    """1/sqrt(D) (textbook scaled dot-product attention; not on the pages)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+# --------------------------------------------------------------------------
+# Whole-cache helpers used by the tests (compositions of the functions above).
+# --------------------------------------------------------------------------
+def uniform_cache(k_bits, v_bits, k_b, v_b, n_packed, n_resid):
+    """One-shot cache for tokens [0, n_packed + n_resid): packed prefix and fp16 window.
+
+    k_bits/v_bits: fp16 bits [B][H][T][D] with T >= n_packed + n_resid.
+    Returns a dict of the packed buffers (library layouts) and the dequantized K/V."""
+    kp, vp = k_bits[:, :, :n_packed], v_bits[:, :, :n_packed]
+    kc, ks, km = quantize_keys_per_channel(kp, k_b)
+    vc, vs, vm = quantize_values_per_token(vp, v_b)
+    kd = dequant_keys_per_channel(kc, ks, km)
+    vd = dequant_values_per_token(vc, vs, vm)
+    kr = k_bits[:, :, n_packed:n_packed + n_resid]
+    vr = v_bits[:, :, n_packed:n_packed + n_resid]
+    return {
+        "k_codes": pack_k_codes(kc, k_b),
+        "k_meta": pack_meta(ks, km),
+        "v_codes": pack_v_codes(vc, v_b),
+        "v_meta": pack_meta(vs, vm),
+        "k_hat": np.concatenate([kd, f16_to_f32(kr)], axis=2),
+        "v_hat": np.concatenate([vd, f16_to_f32(vr)], axis=2),
+    }

@@ -1,0 +1,119 @@
+"""Pins of the oracle's non-uniform datatype and dense-and-sparse outliers (KVQuant
+review: abstract items (iii) and (iv), "Proposed method").
+
+- With the identity code book {0..7} the nuq3 quantizer is the uniform 3-bit
+  quantizer, bit for bit (the normalization reading).
+- Every element maps to the nearest code-book level (brute force).
+- Outliers: exactly k per vector, all at least as large in magnitude as every
+  dense entry, ties broken towards lower indices, kept exactly; none with bp = 0.
+"""
+import numpy as np
+import pytest
+
+import kvq_synth as S
+from oracle import kvq_oracle as O
+
+IDENT = np.arange(8).astype(np.float16).view(np.uint16)
+
+
+def _f16(x):
+    return np.asarray(x, dtype=np.float16).view(np.uint16)
+
+
+def test_outlier_count_rounds_up():
+    assert O.outlier_count(1048576, 100) == 10486
+    assert O.outlier_count(100, 100) == 1
+    assert O.outlier_count(101, 100) == 2
+    assert O.outlier_count(4096, 0) == 0
+    assert O.outlier_count(128, 100) == 2
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_identity_lut_equals_uniform_3bit(seed):
+    rng = np.random.default_rng(seed)
+    x = _f16(rng.standard_normal(512) * rng.uniform(0.1, 30))
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, IDENT, 0)
+    cu, su, mu = O.uniform_quantize_groups(x[None], 3)
+    assert np.array_equal(c, cu[0]) and s == su[0] and m == mu[0]
+    assert np.array_equal(xh, O.uniform_dequant(cu, su, mu)[0])
+    assert oi.size == 0
+
+
+def test_identity_lut_values_per_token():
+    v = S.gen_tensor(4, S.TID_V, 1, 1, 64, 128)[0, 0]
+    c, s, m, xh = O.nuq_quantize_values(v, IDENT)
+    cu, su, mu = O.uniform_quantize_groups(v, 3)
+    assert np.array_equal(c, cu) and np.array_equal(s, su) and np.array_equal(m, mu)
+
+
+def test_nearest_level_brute_force():
+    lut = S.nuq3_lut()
+    L = O.f16_to_f32(lut).astype(np.float64)
+    rng = np.random.default_rng(9)
+    x = _f16(rng.standard_normal(4000) * 2)
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, lut, 0)
+    sf, mf = float(O.f16_to_f32(s)), float(O.f16_to_f32(m))
+    xn = (O.f16_to_f32(x).astype(np.float64) - mf) / sf
+    d = np.abs(xn[:, None] - L[None, :])
+    best = d.argmin(1)
+    dc = d[np.arange(len(c)), c]
+    assert np.all((c == best) | (np.abs(dc - d.min(1)) <= 1e-5))
+    assert np.mean(c == best) > 0.999
+
+
+def test_ties_go_to_even_index():
+    lut = _f16([0, 1, 2, 3, 4, 5, 6, 7])
+    # min 0, max 7 -> scale 1; 2.5 is a tie between levels 2 and 3 -> 2; 3.5 -> 4
+    x = _f16([0, 7, 2.5, 3.5, 6.5, 0.5])
+    c, *_ = O.nuq_quantize_vector(x, lut, 0)
+    assert list(c[2:]) == [2, 4, 6, 0]
+
+
+def test_outliers_largest_magnitudes_ties_to_lower_index():
+    x = np.zeros(200)
+    x[:] = np.linspace(-1, 1, 200)
+    x[[3, 50, 120]] = [9.0, -9.0, 9.0]     # three equal magnitudes: tie
+    x[77] = -20.0
+    xb = _f16(x)
+    c, s, m, oi, xh = O.nuq_quantize_vector(xb, S.nuq3_lut(), 3)
+    assert list(oi) == [3, 50, 77]
+    assert np.array_equal(xh[oi], O.f16_to_f32(xb)[oi])
+
+
+@pytest.mark.parametrize("bp", [0, 100, 250])
+def test_outlier_invariants_keys(bp):
+    B, H, N, D = 1, 1, 640, 128
+    k = S.gen_tensor(12, S.TID_K, B, H, N, D, gains=S.key_gains(12, H, D, 3, 100.0))[0, 0]
+    lut = S.nuq3_lut()
+    codes, sc, mn, rp, ent, xh = O.nuq_quantize_keys(k, lut, bp)
+    kk = O.outlier_count(N, bp)
+    assert rp[0] == 0 and rp[-1] == D * kk and np.all(np.diff(rp) >= 0)
+    cols = (ent & 0xFFFF).astype(np.int64)
+    vals = (ent >> 16).astype(np.uint16)
+    rows = np.repeat(np.arange(N), np.diff(rp))
+    assert np.array_equal(vals, k[rows, cols])                  # exact fp16 values
+    for t in range(N):                                          # columns ascending per row
+        seg = cols[rp[t]:rp[t + 1]]
+        assert np.all(np.diff(seg) > 0)
+    mag = (k & 0x7FFF).astype(np.int64)
+    is_out = np.zeros((N, D), bool)
+    is_out[rows, cols] = True
+    for d in range(D):
+        assert is_out[:, d].sum() == kk
+        if kk:
+            assert mag[is_out[:, d], d].min() >= mag[~is_out[:, d], d].max()
+            # dense min/max exclude outliers
+            xd = O.f16_to_f32(k[~is_out[:, d], d])
+            assert O.f16_to_f32(mn[d]) == xd.min() + np.float32(0)
+    x = O.f16_to_f32(k)
+    assert np.array_equal(xh[is_out], x[is_out])
+    if bp == 0:
+        c0, s0, m0, _, xh0 = O.nuq_quantize_vector(k[:, 5], lut, 0)
+        assert np.array_equal(codes[:, 5], c0) and sc[5] == s0
+
+
+def test_all_outliers_degenerate():
+    x = _f16([1.0, -2.0, 3.0])
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, S.nuq3_lut(), 3)
+    assert s == 0 and m == 0 and not c.any()
+    assert np.array_equal(xh, O.f16_to_f32(x))
