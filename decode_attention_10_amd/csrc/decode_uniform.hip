@@ -1,0 +1,427 @@
+// Decode attention computed directly over the packed uniform cache.
+//
+// Every generated token reads the whole cache, so the step is bound by streaming
+// the packed codes and metadata from HBM ("The KV cache has a geometry problem",
+// section "Why the KV cache is a problem"; KIVI post, "Experiments": loading the
+// cache dominates long-context generation).  Scores are q . k_hat over the packed
+// tokens (dequantization fused) and over the fp16 window, then a softmax over all
+// of them and the p-weighted sum of v_hat.
+//
+// Algebra used to keep the inner loops to one multiply-add per code:
+//   q . k_hat_t = sum_d (q_d * scale_d) * code_td + sum_d q_d * min_d      (keys)
+//   sum_t p_t v_hat_td = sum_t (p_t * scale_tg) * code_td + sum_t p_t * min_tg
+// so a block needs one per-channel vector q*scale (keys) and one per-token
+// vector p*scale (values), staged in LDS, and the min terms are one reduction.
+//
+// Unpacking: a 2-bit (or 4-bit) field moved into the low mantissa bits of an fp16
+// half word is an fp16 subnormal of value code * 2^(pos - 24); one AND extracts two
+// such codes (both fp16 halves of a register), and v_fma_mix_f32 multiplies an fp16
+// half by an fp32 operand.  The power of two 2^(24 - pos) is folded into the staged
+// q*scale / p*scale values.  Products are exact; sums are fp32.
+//
+// Work split: a workgroup of 4 waves handles one (batch, kv head) and a range of
+// blocks (split-K over the context, as in flash-decoding); a wave streams one
+// 32-token block at a time (lane = token x channel half for keys, lane = channel
+// pair for values), with the next block's loads in flight.  The fp16 window is an
+// extra split.  Waves merge in LDS; splits merge in the same launch: the last
+// workgroup of a (batch, kv head) to finish (atomic ticket) combines the partial
+// (max, sum, output) triples and writes the output.
+#include "kvq_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kNegInf = -__builtin_inff();
+
+// Bit position of field j (within its 16-bit half, after the shift used to reach
+// it) for a word holding 32/B fields of B bits.
+__host__ __device__ constexpr int field_pos(int bits, int j) {
+  return bits == 2 ? (j < 5 ? 2 * j : j < 8 ? 2 * (j - 5) : j < 13 ? 2 * (j - 8) : 2 * (j - 13))
+                   : 4 * (j & 1);
+}
+// 2^(24 - pos): undoes the subnormal scaling of a field.
+__device__ __forceinline__ float field_scale(int bits, int j) {
+  return __builtin_bit_cast(float, (uint32_t)(127 + 24 - field_pos(bits, j)) << 23);
+}
+
+// acc += sum_j w_j * field_j(word), with w the 32/B weights of the word's fields.
+template <int B>
+__device__ __forceinline__ float dot_word(uint32_t w, const float* wt, float acc) {
+  if constexpr (B == 2) {
+    const uint32_t w10 = w >> 10;
+    uint32_t x;
+    x = w & 0x00030003u;   acc = fmaf(wt[0], lo_f16(x), acc);  acc = fmaf(wt[8], hi_f16(x), acc);
+    x = w & 0x000C000Cu;   acc = fmaf(wt[1], lo_f16(x), acc);  acc = fmaf(wt[9], hi_f16(x), acc);
+    x = w & 0x00300030u;   acc = fmaf(wt[2], lo_f16(x), acc);  acc = fmaf(wt[10], hi_f16(x), acc);
+    x = w & 0x00C000C0u;   acc = fmaf(wt[3], lo_f16(x), acc);  acc = fmaf(wt[11], hi_f16(x), acc);
+    x = w & 0x03000300u;   acc = fmaf(wt[4], lo_f16(x), acc);  acc = fmaf(wt[12], hi_f16(x), acc);
+    x = w10 & 0x00030003u; acc = fmaf(wt[5], lo_f16(x), acc);  acc = fmaf(wt[13], hi_f16(x), acc);
+    x = w10 & 0x000C000Cu; acc = fmaf(wt[6], lo_f16(x), acc);  acc = fmaf(wt[14], hi_f16(x), acc);
+    x = w10 & 0x00300030u; acc = fmaf(wt[7], lo_f16(x), acc);  acc = fmaf(wt[15], hi_f16(x), acc);
+  } else {
+    const uint32_t w8 = w >> 8;
+    uint32_t x;
+    x = w & 0x000F000Fu;  acc = fmaf(wt[0], lo_f16(x), acc);  acc = fmaf(wt[4], hi_f16(x), acc);
+    x = w & 0x00F000F0u;  acc = fmaf(wt[1], lo_f16(x), acc);  acc = fmaf(wt[5], hi_f16(x), acc);
+    x = w8 & 0x000F000Fu; acc = fmaf(wt[2], lo_f16(x), acc);  acc = fmaf(wt[6], hi_f16(x), acc);
+    x = w8 & 0x00F000F0u; acc = fmaf(wt[3], lo_f16(x), acc);  acc = fmaf(wt[7], hi_f16(x), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float sum32(float x) {   // over lane bits 0..4
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float max32(float x) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+template <int KB, int VB>
+struct BlockRegs {
+  uint32_t kc[kHeadDim * KB / 64];   // this lane's half of a token row
+  uint32_t km[2];                    // key meta of channels 2l, 2l+1
+  uint32_t vc[2 * VB];               // value rows of channels 2l, 2l+1
+  uint32_t vm[2];                    // value meta of token t, groups 2h, 2h+1
+};
+
+template <int KB, int VB>
+__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& r, const DecodeArgs& a,
+                                           int64_t blk, int lane) {
+  constexpr int WK = kHeadDim * KB / 32;
+  const int t = lane & 31, half = lane >> 5;
+  const uint4* kp = reinterpret_cast<const uint4*>(a.k_codes + blk * (kGroup * WK) +
+                                                   t * WK + half * (WK / 2));
+#pragma unroll
+  for (int i = 0; i < WK / 8; ++i) {
+    const uint4 u = kp[i];
+    r.kc[4 * i] = u.x; r.kc[4 * i + 1] = u.y; r.kc[4 * i + 2] = u.z; r.kc[4 * i + 3] = u.w;
+  }
+  const uint2 km = *reinterpret_cast<const uint2*>(a.k_meta + blk * kHeadDim + 2 * lane);
+  r.km[0] = km.x; r.km[1] = km.y;
+  const uint4* vp = reinterpret_cast<const uint4*>(a.v_codes + blk * (kHeadDim * VB) +
+                                                   2 * lane * VB);
+#pragma unroll
+  for (int i = 0; i < VB / 2; ++i) {
+    const uint4 u = vp[i];
+    r.vc[4 * i] = u.x; r.vc[4 * i + 1] = u.y; r.vc[4 * i + 2] = u.z; r.vc[4 * i + 3] = u.w;
+  }
+  const uint2 vm = *reinterpret_cast<const uint2*>(a.v_meta + (blk * kGroup + t) * 4 + 2 * half);
+  r.vm[0] = vm.x; r.vm[1] = vm.y;
+}
+
+template <int GQ>
+struct WaveState {
+  float m[GQ];        // running max (log2 domain), wave-uniform
+  float l[GQ];        // this lane's sum of p over its tokens
+  float o[GQ][2];     // output accumulators of channels 2l, 2l+1
+  float mv[GQ][2];    // sum_t p_t * min_tg for groups 2h, 2h+1 (token lanes)
+};
+
+// Online softmax update for one head; s is this lane's token score (log2 units).
+__device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
+  const float mb = max32(s);
+  const float mn = fmaxf(m, mb);
+  alpha = exp2f(m - mn);
+  const float p = exp2f(s - mn);
+  m = mn;
+  l = l * alpha + p;
+  return p;
+}
+
+template <int KB, int VB, int GQ>
+__device__ __forceinline__ void process_block(const BlockRegs<KB, VB>& r, WaveState<GQ>& st,
+                                              const uint32_t* qreg, float (*qsL)[kHeadDim],
+                                              float (*psL)[4][kGroup], float scale_log2,
+                                              int lane) {
+  constexpr int WK = kHeadDim * KB / 32;
+  constexpr int CPW = 32 / KB;
+  constexpr int TPW = 32 / VB;
+  const int t = lane & 31, half = lane >> 5;
+
+  // ---- keys: q*scale per channel into LDS, q.min reduced over the wave
+  const float ks0 = lo_f16(r.km[0]), kn0 = hi_f16(r.km[0]);
+  const float ks1 = lo_f16(r.km[1]), kn1 = hi_f16(r.km[1]);
+  const float f0 = field_scale(KB, (2 * lane) % CPW), f1 = field_scale(KB, (2 * lane + 1) % CPW);
+  float cmin[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const float q0 = lo_f16(qreg[j]), q1 = hi_f16(qreg[j]);
+    *reinterpret_cast<float2*>(&qsL[j][2 * lane]) = make_float2(q0 * ks0 * f0, q1 * ks1 * f1);
+    cmin[j] = q0 * kn0 + q1 * kn1;
+  }
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) cmin[j] = wave_sum(cmin[j]);
+
+  float s[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float acc = 0.f;
+#pragma unroll
+    for (int wi = 0; wi < WK / 2; ++wi) {
+      float wt[CPW];
+      const float4* qp = reinterpret_cast<const float4*>(&qsL[j][half * 64 + wi * CPW]);
+#pragma unroll
+      for (int k = 0; k < CPW / 4; ++k) {
+        const float4 v = qp[k];
+        wt[4 * k] = v.x; wt[4 * k + 1] = v.y; wt[4 * k + 2] = v.z; wt[4 * k + 3] = v.w;
+      }
+      acc = dot_word<KB>(r.kc[wi], wt, acc);
+    }
+    acc += __shfl_xor(acc, 32);
+    s[j] = (acc + cmin[j]) * scale_log2;
+  }
+
+  // ---- softmax
+  float p[GQ], alpha[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) p[j] = softmax_step(s[j], st.m[j], st.l[j], alpha[j]);
+
+  // ---- values: p*scale per token into LDS, p*min accumulated per lane
+  const float vs0 = lo_f16(r.vm[0]), vn0 = hi_f16(r.vm[0]);
+  const float vs1 = lo_f16(r.vm[1]), vn1 = hi_f16(r.vm[1]);
+  const float ft = field_scale(VB, t % TPW);
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    psL[j][2 * half][t] = p[j] * vs0 * ft;
+    psL[j][2 * half + 1][t] = p[j] * vs1 * ft;
+    st.mv[j][0] = st.mv[j][0] * alpha[j] + p[j] * vn0;
+    st.mv[j][1] = st.mv[j][1] * alpha[j] + p[j] * vn1;
+  }
+  const int gi = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float wt[kGroup];
+    const float4* pp = reinterpret_cast<const float4*>(&psL[j][gi][0]);
+#pragma unroll
+    for (int k = 0; k < kGroup / 4; ++k) {
+      const float4 v = pp[k];
+      wt[4 * k] = v.x; wt[4 * k + 1] = v.y; wt[4 * k + 2] = v.z; wt[4 * k + 3] = v.w;
+    }
+    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
+#pragma unroll
+    for (int w = 0; w < VB; ++w) {
+      o0 = dot_word<VB>(r.vc[w], wt + w * TPW, o0);
+      o1 = dot_word<VB>(r.vc[VB + w], wt + w * TPW, o1);
+    }
+    st.o[j][0] = o0;
+    st.o[j][1] = o1;
+  }
+}
+
+// One chunk of up to 32 fp16 window tokens.
+template <int GQ>
+__device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, int c,
+                                               WaveState<GQ>& st, const uint32_t (*qh)[64],
+                                               float (*pL)[kGroup], int lane) {
+  const int t = lane & 31, half = lane >> 5;
+  const int tok0 = c * kGroup;
+  const int nvalid = min(kGroup, a.n_resid - tok0);
+  const bool valid = t < nvalid;
+  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim;
+  uint32_t kw[32];
+  if (valid) {
+    const uint4* kp = reinterpret_cast<const uint4*>(kr + t * kHeadDim + half * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 u = kp[i];
+      kw[4 * i] = u.x; kw[4 * i + 1] = u.y; kw[4 * i + 2] = u.z; kw[4 * i + 3] = u.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) kw[i] = 0;
+  }
+  float p[GQ], alpha[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float acc = 0.f;
+    const uint4* qp = reinterpret_cast<const uint4*>(&qh[j][half * 32]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 u = qp[i];
+      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i]), as_h2(u.x), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 1]), as_h2(u.y), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 2]), as_h2(u.z), acc, false);
+      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 3]), as_h2(u.w), acc, false);
+    }
+    acc += __shfl_xor(acc, 32);
+    const float s = valid ? acc * a.scale_log2 : kNegInf;
+    p[j] = softmax_step(s, st.m[j], st.l[j], alpha[j]);
+    if (half == 0) pL[j][t] = p[j];
+  }
+  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    st.o[j][0] *= alpha[j];
+    st.o[j][1] *= alpha[j];
+    st.mv[j][0] *= alpha[j];
+    st.mv[j][1] *= alpha[j];
+  }
+  for (int k = 0; k < nvalid; ++k) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(vr + k * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+      const float pk = pL[j][k];
+      st.o[j][0] = fmaf(pk, lo_f16(v), st.o[j][0]);
+      st.o[j][1] = fmaf(pk, hi_f16(v), st.o[j][1]);
+    }
+  }
+}
+
+template <int KB, int VB, int GQ>
+__global__ __launch_bounds__(kThreads) void decode_uniform_kernel(DecodeArgs a) {
+  __shared__ __align__(16) uint32_t qh[GQ][64];
+  __shared__ __align__(16) float qsL[kWaves][GQ][kHeadDim];
+  __shared__ __align__(16) float psL[kWaves][GQ][4][kGroup];
+  __shared__ float wm[kWaves][GQ], wl[kWaves][GQ];
+  __shared__ __align__(16) float wo[kWaves][GQ][kHeadDim];
+  __shared__ uint32_t ticket;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int split = blockIdx.x % a.splits;
+  const int64_t bh = blockIdx.x / a.splits;
+  const int b = (int)(bh / a.kv_heads);
+  const int hkv = (int)(bh % a.kv_heads);
+  const int hq0 = hkv * GQ;
+
+  uint32_t qreg[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    qreg[j] = *reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.q_heads + hq0 + j) *
+                                                           kHeadDim + 2 * lane);
+    if (wave == 0) qh[j][lane] = qreg[j];
+  }
+  __syncthreads();
+
+  WaveState<GQ> st;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    st.m[j] = kNegInf;
+    st.l[j] = 0.f;
+    st.o[j][0] = st.o[j][1] = 0.f;
+    st.mv[j][0] = st.mv[j][1] = 0.f;
+  }
+
+  if (split < a.packed_splits) {
+    const int b0 = split * a.blocks_per_split;
+    const int b1 = min(a.n_blocks, b0 + a.blocks_per_split);
+    const int64_t base = bh * a.cap_blocks;
+    int i = b0 + wave;
+    BlockRegs<KB, VB> cur, nxt;
+    if (i < b1) load_block<KB, VB>(cur, a, base + i, lane);
+    for (; i < b1; i += kWaves) {
+      if (i + kWaves < b1) load_block<KB, VB>(nxt, a, base + i + kWaves, lane);
+      process_block<KB, VB, GQ>(cur, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+      cur = nxt;
+    }
+  } else {
+    const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+    for (int c = wave; c < nchunks; c += kWaves)
+      process_window<GQ>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
+  }
+
+  // ---- finish the wave: totals of l and of the min terms, then the WG merge
+  const int k_sel = (lane >> 4) & 1;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const float lt = sum32(st.l[j]);
+    const float mv0 = sum32(st.mv[j][0]);
+    const float mv1 = sum32(st.mv[j][1]);
+    const float mvg = k_sel ? mv1 : mv0;
+    if (lane == 0) {
+      wm[wave][j] = st.m[j];
+      wl[wave][j] = lt;
+    }
+    *reinterpret_cast<float2*>(&wo[wave][j][2 * lane]) =
+        make_float2(st.o[j][0] + mvg, st.o[j][1] + mvg);
+  }
+  __syncthreads();
+
+  const bool single = a.splits == 1;
+  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += kThreads) {
+    const int j = idx >> 7, d = idx & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][j]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float e = exp2f(wm[w][j] - M);
+        L += wl[w][j] * e;
+        O += wo[w][j][d] * e;
+      }
+    }
+    const int64_t row = (int64_t)b * a.q_heads + hq0 + j;
+    if (single) {
+      a.out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+    } else {
+      float* P = a.partials + (row * a.splits + split) * kPartialStride;
+      P[d] = O;
+      if (d == 0) {
+        P[kHeadDim] = M;
+        P[kHeadDim + 1] = L;
+      }
+    }
+  }
+  if (single) return;
+
+  // ---- split merge by the last workgroup of this (batch, kv head)
+  __threadfence();
+  __syncthreads();
+  uint32_t* cnt = a.counters + bh;
+  if (threadIdx.x == 0)
+    ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket != (uint32_t)(a.splits - 1)) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += kThreads) {
+    const int j = idx >> 7, d = idx & 127;
+    const int64_t row = (int64_t)b * a.q_heads + hq0 + j;
+    const float* P = a.partials + row * a.splits * kPartialStride;
+    float M = kNegInf;
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+      for (int s = 0; s < a.splits; ++s) {
+        const float ms = P[s * kPartialStride + kHeadDim];
+        const float e = exp2f(ms - M);
+        L += P[s * kPartialStride + kHeadDim + 1] * e;
+        O += P[s * kPartialStride + d] * e;
+      }
+    }
+    a.out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
+                                 hipStream_t s) {
+  const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
+  dim3 grid((unsigned)wgs), block(kThreads);
+#define KVQ_DL(KB_, VB_, G_)                                                        \
+  if (k_bits == KB_ && v_bits == VB_ && gq == G_) {                                 \
+    decode_uniform_kernel<KB_, VB_, G_><<<grid, block, 0, s>>>(a);                  \
+    return hipGetLastError();                                                       \
+  }
+#define KVQ_DLG(G_) KVQ_DL(2, 2, G_) KVQ_DL(2, 4, G_) KVQ_DL(4, 2, G_) KVQ_DL(4, 4, G_)
+  KVQ_DLG(1) KVQ_DLG(2) KVQ_DLG(4) KVQ_DLG(8)
+#undef KVQ_DLG
+#undef KVQ_DL
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,92 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kGroup = 32;        // tokens per packed block, channels per value group
+constexpr int kHeadDim = 128;     // the GPU kernels are built for D = 128
+constexpr int kWave = 64;
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t w) { return __builtin_bit_cast(h2_t, w); }
+__device__ __forceinline__ float lo_f16(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float hi_f16(uint32_t w) { return (float)as_h2(w)[1]; }
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default mode).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ---- launch parameter blocks (host fills, kernels read) ----------------------
+struct QuantArgs {
+  const uint16_t* k;        // source keys (NULL: skip keys)
+  const uint16_t* v;        // source values (NULL: skip values)
+  int64_t ks_b, ks_h, ks_t; // element strides of the key source
+  int64_t vs_b, vs_h, vs_t;
+  uint32_t* k_codes;
+  uint32_t* k_meta;
+  uint32_t* v_codes;
+  uint32_t* v_meta;
+  int32_t kv_heads;
+  int32_t n_blocks;         // blocks of 32 tokens to quantize per (b, h)
+  int64_t blk0;             // destination block index of the first block
+  int64_t cap_blocks;       // capacity_tokens / 32
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_resid;
+  uint16_t* v_resid;
+  int32_t rows;             // batch * kv_heads
+  int32_t residual_len;
+  int32_t slot;
+};
+
+struct DecodeArgs {
+  const uint32_t* k_codes;
+  const uint32_t* k_meta;
+  const uint32_t* v_codes;
+  const uint32_t* v_meta;
+  const uint16_t* k_resid;
+  const uint16_t* v_resid;
+  const uint16_t* q;
+  float* out;
+  float* partials;          // [batch][q_heads][splits][kPartialStride]
+  uint32_t* counters;       // [batch][kv_heads]
+  // nuq extras
+  const uint16_t* lut_k;
+  const uint16_t* lut_v;
+  const int32_t* csr_rowptr;
+  const uint32_t* csr_ent;
+  int64_t csr_capacity;
+  float rope_theta;
+  int32_t batch, kv_heads, q_heads;
+  int32_t residual_len;
+  int64_t cap_blocks;
+  int32_t n_blocks;         // packed blocks (n_packed / 32)
+  int32_t n_resid;
+  int32_t splits;           // total splits (packed splits + window split)
+  int32_t packed_splits;
+  int32_t blocks_per_split;
+  float scale_log2;         // sm_scale * log2(e)
+};
+
+constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
+
+// ---- launchers (defined in the .hip files) ------------------------------------
+hipError_t launch_quant_uniform(const QuantArgs& a, int batch, int k_bits, int v_bits,
+                                hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
+                                 hipStream_t s);
+
+}  // namespace kvq

@@ -40,7 +40,6 @@ TID_K = 1
 TID_V = 2
 TID_Q = 3
 TID_OUTLIER = 4
-TID_KNEW = 5   # tokens appended after the prefill (same coordinates as K/V)
 
 
 def mix64(z):
@@ -198,3 +197,39 @@ WORKLOADS = {
 def n_outlier_channels(head_dim: int, frac: float = 0.02) -> int:
     """Rounded count of outlier channels for a fraction of the head dimension."""
     return int(math.floor(frac * head_dim + 0.5))
+
+
+# ---- device generator (kvq_synth/synth.hip, built into libkvq_synth.so) ----------------
+_synth_lib = None
+
+
+def _load_synth():
+    global _synth_lib
+    if _synth_lib is None:
+        import ctypes as C
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq_synth.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: run python -m decode_attention_10_amd.build")
+        import torch  # noqa: F401  (share torch's HIP runtime, see the binding)
+        lib = C.CDLL(path)
+        lib.kvq_synth_fill.restype = C.c_int
+        lib.kvq_synth_fill.argtypes = [C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_int64,
+                                       C.c_int32, C.c_int64, C.c_int32, C.c_void_p, C.c_void_p]
+        _synth_lib = lib
+    return _synth_lib
+
+
+def fill_device(out, seed: int, tensor_id: int, batch: int, heads: int, tokens: int,
+                head_dim: int, gains=None, t0: int = 0, b0: int = 0, stream=None):
+    """Fill a device tensor (int16/uint16 storage, [batch][heads][tokens][head_dim]) with the
+    values gen_tensor() defines.  ``gains``: device float32 [heads][head_dim] or None."""
+    import torch
+    lib = _load_synth()
+    assert out.numel() >= batch * heads * tokens * head_dim and out.element_size() == 2
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = lib.kvq_synth_fill(out.data_ptr(), stream_key(seed, tensor_id), batch, heads, tokens,
+                            head_dim, t0, b0, None if gains is None else gains.data_ptr(), s)
+    if rc != 0:
+        raise RuntimeError(f"kvq_synth_fill failed ({rc})")
+    return out
