@@ -1,0 +1,250 @@
+"""Benchmark of the packed-KV decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode step of one layer: append the new token's K/V to the fp16
+window (every 128th step the window is full and is first quantized into the packed
+cache: the per-channel key and per-token value quantizers) and then decode attention
+over the whole cache.  The layer caches rotate (several copies, > 768 MB in all) so
+that every step streams its cache from HBM rather than from the 256 MB Infinity
+Cache.  Each layer's state is restored after its step, so every decode sees the
+configured context.
+
+Printed: one JSON line.  value = decode-attention GB/s (algorithmic bytes of codes,
+metadata, fp16 window, q and out per launch / mean decode kernel time from HIP events
+on the launch stream).  Also tokens*ctx/s, prefill quantize GB/s, the roofline of the
+decode kernel and the oracle timed on a bounded host sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
+
+
+def decode_bytes(w, n_packed: int, n_resid: int) -> int:
+    """Algorithmic bytes one decode launch must move: packed codes and metadata, the fp16
+    window, q and the fp32 output."""
+    bh = w.batch * w.kv_heads
+    D = w.head_dim
+    codes = bh * n_packed * D * (w.k_bits + w.v_bits) // 8
+    meta = bh * (n_packed // 32) * D * 4 + bh * n_packed * (D // 32) * 4
+    window = 2 * bh * n_resid * D * 2
+    return codes + meta + window + w.batch * w.q_heads * D * (2 + 4)
+
+
+def quantize_bytes(w, n_tokens: int) -> int:
+    """Prefill quantize: fp16 K and V read, packed codes and metadata written."""
+    bh = w.batch * w.kv_heads
+    D = w.head_dim
+    read = 2 * bh * n_tokens * D * 2
+    written = bh * n_tokens * D * (w.k_bits + w.v_bits) // 8 + \
+        bh * (n_tokens // 32) * D * 4 + bh * n_tokens * (D // 32) * 4
+    return read + written
+
+
+def cpu_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, budget_s: float = 20.0) -> dict:
+    """The oracle (unchanged) on a bounded sample: whole (batch, kv head) units of the same
+    workload.  Per unit the oracle builds the packed cache from host-generated K/V (setup,
+    untimed), then the timed part unpacks it, dequantizes and runs float64 attention.
+    Stops after ``budget_s`` of wall time.  One thread (BLAS pinned to 1)."""
+    from threadpoolctl import threadpool_limits
+
+    import kvq_synth as S
+    from oracle import kvq_oracle as O
+    T = w.n_packed + w.n_resid
+    g = w.gains()
+    sm = O.default_sm_scale(w.head_dim)
+    gq = w.q_heads // w.kv_heads
+    done, t_used, nbytes = 0, 0.0, 0
+    per_unit = decode_bytes(w, w.n_packed, w.n_resid) // (w.batch * w.kv_heads)
+    wall0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while time.perf_counter() - wall0 < budget_s and done < w.batch * w.kv_heads:
+            b, h = divmod(done, w.kv_heads)
+            k = S.gen_tensor(w.seed, S.TID_K, w.batch, w.kv_heads, T, w.head_dim, gains=g,
+                             heads_sel=[h], batch_sel=[b])
+            v = S.gen_tensor(w.seed, S.TID_V, w.batch, w.kv_heads, T, w.head_dim,
+                             heads_sel=[h], batch_sel=[b])
+            q = S.gen_tensor(w.seed, S.TID_Q, w.batch, w.q_heads, 1, w.head_dim,
+                             heads_sel=list(range(h * gq, (h + 1) * gq)), batch_sel=[b])[:, :, 0]
+            c = O.uniform_cache(k, v, w.k_bits, w.v_bits, w.n_packed, w.n_resid)
+            t0 = time.perf_counter()
+            kc = O.unpack_k_codes(c["k_codes"], w.k_bits, w.head_dim)
+            vc = O.unpack_v_codes(c["v_codes"], w.v_bits)
+            ks, km = O.unpack_meta(c["k_meta"])
+            vs, vm = O.unpack_meta(c["v_meta"])
+            kd = O.dequant_keys_per_channel(kc, ks, km)
+            vd = O.dequant_values_per_token(vc, vs, vm)
+            kd = np.concatenate([kd, O.f16_to_f32(k[:, :, w.n_packed:])], axis=2)
+            vd = np.concatenate([vd, O.f16_to_f32(v[:, :, w.n_packed:])], axis=2)
+            O.decode_attention_f64(O.f16_to_f32(q), kd, vd, sm)
+            t_used += time.perf_counter() - t0
+            nbytes += per_unit
+            done += 1
+    return {"value": round(nbytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.kv_heads} (batch, kv head) units of {w.name}: "
+                      f"unpack + dequantize + float64 attention, {t_used:.1f} s on 1 thread "
+                      f"of {cpu_cores()} available"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-mb", type=float, default=768.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU design is "
+              f"described in DESIGN.md and not built", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_10_amd as K
+    import kvq_synth as S
+    w = S.WORKLOADS[args.workload]
+    if w.kind != "uniform":
+        raise SystemExit(f"workload {w.name} is not a uniform cache")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    B, Hkv, Hq, D, N, R = w.batch, w.kv_heads, w.q_heads, w.head_dim, w.n_packed, w.residual_len
+    T = N + w.n_resid
+    cap = N + R
+
+    # ---- inputs on the device (generator kernel), prefill into the layer copies
+    gains = torch.from_numpy(w.gains()).to(dev)
+    k_src = torch.empty((B, Hkv, T + 1, D), dtype=torch.int16, device=dev)
+    v_src = torch.empty((B, Hkv, T + 1, D), dtype=torch.int16, device=dev)
+    S.fill_device(k_src, w.seed, S.TID_K, B, Hkv, T + 1, D, gains=gains)
+    S.fill_device(v_src, w.seed, S.TID_V, B, Hkv, T + 1, D)
+    q = torch.empty((B, Hq, 1, D), dtype=torch.int16, device=dev)
+    S.fill_device(q, w.seed, S.TID_Q, B, Hq, 1, D)
+    k_new = k_src[:, :, T].contiguous()
+    v_new = v_src[:, :, T].contiguous()
+
+    per_layer = decode_bytes(w, N, w.n_resid)
+    layers = max(1, math.ceil(args.min_rotation_mb * 1e6 / per_layer))
+    caches = []
+    sT = (B, Hkv * (T + 1) * D, (T + 1) * D, D)
+    for _ in range(layers):
+        c = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R)
+        K.kvq_quantize_keys(c.c, k_src, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(c.c, v_src, sT[1], sT[2], sT[3], 0, N)
+        kr = c.buf("k_resid").view(torch.int16).view(B, Hkv, R, D)
+        vr = c.buf("v_resid").view(torch.int16).view(B, Hkv, R, D)
+        kr[:, :, :w.n_resid] = k_src[:, :, N:T]
+        vr[:, :, :w.n_resid] = v_src[:, :, N:T]
+        caches.append(c)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws_bytes = K.kvq_workspace_bytes(caches[0].c, Hq, K.KVQ_OP_DECODE_ATTN)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+
+    # prefill quantize rate (keys + values over the whole packed context), own copy
+    qc = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1) / reps
+    quant_gbs = quantize_bytes(w, N) / (quant_ms * 1e-3) / 1e9
+    del qc
+
+    # ---- the step: append (flush every 128th) + decode, layers rotating
+    def step(i: int, evs=None):
+        c = caches[i % layers].c
+        flush = (i % R) == R - 1
+        c.n_packed, c.n_resid = N, (R if flush else w.n_resid - 1)
+        K.kvq_append_flush(c, k_new, v_new)
+        nbytes = decode_bytes(w, int(c.n_packed), int(c.n_resid))
+        if evs is not None:
+            evs[0].record(stream)
+        K.kvq_decode_attn(c, q, Hq, sm, 0.0, out, ws, ws_bytes)
+        if evs is not None:
+            evs[1].record(stream)
+        c.n_packed, c.n_resid = N, w.n_resid
+        return nbytes
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    nbytes = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        nbytes.append(step(args.warmup + i, evs[i]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    mean_dec_s = float(dec_ms.mean()) * 1e-3
+    mean_bytes = float(np.mean(nbytes))
+    gbs = mean_bytes / mean_dec_s / 1e9
+    tok_ctx = B * T / mean_dec_s
+
+    res = {
+        "metric": "decode-attn HBM GB/s on packed KV (% of peak); tokens*ctx/s; quantize GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {B}, {Hq} q / {Hkv} kv heads, head_dim {D}, "
+                               f"{N} packed + {w.n_resid} fp16 window tokens, K int{w.k_bits} "
+                               f"per-channel / V int{w.v_bits} per-token, group 32",
+                   "layers_rotated": layers, "flush_every": R},
+        "decode_us": round(mean_dec_s * 1e6, 3),
+        "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+                              round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "tokens_ctx_per_s": round(tok_ctx, 1),
+        "quantize_gbs": round(quant_gbs, 1),
+        "quantize_ms_prefill": round(quant_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -23,9 +23,9 @@
 // blocks (split-K over the context, as in flash-decoding); a wave streams one
 // 32-token block at a time (lane = token x channel half for keys, lane = channel
 // pair for values), with the next block's loads in flight.  The fp16 window is an
-// extra split.  Waves merge in LDS; splits merge in the same launch: the last
-// workgroup of a (batch, kv head) to finish (atomic ticket) combines the partial
-// (max, sum, output) triples and writes the output.
+// extra split.  Waves merge in LDS.  With one split per (batch, kv head) the
+// workgroup writes the output; otherwise it writes a (max, sum, output) partial and a
+// second small launch merges the splits.
 #include "kvq_common.h"
 
 namespace kvq {
@@ -71,19 +71,46 @@ __device__ __forceinline__ float dot_word(uint32_t w, const float* wt, float acc
   return acc;
 }
 
+// DPP lane permutations (gfx9 encodings): quad_perm, row mirrors, row broadcasts.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, x), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float readlane63(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+// Sum over all 64 lanes, returned wave-uniform.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp<kQuadSwap1>(0.f, x);
+  x += dpp<kQuadSwap2>(0.f, x);
+  x += dpp<kRowHalfMirror>(0.f, x);
+  x += dpp<kRowMirror>(0.f, x);
+  x += dpp<kRowBcast15, 0xA>(0.f, x);
+  x += dpp<kRowBcast31, 0xC>(0.f, x);
+  return readlane63(x);
+}
+// Max over all 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(kNegInf, x));
+  x = fmaxf(x, dpp<kQuadSwap2>(kNegInf, x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(kNegInf, x));
+  x = fmaxf(x, dpp<kRowMirror>(kNegInf, x));
+  x = fmaxf(x, dpp<kRowBcast15, 0xA>(kNegInf, x));
+  x = fmaxf(x, dpp<kRowBcast31, 0xC>(kNegInf, x));
+  return readlane63(x);
 }
 __device__ __forceinline__ float sum32(float x) {   // over lane bits 0..4
 #pragma unroll
   for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float max32(float x) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
 }
 
@@ -128,14 +155,19 @@ struct WaveState {
   float mv[GQ][2];    // sum_t p_t * min_tg for groups 2h, 2h+1 (token lanes)
 };
 
-// Online softmax update for one head; s is this lane's token score (log2 units).
+// Online softmax update for one head; s is this lane's token score (log2 units; the
+// two lane halves hold the same tokens).  The block maximum is only reduced when some
+// score exceeds the running maximum, which after the first blocks is rare.
 __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
-  const float mb = max32(s);
-  const float mn = fmaxf(m, mb);
-  alpha = exp2f(m - mn);
-  const float p = exp2f(s - mn);
-  m = mn;
-  l = l * alpha + p;
+  alpha = 1.0f;
+  if (__any(s > m)) {
+    const float mn = fmaxf(m, wave_max(s));
+    alpha = exp2f(m - mn);
+    m = mn;
+    l *= alpha;
+  }
+  const float p = exp2f(s - m);
+  l += p;
   return p;
 }
 
@@ -267,28 +299,42 @@ __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, 
     st.mv[j][0] *= alpha[j];
     st.mv[j][1] *= alpha[j];
   }
-  for (int k = 0; k < nvalid; ++k) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(vr + k * kHeadDim);
+  uint32_t vw[kGroup];
 #pragma unroll
-    for (int j = 0; j < GQ; ++j) {
-      const float pk = pL[j][k];
-      st.o[j][0] = fmaf(pk, lo_f16(v), st.o[j][0]);
-      st.o[j][1] = fmaf(pk, hi_f16(v), st.o[j][1]);
+  for (int k = 0; k < kGroup; ++k)
+    vw[k] = *reinterpret_cast<const uint32_t*>(vr + min(k, nvalid - 1) * kHeadDim);
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const float4* pp = reinterpret_cast<const float4*>(&pL[j][0]);
+    float o0 = st.o[j][0], o1 = st.o[j][1];
+#pragma unroll
+    for (int k4 = 0; k4 < kGroup / 4; ++k4) {
+      const float4 p4 = pp[k4];
+      const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o0 = fmaf(pk[u], lo_f16(vw[4 * k4 + u]), o0);
+        o1 = fmaf(pk[u], hi_f16(vw[4 * k4 + u]), o1);
+      }
     }
+    st.o[j][0] = o0;
+    st.o[j][1] = o1;
   }
 }
 
+#ifndef KVQ_DECODE_MIN_WAVES
+#define KVQ_DECODE_MIN_WAVES 1
+#endif
 template <int KB, int VB, int GQ>
-__global__ __launch_bounds__(kThreads) void decode_uniform_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, KVQ_DECODE_MIN_WAVES) void decode_uniform_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint32_t qh[GQ][64];
   __shared__ __align__(16) float qsL[kWaves][GQ][kHeadDim];
   __shared__ __align__(16) float psL[kWaves][GQ][4][kGroup];
   __shared__ float wm[kWaves][GQ], wl[kWaves][GQ];
   __shared__ __align__(16) float wo[kWaves][GQ][kHeadDim];
-  __shared__ uint32_t ticket;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int split = blockIdx.x % a.splits;
   const int64_t bh = blockIdx.x / a.splits;
   const int b = (int)(bh / a.kv_heads);
@@ -317,13 +363,27 @@ __global__ __launch_bounds__(kThreads) void decode_uniform_kernel(DecodeArgs a) 
     const int b0 = split * a.blocks_per_split;
     const int b1 = min(a.n_blocks, b0 + a.blocks_per_split);
     const int64_t base = bh * a.cap_blocks;
+    // Two blocks in flight ahead of the one being processed.  The prefetch index is
+    // clamped rather than guarded so every iteration issues the same loads and the
+    // wait before processing only covers the oldest block.
+    const int last = b1 - 1;
     int i = b0 + wave;
-    BlockRegs<KB, VB> cur, nxt;
-    if (i < b1) load_block<KB, VB>(cur, a, base + i, lane);
-    for (; i < b1; i += kWaves) {
-      if (i + kWaves < b1) load_block<KB, VB>(nxt, a, base + i + kWaves, lane);
-      process_block<KB, VB, GQ>(cur, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-      cur = nxt;
+    if (i < b1) {
+      BlockRegs<KB, VB> r0, r1, r2;
+      load_block<KB, VB>(r0, a, base + i, lane);
+      load_block<KB, VB>(r1, a, base + min(i + kWaves, last), lane);
+      // Unrolled by three with rotating roles: no register copies, so no wait on the
+      // loads just issued.
+      for (; i < b1; i += 3 * kWaves) {
+        load_block<KB, VB>(r2, a, base + min(i + 2 * kWaves, last), lane);
+        process_block<KB, VB, GQ>(r0, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+        if (i + kWaves >= b1) break;
+        load_block<KB, VB>(r0, a, base + min(i + 3 * kWaves, last), lane);
+        process_block<KB, VB, GQ>(r1, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+        if (i + 2 * kWaves >= b1) break;
+        load_block<KB, VB>(r1, a, base + min(i + 4 * kWaves, last), lane);
+        process_block<KB, VB, GQ>(r2, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+      }
     }
   } else {
     const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
@@ -375,38 +435,32 @@ __global__ __launch_bounds__(kThreads) void decode_uniform_kernel(DecodeArgs a) 
       }
     }
   }
-  if (single) return;
+}
 
-  // ---- split merge by the last workgroup of this (batch, kv head)
-  __threadfence();
-  __syncthreads();
-  uint32_t* cnt = a.counters + bh;
-  if (threadIdx.x == 0)
-    ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (ticket != (uint32_t)(a.splits - 1)) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += kThreads) {
-    const int j = idx >> 7, d = idx & 127;
-    const int64_t row = (int64_t)b * a.q_heads + hq0 + j;
-    const float* P = a.partials + row * a.splits * kPartialStride;
-    float M = kNegInf;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
-    float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float ms = P[s * kPartialStride + kHeadDim];
-        const float e = exp2f(ms - M);
-        L += P[s * kPartialStride + kHeadDim + 1] * e;
-        O += P[s * kPartialStride + d] * e;
-      }
+// Combines the per-split (max, sum, output) partials of one (batch, query head) row.
+// A separate launch: the kernel boundary makes every split's stores visible, which
+// costs far less than device-scope fences in each workgroup of the main kernel.
+__global__ __launch_bounds__(kHeadDim) void merge_splits_kernel(const float* partials,
+                                                               float* out, int splits) {
+  const int64_t row = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* P = partials + row * splits * kPartialStride;
+  float M = kNegInf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
+  float L = 0.f, O = 0.f;
+  if (M != kNegInf) {
+    for (int s = 0; s < splits; ++s) {
+      const float e = exp2f(P[s * kPartialStride + kHeadDim] - M);
+      L += P[s * kPartialStride + kHeadDim + 1] * e;
+      O += P[s * kPartialStride + d] * e;
     }
-    a.out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
 }
 
 }  // namespace
+
+hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
@@ -415,13 +469,22 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
 #define KVQ_DL(KB_, VB_, G_)                                                        \
   if (k_bits == KB_ && v_bits == VB_ && gq == G_) {                                 \
     decode_uniform_kernel<KB_, VB_, G_><<<grid, block, 0, s>>>(a);                  \
-    return hipGetLastError();                                                       \
+    hipError_t e_ = hipGetLastError();                                              \
+    if (e_ != hipSuccess || a.splits == 1) return e_;                               \
+    return launch_merge_splits(a, s);                                               \
   }
 #define KVQ_DLG(G_) KVQ_DL(2, 2, G_) KVQ_DL(2, 4, G_) KVQ_DL(4, 2, G_) KVQ_DL(4, 4, G_)
   KVQ_DLG(1) KVQ_DLG(2) KVQ_DLG(4) KVQ_DLG(8)
 #undef KVQ_DLG
 #undef KVQ_DL
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.batch * a.q_heads;
+  merge_splits_kernel<<<dim3((unsigned)rows), dim3(kHeadDim), 0, s>>>(a.partials, a.out,
+                                                                       a.splits);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

@@ -61,7 +61,6 @@ struct DecodeArgs {
   const uint16_t* q;
   float* out;
   float* partials;          // [batch][q_heads][splits][kPartialStride]
-  uint32_t* counters;       // [batch][kv_heads]
   // nuq extras
   const uint16_t* lut_k;
   const uint16_t* lut_v;

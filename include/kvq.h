@@ -167,9 +167,9 @@ int64_t kvq_csr_entries_needed(const kvq_cache* c);
 
 /* Device scratch bytes that `op` needs for this descriptor (decode: for any
  * n_packed <= capacity_tokens and n_resid <= residual_len; q_heads is ignored by
- * the quantize op).  The decode workspace holds split partials and merge
- * counters: zero-fill it once before its first use; every call leaves the
- * counters at zero again.  Returns 0 if the op needs none or on invalid input. */
+ * the quantize op).  The decode workspace holds per-split partial results; its
+ * contents need no initialization and are overwritten by every call.  Returns 0
+ * if the op needs none or on invalid input. */
 size_t kvq_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t op);
 
 /* Quantize keys of tokens [token_offset, token_offset + n_tokens) into the packed
