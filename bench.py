@@ -10,9 +10,14 @@ that every step streams its cache from HBM rather than from the 256 MB Infinity
 Cache.  Each layer's state is restored after its step, so every decode sees the
 configured context.
 
-Printed: one JSON line.  value = decode-attention GB/s (algorithmic bytes of codes,
-metadata, fp16 window, q and out per launch / mean decode kernel time from HIP events
-on the launch stream).  Also tokens*ctx/s, prefill quantize GB/s, the roofline of the
+The launch-bound step loop is captured in HIP graphs (one round of 128 steps per
+graph) and the timed region replays them, so ms_per_step is GPU time, not Python
+launch overhead.
+
+Printed: one JSON line.  value = decode-attention GB/s: algorithmic bytes of codes,
+metadata, fp16 window, q and out per decode / mean decode time, from HIP events on
+the launch stream around replays of a decode-only graph (kernel plus the small gap
+between launches).  Also tokens*ctx/s, prefill quantize GB/s, the roofline of the
 decode kernel and the oracle timed on a bounded host sample.
 """
 from __future__ import annotations
@@ -109,7 +114,7 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--steps", type=int, default=1024, help="rounded down to whole rounds of 128")
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,52 +171,78 @@ def main() -> int:
 
     # prefill quantize rate (keys + values over the whole packed context), own copy
     qc = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R)
+
+    def prefill():
+        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
+
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(3):
-        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
-        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
-    reps = 10
+        prefill()
+    reps = 20
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)          # host enqueues behind a busy GPU
     e0.record(stream)
     for _ in range(reps):
-        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
-        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
+        prefill()
     e1.record(stream)
     torch.cuda.synchronize()
     quant_ms = e0.elapsed_time(e1) / reps
     quant_gbs = quantize_bytes(w, N) / (quant_ms * 1e-3) / 1e9
     del qc
 
-    # ---- the step: append (flush every 128th) + decode, layers rotating
-    def step(i: int, evs=None):
+    # ---- the step: append (flush every R-th step) + decode, layers rotating.  A round of
+    # R steps is captured in a HIP graph (launch-bound loop -> one graph launch); the
+    # captured kernel arguments fix each step's cache state, restored after the step.
+    def step(i: int) -> int:
         c = caches[i % layers].c
         flush = (i % R) == R - 1
         c.n_packed, c.n_resid = N, (R if flush else w.n_resid - 1)
         K.kvq_append_flush(c, k_new, v_new)
         nbytes = decode_bytes(w, int(c.n_packed), int(c.n_resid))
-        if evs is not None:
-            evs[0].record(stream)
         K.kvq_decode_attn(c, q, Hq, sm, 0.0, out, ws, ws_bytes)
-        if evs is not None:
-            evs[1].record(stream)
         c.n_packed, c.n_resid = N, w.n_resid
         return nbytes
 
-    for i in range(args.warmup):
+    def decode_only(i: int) -> None:
+        K.kvq_decode_attn(caches[i % layers].c, q, Hq, sm, 0.0, out, ws, ws_bytes)
+
+    cap_stream = torch.cuda.Stream()
+    round_len = R
+    step_graph, dec_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    for i in range(round_len):                 # eager warm-up of every step shape
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    nbytes = []
+    with torch.cuda.stream(cap_stream):
+        with torch.cuda.graph(step_graph, stream=cap_stream):
+            nbytes = [step(i) for i in range(round_len)]
+        with torch.cuda.graph(dec_graph, stream=cap_stream):
+            for i in range(round_len):
+                decode_only(i)
     torch.cuda.synchronize()
+    rounds = max(1, args.steps // round_len)
+    steps = rounds * round_len
+    for _ in range(max(1, args.warmup // round_len)):
+        step_graph.replay()
+        dec_graph.replay()
+    torch.cuda.synchronize()
+
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        nbytes.append(step(args.warmup + i, evs[i]))
+    for _ in range(rounds):
+        step_graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    mean_dec_s = float(dec_ms.mean()) * 1e-3
-    mean_bytes = float(np.mean(nbytes))
-    gbs = mean_bytes / mean_dec_s / 1e9
+
+    # decode kernel time: events around replays of the decode-only graph
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(rounds):
+        dec_graph.replay()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    mean_dec_s = d0.elapsed_time(d1) * 1e-3 / (rounds * round_len)
+    dec_bytes = decode_bytes(w, N, w.n_resid)
+    gbs = dec_bytes / mean_dec_s / 1e9
     tok_ctx = B * T / mean_dec_s
 
     res = {
@@ -219,9 +250,9 @@ def main() -> int:
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(wall / steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -232,8 +263,7 @@ def main() -> int:
                                f"per-channel / V int{w.v_bits} per-token, group 32",
                    "layers_rotated": layers, "flush_every": R},
         "decode_us": round(mean_dec_s * 1e6, 3),
-        "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-                              round(float(np.percentile(dec_ms, 90)) * 1e3, 3)],
+        "step_bytes_mean": int(np.mean(nbytes)),
         "tokens_ctx_per_s": round(tok_ctx, 1),
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_ms_prefill": round(quant_ms, 4),

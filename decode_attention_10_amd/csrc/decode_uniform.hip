@@ -31,9 +31,8 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kWindowUnits = 4;   // a 32-token fp16 window chunk weighs as 4 packed blocks
 
 // Bit position of field j (within its 16-bit half, after the shift used to reach
 // it) for a word holding 32/B fields of B bits.
@@ -322,16 +321,19 @@ __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, 
   }
 }
 
-#ifndef KVQ_DECODE_MIN_WAVES
-#define KVQ_DECODE_MIN_WAVES 1
-#endif
-template <int KB, int VB, int GQ>
-__global__ __launch_bounds__(kThreads, KVQ_DECODE_MIN_WAVES) void decode_uniform_kernel(DecodeArgs a) {
+// Work units: packed block i is unit i (0 <= i < n_blocks); window chunk c (32 fp16
+// tokens) is units [n_blocks + kWindowUnits*c, n_blocks + kWindowUnits*(c+1)), weighted
+// by its larger byte count.  A split covers a contiguous unit range; each wave of the
+// split covers a contiguous sub-range: the packed blocks in it, and every window
+// chunk whose first unit falls in it.
+template <int KB, int VB, int GQ, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a) {
+  constexpr int NT = NW * kWave;
   __shared__ __align__(16) uint32_t qh[GQ][64];
-  __shared__ __align__(16) float qsL[kWaves][GQ][kHeadDim];
-  __shared__ __align__(16) float psL[kWaves][GQ][4][kGroup];
-  __shared__ float wm[kWaves][GQ], wl[kWaves][GQ];
-  __shared__ __align__(16) float wo[kWaves][GQ][kHeadDim];
+  __shared__ __align__(16) float qsL[NW][GQ][kHeadDim];
+  __shared__ __align__(16) float psL[NW][GQ][4][kGroup];
+  __shared__ float wm[NW][GQ], wl[NW][GQ];
+  __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -359,36 +361,40 @@ __global__ __launch_bounds__(kThreads, KVQ_DECODE_MIN_WAVES) void decode_uniform
     st.mv[j][0] = st.mv[j][1] = 0.f;
   }
 
-  if (split < a.packed_splits) {
-    const int b0 = split * a.blocks_per_split;
-    const int b1 = min(a.n_blocks, b0 + a.blocks_per_split);
+  const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+  const int units = a.n_blocks + kWindowUnits * nchunks;
+  const int s0 = (int)((int64_t)units * split / a.splits);
+  const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
+  const int w0 = s0 + (int)((int64_t)(s1 - s0) * wave / NW);
+  const int w1 = s0 + (int)((int64_t)(s1 - s0) * (wave + 1) / NW);
+
+  // ---- window chunks first (their loads are short), then the packed blocks
+  for (int c = 0; c < nchunks; ++c) {
+    const int u = a.n_blocks + kWindowUnits * c;
+    if (u >= w0 && u < w1)
+      process_window<GQ>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
+  }
+  const int b0 = w0, b1 = min(w1, a.n_blocks);
+  if (b0 < b1) {
     const int64_t base = bh * a.cap_blocks;
     // Two blocks in flight ahead of the one being processed.  The prefetch index is
-    // clamped rather than guarded so every iteration issues the same loads and the
-    // wait before processing only covers the oldest block.
+    // clamped rather than guarded so every iteration issues the same loads, and the
+    // loop is unrolled by three with rotating roles so no register copy has to wait
+    // for the loads just issued.
     const int last = b1 - 1;
-    int i = b0 + wave;
-    if (i < b1) {
-      BlockRegs<KB, VB> r0, r1, r2;
-      load_block<KB, VB>(r0, a, base + i, lane);
-      load_block<KB, VB>(r1, a, base + min(i + kWaves, last), lane);
-      // Unrolled by three with rotating roles: no register copies, so no wait on the
-      // loads just issued.
-      for (; i < b1; i += 3 * kWaves) {
-        load_block<KB, VB>(r2, a, base + min(i + 2 * kWaves, last), lane);
-        process_block<KB, VB, GQ>(r0, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-        if (i + kWaves >= b1) break;
-        load_block<KB, VB>(r0, a, base + min(i + 3 * kWaves, last), lane);
-        process_block<KB, VB, GQ>(r1, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-        if (i + 2 * kWaves >= b1) break;
-        load_block<KB, VB>(r1, a, base + min(i + 4 * kWaves, last), lane);
-        process_block<KB, VB, GQ>(r2, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-      }
+    BlockRegs<KB, VB> r0, r1, r2;
+    load_block<KB, VB>(r0, a, base + b0, lane);
+    load_block<KB, VB>(r1, a, base + min(b0 + 1, last), lane);
+    for (int i = b0; i < b1; i += 3) {
+      load_block<KB, VB>(r2, a, base + min(i + 2, last), lane);
+      process_block<KB, VB, GQ>(r0, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+      if (i + 1 >= b1) break;
+      load_block<KB, VB>(r0, a, base + min(i + 3, last), lane);
+      process_block<KB, VB, GQ>(r1, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+      if (i + 2 >= b1) break;
+      load_block<KB, VB>(r1, a, base + min(i + 4, last), lane);
+      process_block<KB, VB, GQ>(r2, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
     }
-  } else {
-    const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
-    for (int c = wave; c < nchunks; c += kWaves)
-      process_window<GQ>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
   }
 
   // ---- finish the wave: totals of l and of the min terms, then the WG merge
@@ -409,15 +415,15 @@ __global__ __launch_bounds__(kThreads, KVQ_DECODE_MIN_WAVES) void decode_uniform
   __syncthreads();
 
   const bool single = a.splits == 1;
-  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += NT) {
     const int j = idx >> 7, d = idx & 127;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][j]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][j]);
     float L = 0.f, O = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float e = exp2f(wm[w][j] - M);
         L += wl[w][j] * e;
         O += wo[w][j][d] * e;
@@ -465,17 +471,21 @@ hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
-  dim3 grid((unsigned)wgs), block(kThreads);
-#define KVQ_DL(KB_, VB_, G_)                                                        \
-  if (k_bits == KB_ && v_bits == VB_ && gq == G_) {                                 \
-    decode_uniform_kernel<KB_, VB_, G_><<<grid, block, 0, s>>>(a);                  \
+  const int nw = a.waves_per_group;
+  dim3 grid((unsigned)wgs), block((unsigned)(nw * kWave));
+#define KVQ_DL(KB_, VB_, G_, NW_)                                                   \
+  if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_) {                    \
+    decode_uniform_kernel<KB_, VB_, G_, NW_><<<grid, block, 0, s>>>(a);             \
     hipError_t e_ = hipGetLastError();                                              \
     if (e_ != hipSuccess || a.splits == 1) return e_;                               \
     return launch_merge_splits(a, s);                                               \
   }
-#define KVQ_DLG(G_) KVQ_DL(2, 2, G_) KVQ_DL(2, 4, G_) KVQ_DL(4, 2, G_) KVQ_DL(4, 4, G_)
-  KVQ_DLG(1) KVQ_DLG(2) KVQ_DLG(4) KVQ_DLG(8)
-#undef KVQ_DLG
+#define KVQ_DLB(G_, NW_) KVQ_DL(2, 2, G_, NW_) KVQ_DL(2, 4, G_, NW_) KVQ_DL(4, 2, G_, NW_) \
+  KVQ_DL(4, 4, G_, NW_)
+  KVQ_DLB(1, 4) KVQ_DLB(2, 4) KVQ_DLB(4, 4) KVQ_DLB(8, 4)
+  KVQ_DLB(1, 8) KVQ_DLB(2, 8) KVQ_DLB(4, 8) KVQ_DLB(8, 8)
+  KVQ_DLB(1, 16)
+#undef KVQ_DLB
 #undef KVQ_DL
   return hipErrorInvalidValue;
 }

@@ -73,9 +73,8 @@ struct DecodeArgs {
   int64_t cap_blocks;
   int32_t n_blocks;         // packed blocks (n_packed / 32)
   int32_t n_resid;
-  int32_t splits;           // total splits (packed splits + window split)
-  int32_t packed_splits;
-  int32_t blocks_per_split;
+  int32_t splits;           // workgroups per (batch, kv head)
+  int32_t waves_per_group;  // 4, 8 or 16
   float scale_log2;         // sm_scale * log2(e)
 };
 
