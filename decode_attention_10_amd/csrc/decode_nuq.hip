@@ -1,0 +1,440 @@
+// Decode attention over the non-uniform cache with outliers and RoPE after
+// dequantization (KVQuant review, abstract items (ii)-(iv); "The KV cache has a
+// geometry problem", section on rotary embeddings: quantize keys before the rotation,
+// rotate after dequantization).
+//
+// Key t (position t) after dequantization: k~_d = lut[c_td] * s_d + m_d, or the exact
+// fp16 value at an outlier.  With RoPE on interleaved pairs, q . R(t) k~ is
+//   sum_i Re(a_i(t)) k~_2i + Im(a_i(t)) k~_2i+1,   a_i(t) = (q_2i + i q_2i+1) e^(-i t th_i)
+// so one lane owns a channel pair i, keeps a_i for the current token and advances it
+// by e^(-i th_i) per token (a complex product); each block restarts it from an angle
+// t0 * th_i reduced modulo 2 pi in fp64.  Per-pair partial scores of the block's 32
+// tokens are then summed across lanes.  Outliers: the dense pass uses the stored code
+// everywhere; the lane of token t then walks the token's CSR row and adds
+// a_col(t) * (x - dequant(code)) for each entry, in row order.
+//
+// Values: one lane per channel pair as well; o_d += (p_t * s_t) * lut[c_td] plus the
+// per-token minimum term sum_t p_t m_t, identical for every channel.
+// Code-book lookups: four codes in the four bytes of a word select bytes of the
+// eight-entry fp16 table with v_perm_b32.
+#include "kvq_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kWindowUnits = 4;
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+struct Lut {
+  uint32_t lo_a, lo_b, hi_a, hi_b;   // low / high bytes of entries 0-3 and 4-7
+};
+
+__device__ __forceinline__ Lut load_lut(const uint16_t* lut) {
+  uint32_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = lut[i];
+  Lut r;
+  r.lo_a = (e[0] & 255) | (e[1] & 255) << 8 | (e[2] & 255) << 16 | (e[3] & 255) << 24;
+  r.lo_b = (e[4] & 255) | (e[5] & 255) << 8 | (e[6] & 255) << 16 | (e[7] & 255) << 24;
+  r.hi_a = (e[0] >> 8) | (e[1] >> 8) << 8 | (e[2] >> 8) << 16 | (e[3] >> 8) << 24;
+  r.hi_b = (e[4] >> 8) | (e[5] >> 8) << 8 | (e[6] >> 8) << 16 | (e[7] >> 8) << 24;
+  return r;
+}
+
+// Four codes (one per byte, 0..7) -> their fp16 entries as two packed pairs.
+__device__ __forceinline__ void lut4(const Lut& L, uint32_t codes, uint32_t& p01, uint32_t& p23) {
+  const uint32_t lo = __builtin_amdgcn_perm(L.lo_b, L.lo_a, codes);
+  const uint32_t hi = __builtin_amdgcn_perm(L.hi_b, L.hi_a, codes);
+  p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// Codes of tokens 4m..4m+3 of one channel's three nuq3 words, one per byte.
+__device__ __forceinline__ uint32_t codes4(const uint32_t* w, int m) {
+  const uint32_t lo = (w[m >> 2] >> (2 * (m & 3))) & 0x03030303u;
+  const uint32_t hi = (w[2] >> m) & 0x01010101u;
+  return lo | (hi << 2);
+}
+
+__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
+  const int jj = j & 15;
+  const uint32_t lo = (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
+  const uint32_t hi = (w[2] >> (8 * (j & 3) + (j >> 2))) & 1u;
+  return lo | (hi << 2);
+}
+
+__device__ __forceinline__ float lut_value(const uint16_t* lut, uint32_t c) {
+  return f16_bits_to_f32(lut[c]);
+}
+
+// e^(-i phi) for phi = t * theta reduced modulo 2 pi in fp64.
+__device__ __forceinline__ float2 rot_at(int64_t t, double theta) {
+  double ph = fmod((double)t * theta, kTwoPi);
+  float s, c;
+  sincosf((float)ph, &s, &c);
+  return make_float2(c, -s);
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+__device__ __forceinline__ float sum32(float x) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float old, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, x), CTRL,
+                                                               ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(kNegInf, x));
+  x = fmaxf(x, dpp<0x4E>(kNegInf, x));
+  x = fmaxf(x, dpp<0x141>(kNegInf, x));
+  x = fmaxf(x, dpp<0x140>(kNegInf, x));
+  x = fmaxf(x, dpp<0x142, 0xA>(kNegInf, x));
+  x = fmaxf(x, dpp<0x143, 0xC>(kNegInf, x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Lane l ends with the sum over all 64 lanes of v[l & 31] (transposed reduction).
+__device__ __forceinline__ float transpose_sum32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int d = 16; d >= 1; d >>= 1) {
+    const bool up = lane & d;
+#pragma unroll
+    for (int i = 0; i < d; ++i) {
+      const float keep = up ? v[i + d] : v[i];
+      const float send = up ? v[i] : v[i + d];
+      v[i] = keep + __shfl_xor(send, d);
+    }
+  }
+  return v[0] + __shfl_xor(v[0], 32);
+}
+
+template <int GQ>
+struct NuqState {
+  float m[GQ], l[GQ], o[GQ][2], mv[GQ];
+};
+
+__device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
+  alpha = 1.0f;
+  if (__any(s > m)) {
+    const float mn = fmaxf(m, wave_max(s));
+    alpha = exp2f(m - mn);
+    m = mn;
+    l *= alpha;
+  }
+  const float p = exp2f(s - m);
+  l += p;
+  return p;
+}
+
+struct PairConsts {
+  float2 q[8];        // (q_2i, q_2i+1) per query head
+  float2 step;        // e^(-i theta_i)
+  double theta;       // theta_i
+  float ks0, km0, ks1, km1;   // key scale / min of channels 2i, 2i+1
+};
+
+// Softmax over the block's scores and the value accumulation shared by packed blocks
+// and window chunks: s[] holds this lane's token (lane & 31) score per head (log2
+// units, -inf for missing tokens); vw[] the lane's value weights source.
+template <int GQ>
+__device__ __forceinline__ void softmax_block(NuqState<GQ>& st, const float* s, float* p,
+                                              float* alpha) {
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) p[j] = softmax_step(s[j], st.m[j], st.l[j], alpha[j]);
+}
+
+template <int GQ>
+__device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t blk, int64_t t0,
+                                  const PairConsts& pc, const Lut& lk, const Lut& lv,
+                                  NuqState<GQ>& st, float (*psL)[kGroup], int lane) {
+  const int t = lane & 31;
+  const int64_t gblk = bh * a.cap_blocks + blk;
+  uint32_t kw0[3], kw1[3], vw0[3], vw1[3];
+  {
+    const uint32_t* kp = a.k_codes + (gblk * kHeadDim + 2 * lane) * 3;
+    const uint32_t* vp = a.v_codes + (gblk * kHeadDim + 2 * lane) * 3;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      kw0[i] = kp[i]; kw1[i] = kp[3 + i];
+      vw0[i] = vp[i]; vw1[i] = vp[3 + i];
+    }
+  }
+  const uint32_t vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
+  const int32_t* rp = a.csr_rowptr ? a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1) : nullptr;
+  int32_t r0 = 0, r1 = 0;
+  if (rp) {
+    r0 = rp[t0 + t];
+    r1 = rp[t0 + t + 1];
+  }
+
+  // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
+  // rotated-query partial scores and their sum across lanes
+  float kd0[32], kd1[32];
+#pragma unroll
+  for (int m4 = 0; m4 < 8; ++m4) {
+    uint32_t a01, a23, b01, b23;
+    lut4(lk, codes4(kw0, m4), a01, a23);
+    lut4(lk, codes4(kw1, m4), b01, b23);
+    kd0[4 * m4 + 0] = fmaf(lo_f16(a01), pc.ks0, pc.km0);
+    kd0[4 * m4 + 1] = fmaf(hi_f16(a01), pc.ks0, pc.km0);
+    kd0[4 * m4 + 2] = fmaf(lo_f16(a23), pc.ks0, pc.km0);
+    kd0[4 * m4 + 3] = fmaf(hi_f16(a23), pc.ks0, pc.km0);
+    kd1[4 * m4 + 0] = fmaf(lo_f16(b01), pc.ks1, pc.km1);
+    kd1[4 * m4 + 1] = fmaf(hi_f16(b01), pc.ks1, pc.km1);
+    kd1[4 * m4 + 2] = fmaf(lo_f16(b23), pc.ks1, pc.km1);
+    kd1[4 * m4 + 3] = fmaf(hi_f16(b23), pc.ks1, pc.km1);
+  }
+  const float2 base = rot_at(t0, pc.theta);
+  float s[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float part[32];
+    float2 ar = cmul(pc.q[j], base);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      part[k] = fmaf(ar.x, kd0[k], ar.y * kd1[k]);
+      ar = cmul(ar, pc.step);
+    }
+    s[j] = transpose_sum32(part, lane);
+  }
+
+  // ---- outliers of token t: exact value instead of the dequantized code
+  if (rp && lane < 32) {
+    const int64_t e_end = min((int64_t)r1, a.csr_capacity);
+    for (int64_t e = max(r0, 0); e < e_end; ++e) {
+      const uint32_t ent = a.csr_ent[bh * a.csr_capacity + e];
+      const int col = (int)(ent & (kHeadDim - 1));
+      const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
+      const uint32_t* cw = a.k_codes + (gblk * kHeadDim + col) * 3;
+      const uint32_t cwr[3] = {cw[0], cw[1], cw[2]};
+      const uint32_t km = a.k_meta[bh * kHeadDim + col];
+      const float khat = fmaf(lut_value(a.lut_k, code_at(cwr, t)), lo_f16(km), hi_f16(km));
+      const double th = pow((double)a.rope_theta, -2.0 * (double)(col >> 1) / kHeadDim);
+      const float2 r = rot_at(t0 + t, th);
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) {
+        const uint32_t qq = *reinterpret_cast<const uint32_t*>(
+            a.q + (((bh / a.kv_heads) * a.q_heads + (bh % a.kv_heads) * GQ + j) * kHeadDim +
+                   (col & ~1)));
+        const float2 aq = cmul(make_float2(lo_f16(qq), hi_f16(qq)), r);
+        s[j] += ((col & 1) ? aq.y : aq.x) * (x - khat);
+      }
+    }
+  }
+
+  // ---- softmax (both lane halves carry the corrected score of token t)
+  float p[GQ], alpha[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) s[j] = __shfl(s[j], t) * a.scale_log2;
+  softmax_block<GQ>(st, s, p, alpha);
+
+  // ---- values: p * scale per token into LDS, p * min per lane
+  const float vs = lo_f16(vmeta), vm = hi_f16(vmeta);
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    if (lane < 32) psL[j][t] = p[j] * vs;
+    st.mv[j] = st.mv[j] * alpha[j] + (lane < 32 ? p[j] * vm : 0.0f);
+  }
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
+    const float4* pp = reinterpret_cast<const float4*>(&psL[j][0]);
+#pragma unroll
+    for (int m4 = 0; m4 < 8; ++m4) {
+      const float4 w4 = pp[m4];
+      uint32_t a01, a23, b01, b23;
+      lut4(lv, codes4(vw0, m4), a01, a23);
+      lut4(lv, codes4(vw1, m4), b01, b23);
+      o0 = fmaf(w4.x, lo_f16(a01), o0); o0 = fmaf(w4.y, hi_f16(a01), o0);
+      o0 = fmaf(w4.z, lo_f16(a23), o0); o0 = fmaf(w4.w, hi_f16(a23), o0);
+      o1 = fmaf(w4.x, lo_f16(b01), o1); o1 = fmaf(w4.y, hi_f16(b01), o1);
+      o1 = fmaf(w4.z, lo_f16(b23), o1); o1 = fmaf(w4.w, hi_f16(b23), o1);
+    }
+    st.o[j][0] = o0;
+    st.o[j][1] = o1;
+  }
+}
+
+// Up to 32 fp16 window tokens (positions n_packed + 32 c + j), rotated like the keys.
+template <int GQ>
+__device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
+                                   const PairConsts& pc, NuqState<GQ>& st,
+                                   float (*psL)[kGroup], int lane) {
+  const int t = lane & 31;
+  const int tok0 = c * kGroup;
+  const int nvalid = min(kGroup, a.n_resid - tok0);
+  const int64_t pos0 = (int64_t)a.n_blocks * kGroup + tok0;
+  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
+  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
+  uint32_t kv[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    kv[k] = *reinterpret_cast<const uint32_t*>(kr + min(k, nvalid - 1) * kHeadDim);
+  const float2 base = rot_at(pos0, pc.theta);
+  float s[GQ], p[GQ], alpha[GQ];
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float part[32];
+    float2 ar = cmul(pc.q[j], base);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      part[k] = fmaf(ar.x, lo_f16(kv[k]), ar.y * hi_f16(kv[k]));
+      ar = cmul(ar, pc.step);
+    }
+    s[j] = transpose_sum32(part, lane) * a.scale_log2;
+    if (t >= nvalid) s[j] = kNegInf;
+  }
+  softmax_block<GQ>(st, s, p, alpha);
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    if (lane < 32) psL[j][t] = p[j];
+    st.mv[j] *= alpha[j];
+  }
+  uint32_t vv[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k)
+    vv[k] = *reinterpret_cast<const uint32_t*>(vr + min(k, nvalid - 1) * kHeadDim);
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float pk = psL[j][k];
+      o0 = fmaf(pk, lo_f16(vv[k]), o0);
+      o1 = fmaf(pk, hi_f16(vv[k]), o1);
+    }
+    st.o[j][0] = o0;
+    st.o[j][1] = o1;
+  }
+}
+
+template <int GQ, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
+  constexpr int NT = NW * kWave;
+  __shared__ __align__(16) float psL[NW][GQ][kGroup];
+  __shared__ float wm[NW][GQ], wl[NW][GQ];
+  __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x % a.splits;
+  const int64_t bh = blockIdx.x / a.splits;
+  const int b = (int)(bh / a.kv_heads);
+  const int hkv = (int)(bh % a.kv_heads);
+  const int hq0 = hkv * GQ;
+
+  PairConsts pc;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const uint32_t qq = *reinterpret_cast<const uint32_t*>(
+        a.q + ((int64_t)b * a.q_heads + hq0 + j) * kHeadDim + 2 * lane);
+    pc.q[j] = make_float2(lo_f16(qq), hi_f16(qq));
+  }
+  pc.theta = a.rope_theta > 0.f ? pow((double)a.rope_theta, -2.0 * lane / kHeadDim) : 0.0;
+  {
+    const float2 r1 = rot_at(1, pc.theta);
+    pc.step = r1;
+  }
+  if (a.n_blocks > 0) {
+    const uint2 km = *reinterpret_cast<const uint2*>(a.k_meta + bh * kHeadDim + 2 * lane);
+    pc.ks0 = lo_f16(km.x); pc.km0 = hi_f16(km.x);
+    pc.ks1 = lo_f16(km.y); pc.km1 = hi_f16(km.y);
+  } else {
+    pc.ks0 = pc.km0 = pc.ks1 = pc.km1 = 0.f;
+  }
+  const Lut lk = load_lut(a.lut_k);
+  const Lut lv = load_lut(a.lut_v);
+
+  NuqState<GQ> st;
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    st.m[j] = kNegInf;
+    st.l[j] = 0.f;
+    st.o[j][0] = st.o[j][1] = 0.f;
+    st.mv[j] = 0.f;
+  }
+
+  const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+  const int units = a.n_blocks + kWindowUnits * nchunks;
+  const int s0 = (int)((int64_t)units * split / a.splits);
+  const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
+  const int w0 = s0 + (int)((int64_t)(s1 - s0) * wave / NW);
+  const int w1 = s0 + (int)((int64_t)(s1 - s0) * (wave + 1) / NW);
+  for (int c = 0; c < nchunks; ++c) {
+    const int u = a.n_blocks + kWindowUnits * c;
+    if (u >= w0 && u < w1) process_nuq_window<GQ>(a, bh, c, pc, st, psL[wave], lane);
+  }
+  for (int i = w0; i < min(w1, a.n_blocks); ++i)
+    process_nuq_block<GQ>(a, bh, i, (int64_t)i * kGroup, pc, lk, lv, st, psL[wave], lane);
+
+  // ---- wave totals and the workgroup merge
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const float lt = sum32(lane < 32 ? st.l[j] : 0.0f);
+    const float mvt = sum32(lane < 32 ? st.mv[j] : 0.0f);
+    const float mvall = __shfl(mvt, 0);
+    const float ltall = __shfl(lt, 0);
+    if (lane == 0) {
+      wm[wave][j] = st.m[j];
+      wl[wave][j] = ltall;
+    }
+    *reinterpret_cast<float2*>(&wo[wave][j][2 * lane]) =
+        make_float2(st.o[j][0] + mvall, st.o[j][1] + mvall);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += NT) {
+    const int j = idx >> 7, d = idx & 127;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][j]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float e = exp2f(wm[w][j] - M);
+        L += wl[w][j] * e;
+        O += wo[w][j][d] * e;
+      }
+    }
+    const int64_t row = (int64_t)b * a.q_heads + hq0 + j;
+    if (a.splits == 1) {
+      a.out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+    } else {
+      float* P = a.partials + (row * a.splits + split) * kPartialStride;
+      P[d] = O;
+      if (d == 0) {
+        P[kHeadDim] = M;
+        P[kHeadDim + 1] = L;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, hipStream_t s) {
+  const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
+  const int nw = a.waves_per_group;
+  dim3 grid((unsigned)wgs), block((unsigned)(nw * kWave));
+#define KVQ_DN(G_, NW_)                                                   \
+  if (gq == G_ && nw == NW_) {                                            \
+    decode_nuq_kernel<G_, NW_><<<grid, block, 0, s>>>(a);                 \
+    hipError_t e_ = hipGetLastError();                                    \
+    if (e_ != hipSuccess || a.splits == 1) return e_;                     \
+    return launch_merge_splits(a, s);                                     \
+  }
+  KVQ_DN(1, 4) KVQ_DN(2, 4) KVQ_DN(4, 4) KVQ_DN(8, 4)
+#undef KVQ_DN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -466,8 +466,6 @@ __global__ __launch_bounds__(kHeadDim) void merge_splits_kernel(const float* par
 
 }  // namespace
 
-hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
-
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;

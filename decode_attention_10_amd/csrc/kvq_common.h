@@ -79,6 +79,45 @@ struct DecodeArgs {
 };
 
 constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
+constexpr int kNuqChunk = 2048;                // tokens per chunk in the nuq key passes
+
+struct NuqKeysArgs {
+  const uint16_t* k;        // keys of token 0: element (b, h, t, d) at b*sb + h*sh + t*st + d
+  int64_t sb, sh, st;
+  const uint16_t* lut;      // fp16[8]
+  int32_t kv_heads;
+  int32_t bh_count;         // batch * kv_heads
+  int64_t n_tokens;         // tokens quantized (multiple of 32)
+  int32_t nchunks;          // ceil(n_tokens / kNuqChunk)
+  int64_t k_out;            // outliers per channel
+  int64_t cap_tokens, cap_blocks, csr_capacity;
+  uint32_t* k_codes;
+  uint32_t* k_meta;
+  int32_t* rowptr;          // NULL: no outliers
+  uint32_t* ent;
+  // workspace
+  uint32_t* hist_hi;        // [bh][D][256]
+  uint32_t* hist_lo;        // [bh][D][128]
+  int32_t* thr;             // [bh][D][4]: T, need, high bin, count above
+  float* norm;              // [bh][D][2]: min, 1/scale
+  uint32_t* chunk_stats;    // [bh][nchunks][D][8]
+  uint32_t* tie_prefix;     // [bh][nchunks][D]
+  uint32_t* outmask;        // [bh][cap_tokens][4]
+  uint32_t* chunk_cnt;      // [bh][nchunks]
+  uint32_t* chunk_off;      // [bh][nchunks]
+};
+
+struct NuqValuesArgs {
+  const uint16_t* v;        // values of token tok0
+  int64_t sb, sh, st;
+  const uint16_t* lut;
+  int32_t kv_heads, bh_count;
+  int32_t n_blocks;
+  int64_t tok0;
+  int64_t cap_tokens, cap_blocks;
+  uint32_t* v_codes;
+  uint32_t* v_meta;
+};
 
 // ---- launchers (defined in the .hip files) ------------------------------------
 hipError_t launch_quant_uniform(const QuantArgs& a, int batch, int k_bits, int v_bits,
@@ -86,5 +125,9 @@ hipError_t launch_quant_uniform(const QuantArgs& a, int batch, int k_bits, int v
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s);
+hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s);
+hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s);
+hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, hipStream_t s);
 
 }  // namespace kvq

@@ -1,0 +1,481 @@
+// Non-uniform 3-bit quantizers with per-vector dense-and-sparse outliers.
+//
+// KVQuant review ("KVQuant: Towards 10 Million Context Length LLM Inference with KV
+// Cache Quantization"), abstract items (i)-(iv): keys are quantized per channel and
+// before RoPE, with a non-uniform datatype, and in each vector the largest-magnitude
+// entries are kept in full precision in a sparse matrix; values are quantized per
+// token.  Readings (shared with the oracle): (min, scale) over the dense entries
+// exactly as the uniform quantizer with B = 3; the normalized value (x - min) * inv
+// goes to the nearest code-book level (ties to the even index); a key channel's
+// outliers are its ceil(n * bp / 1e4) largest fp16 magnitudes, ties to lower tokens.
+//
+// Keys (one shot over the whole context, per (batch, head, channel)):
+//   1. magnitude histogram of the top 8 of the 15 magnitude bits, per channel
+//   2. the bin that holds the k-th largest magnitude
+//   3. histogram of the low 7 bits inside that bin  ->  exact threshold T and the
+//      number of elements equal to T that are outliers (the earliest tokens)
+//   4. per chunk of tokens: ties to T, the last positive/negative tie, dense min/max
+//   5. per channel: tie prefix of every chunk, dense min/max -> (scale, min)
+//   6. codes for every element, outlier bitmask per token
+//   7. CSR: per-chunk outlier counts, their scan, then row pointers and entries
+// Every pass reads the keys with coalesced rows; histograms live in LDS and only
+// their non-zero bins reach global memory.
+#include "kvq_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Mids {
+  float m[7];
+};
+
+__device__ __forceinline__ Mids load_mids(const uint16_t* lut) {
+  Mids r;
+#pragma unroll
+  for (int i = 0; i < 7; ++i)
+    r.m[i] = (f16_bits_to_f32(lut[i]) + f16_bits_to_f32(lut[i + 1])) * 0.5f;
+  return r;
+}
+
+// Index of the nearest code-book level (ties to the even index).
+__device__ __forceinline__ uint32_t nuq_code(float xn, const Mids& md) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) c += xn > md.m[i] ? 1u : 0u;
+  float mid_c = md.m[0];
+#pragma unroll
+  for (int i = 1; i < 7; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
+  if (c < 7 && (c & 1u) && xn == mid_c) c += 1;
+  return c;
+}
+
+__device__ __forceinline__ void params3(float mn, float mx, uint32_t* meta, float* mn_o,
+                                        float* inv_o) {
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
+  const uint16_t min_h = f32_to_f16_bits(mn);
+  const uint16_t scale_h = f32_to_f16_bits((mx - mn) / 7.0f);
+  const float s = f16_bits_to_f32(scale_h);
+  *mn_o = mn;
+  *inv_o = (s == 0.0f) ? 0.0f : 1.0f / s;
+  *meta = (uint32_t)scale_h | ((uint32_t)min_h << 16);
+}
+
+__device__ __forceinline__ const uint16_t* key_row(const NuqKeysArgs& a, int64_t bh,
+                                                   int64_t t) {
+  const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
+  return a.k + b * a.sb + h * a.sh + t * a.st;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ---- 1/3: magnitude histograms (LDS counts are u16 pairs packed in u32) ------------
+template <bool LOW>
+__global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
+  __shared__ uint32_t h[kHeadDim][64 + (LOW ? 0 : 64)];   // 256 or 128 bins per channel
+  constexpr int NB = LOW ? 128 : 256;
+  const int64_t bh = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x % a.nchunks;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHeadDim * NB / 2; i += kThreads) (&h[0][0])[i] = 0;
+  int sel0 = -1, sel1 = -1;
+  const int cp = tid & 63;
+  if (LOW) {
+    sel0 = a.thr[(bh * kHeadDim + 2 * cp) * 4 + 2];
+    sel1 = a.thr[(bh * kHeadDim + 2 * cp + 1) * 4 + 2];
+  }
+  __syncthreads();
+  const int64_t t0 = (int64_t)chunk * kNuqChunk;
+  const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  for (int64_t t = t0 + (tid >> 6); t < t1; t += kThreads / 64) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + 2 * cp);
+    const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
+    if (!LOW) {
+      atomicAdd(&h[2 * cp][(m0 >> 7) >> 1], (m0 >> 7) & 1u ? 0x10000u : 1u);
+      atomicAdd(&h[2 * cp + 1][(m1 >> 7) >> 1], (m1 >> 7) & 1u ? 0x10000u : 1u);
+    } else {
+      if ((int)(m0 >> 7) == sel0) atomicAdd(&h[2 * cp][(m0 & 127u) >> 1], m0 & 1u ? 0x10000u : 1u);
+      if ((int)(m1 >> 7) == sel1) atomicAdd(&h[2 * cp + 1][(m1 & 127u) >> 1], m1 & 1u ? 0x10000u : 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* g = LOW ? a.hist_lo : a.hist_hi;
+  for (int i = tid; i < kHeadDim * NB / 2; i += kThreads) {
+    const uint32_t v = (&h[0][0])[i];
+    if (v == 0) continue;
+    const int d = i / (NB / 2), b2 = i % (NB / 2);
+    uint32_t* row = g + (bh * kHeadDim + d) * NB;
+    if (v & 0xFFFFu) atomicAdd(&row[2 * b2], v & 0xFFFFu);
+    if (v >> 16) atomicAdd(&row[2 * b2 + 1], v >> 16);
+  }
+}
+
+// ---- 2/3: thresholds.  thr[(bh*D + d)*4 + {0: T, 1: need, 2: high bin, 3: count above}]
+// T = -1: every element is an outlier; T = 0x8000: none is.
+__global__ void nuq_select_kernel(NuqKeysArgs a, int pass) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.bh_count * kHeadDim) return;
+  int32_t* th = a.thr + i * 4;
+  const int64_t k = a.k_out;
+  if (pass == 0) {
+    th[2] = -1;
+    th[3] = 0;
+    if (k <= 0) { th[0] = 0x8000; th[1] = 0; return; }
+    if (k >= a.n_tokens) { th[0] = -1; th[1] = 0; return; }
+    const uint32_t* hh = a.hist_hi + i * 256;
+    int64_t cum = 0;
+    for (int b = 255; b >= 0; --b) {
+      const int64_t c = hh[b];
+      if (cum + c >= k) { th[2] = b; th[3] = (int32_t)cum; break; }
+      cum += c;
+    }
+  } else {
+    if (th[2] < 0) return;
+    const uint32_t* hl = a.hist_lo + i * 128;
+    int64_t cum = th[3];
+    for (int b = 127; b >= 0; --b) {
+      const int64_t c = hl[b];
+      if (cum + c >= k) {
+        th[0] = (th[2] << 7) | b;
+        th[1] = (int32_t)(k - cum);
+        break;
+      }
+      cum += c;
+    }
+  }
+}
+
+// Stage a 32-token block of keys in LDS.
+__device__ __forceinline__ void load_key_tile(uint16_t (*tile)[kHeadDim], const NuqKeysArgs& a,
+                                              int64_t bh, int64_t t0) {
+  const int t = threadIdx.x >> 3, c = (threadIdx.x & 7) * 16;
+  const uint4* p = reinterpret_cast<const uint4*>(key_row(a, bh, t0 + t) + c);
+  const uint4 u0 = p[0], u1 = p[1];
+  uint4* d = reinterpret_cast<uint4*>(&tile[t][c]);
+  d[0] = u0;
+  d[1] = u1;
+}
+
+// ---- 4: per chunk: ties, last positive / negative tie, dense min / max ----------------
+__global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a) {
+  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
+  const int64_t bh = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x % a.nchunks;
+  const int d = threadIdx.x;
+  int T = 0x8000;
+  if (d < kHeadDim) T = a.thr[(bh * kHeadDim + d) * 4];
+  uint32_t ties = 0;
+  int32_t last_pos = -1, last_neg = -1;
+  float dmin = __builtin_inff(), dmax = -__builtin_inff();
+  const int64_t t0 = (int64_t)chunk * kNuqChunk;
+  const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  for (int64_t tb = t0; tb < t1; tb += kGroup) {
+    load_key_tile(tile, a, bh, tb);
+    __syncthreads();
+    if (d < kHeadDim) {
+      for (int j = 0; j < kGroup; ++j) {
+        const uint16_t x = tile[j][d];
+        const int mag = x & 0x7FFF;
+        if (mag < T) {
+          const float v = f16_bits_to_f32(x);
+          dmin = fminf(dmin, v);
+          dmax = fmaxf(dmax, v);
+        } else if (mag == T) {
+          if (x & 0x8000u) last_neg = (int32_t)ties; else last_pos = (int32_t)ties;
+          ++ties;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (d < kHeadDim) {
+    uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + d) * 8;
+    cs[0] = ties;
+    cs[1] = (uint32_t)last_pos;
+    cs[2] = (uint32_t)last_neg;
+    cs[3] = __builtin_bit_cast(uint32_t, dmin);
+    cs[4] = __builtin_bit_cast(uint32_t, dmax);
+  }
+}
+
+// ---- 5: per channel: tie prefix of each chunk, dense min / max, (scale, min) ----------
+__global__ void nuq_finalize_kernel(NuqKeysArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.bh_count * kHeadDim) return;
+  const int64_t bh = i / kHeadDim;
+  const int d = (int)(i % kHeadDim);
+  const int T = a.thr[i * 4];
+  const int64_t need = a.thr[i * 4 + 1];
+  int64_t prefix = 0, last_pos = -1, last_neg = -1;
+  float dmin = __builtin_inff(), dmax = -__builtin_inff();
+  for (int c = 0; c < a.nchunks; ++c) {
+    const uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + c) * kHeadDim + d) * 8;
+    a.tie_prefix[(bh * a.nchunks + c) * kHeadDim + d] = (uint32_t)prefix;
+    const int32_t lp = (int32_t)cs[1], ln = (int32_t)cs[2];
+    if (lp >= 0) last_pos = max(last_pos, prefix + lp);
+    if (ln >= 0) last_neg = max(last_neg, prefix + ln);
+    prefix += cs[0];
+    dmin = fminf(dmin, __builtin_bit_cast(float, cs[3]));
+    dmax = fmaxf(dmax, __builtin_bit_cast(float, cs[4]));
+  }
+  if (T >= 0 && T < 0x8000) {          // ties ranked need.. are dense
+    const float tv = f16_bits_to_f32((uint16_t)T);
+    if (last_pos >= need) { dmin = fminf(dmin, tv); dmax = fmaxf(dmax, tv); }
+    if (last_neg >= need) { dmin = fminf(dmin, -tv); dmax = fmaxf(dmax, -tv); }
+  }
+  if (!(dmin <= dmax)) { dmin = 0.0f; dmax = 0.0f; }     // no dense entry
+  uint32_t meta;
+  float mn, inv;
+  params3(dmin, dmax, &meta, &mn, &inv);
+  a.k_meta[bh * kHeadDim + d] = meta;
+  a.norm[i * 2] = mn;
+  a.norm[i * 2 + 1] = inv;
+}
+
+// Pack one channel's 32 codes (LDS tile [token][channel] of bytes) into word w.
+__device__ __forceinline__ uint32_t pack_nuq3_word(const uint8_t (*ct)[kHeadDim], int d, int w) {
+  uint32_t bits = 0;
+  if (w < 2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      bits |= (uint32_t)(ct[16 * w + j][d] & 3u) << (8 * (j & 3) + 2 * (j >> 2));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      bits |= (uint32_t)(ct[j][d] >> 2) << (8 * (j & 3) + (j >> 2));
+  }
+  return bits;
+}
+
+// ---- 6: codes and outlier bitmask ---------------------------------------------------
+__global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a) {
+  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
+  __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
+  __shared__ uint32_t om[kGroup][4];
+  const int64_t bh = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x % a.nchunks;
+  const int tid = threadIdx.x;
+  const Mids md = load_mids(a.lut);
+  int T = 0x8000, need = 0;
+  uint32_t rank = 0;
+  float mn = 0.f, inv = 0.f;
+  if (tid < kHeadDim) {
+    const int64_t i = bh * kHeadDim + tid;
+    T = a.thr[i * 4];
+    need = a.thr[i * 4 + 1];
+    rank = a.tie_prefix[(bh * a.nchunks + chunk) * kHeadDim + tid];
+    mn = a.norm[i * 2];
+    inv = a.norm[i * 2 + 1];
+  }
+  const int64_t t0 = (int64_t)chunk * kNuqChunk;
+  const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  for (int64_t tb = t0; tb < t1; tb += kGroup) {
+    load_key_tile(tile, a, bh, tb);
+    if (tid < kGroup * 4) om[tid >> 2][tid & 3] = 0;
+    __syncthreads();
+    if (tid < kHeadDim) {
+      for (int j = 0; j < kGroup; ++j) {
+        const uint16_t x = tile[j][tid];
+        const int mag = x & 0x7FFF;
+        bool out = mag > T;
+        if (mag == T) {
+          out = rank < (uint32_t)need;
+          ++rank;
+        }
+        const uint32_t c = inv == 0.0f ? 0u : nuq_code((f16_bits_to_f32(x) - mn) * inv, md);
+        ct[j][tid] = (uint8_t)c;
+        if (out) atomicOr(&om[j][tid >> 5], 1u << (tid & 31));
+      }
+    }
+    __syncthreads();
+    const int64_t blk = bh * a.cap_blocks + tb / kGroup;
+    for (int wi = tid; wi < kHeadDim * 3; wi += kThreads)
+      a.k_codes[blk * (kHeadDim * 3) + wi] = pack_nuq3_word(ct, wi / 3, wi % 3);
+    if (tid < kGroup * 4)
+      a.outmask[(bh * a.cap_tokens + tb + (tid >> 2)) * 4 + (tid & 3)] = om[tid >> 2][tid & 3];
+    __syncthreads();
+  }
+}
+
+// ---- 7: CSR -------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t row_count(const NuqKeysArgs& a, int64_t bh, int64_t t) {
+  const uint4 m = *reinterpret_cast<const uint4*>(a.outmask + (bh * a.cap_tokens + t) * 4);
+  return __popc(m.x) + __popc(m.y) + __popc(m.z) + __popc(m.w);
+}
+
+__global__ __launch_bounds__(kThreads) void csr_count_kernel(NuqKeysArgs a) {
+  __shared__ uint32_t part[kThreads / kWave];
+  const int64_t bh = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x % a.nchunks;
+  const int64_t t0 = (int64_t)chunk * kNuqChunk;
+  const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  uint32_t s = 0;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) s += row_count(a, bh, t);
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) tot += part[w];
+    a.chunk_cnt[bh * a.nchunks + chunk] = tot;
+  }
+}
+
+// One workgroup per (batch, head): exclusive scan of the chunk counts.
+__global__ __launch_bounds__(kThreads) void csr_scan_kernel(NuqKeysArgs a) {
+  const int64_t bh = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  uint32_t run = 0;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const uint32_t v = a.chunk_cnt[bh * a.nchunks + c];
+    a.chunk_off[bh * a.nchunks + c] = run;
+    run += v;
+  }
+  a.rowptr[bh * (a.cap_tokens + 1) + a.n_tokens] = (int32_t)run;
+}
+
+// Row pointers and entries of one chunk (entries: channel | fp16 value << 16).
+__global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
+  constexpr int PER = kNuqChunk / kThreads;   // consecutive tokens per thread
+  __shared__ uint32_t scan[kThreads];
+  const int64_t bh = blockIdx.x / a.nchunks;
+  const int chunk = blockIdx.x % a.nchunks;
+  const int64_t t0 = (int64_t)chunk * kNuqChunk + (int64_t)threadIdx.x * PER;
+  const int64_t tend = min((int64_t)a.n_tokens, (int64_t)(chunk + 1) * kNuqChunk);
+  uint32_t cnt[PER];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    cnt[i] = (t0 + i < tend) ? row_count(a, bh, t0 + i) : 0u;
+    mine += cnt[i];
+  }
+  scan[threadIdx.x] = mine;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {       // inclusive Hillis-Steele scan
+    const uint32_t v = threadIdx.x >= o ? scan[threadIdx.x - o] : 0u;
+    __syncthreads();
+    scan[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int64_t pos = (int64_t)a.chunk_off[bh * a.nchunks + chunk] + scan[threadIdx.x] - mine;
+  int32_t* rp = a.rowptr + bh * (a.cap_tokens + 1);
+  uint32_t* ent = a.ent + bh * a.csr_capacity;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int64_t t = t0 + i;
+    if (t >= tend) break;
+    rp[t] = (int32_t)pos;
+    if (cnt[i] == 0) continue;
+    const uint4 m = *reinterpret_cast<const uint4*>(a.outmask + (bh * a.cap_tokens + t) * 4);
+    const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+    const uint16_t* row = key_row(a, bh, t);
+    for (int w = 0; w < 4; ++w) {
+      uint32_t bits = mw[w];
+      while (bits) {
+        const int d = 32 * w + __builtin_ctz(bits);
+        bits &= bits - 1;
+        if (pos < a.csr_capacity) ent[pos] = (uint32_t)d | ((uint32_t)row[d] << 16);
+        ++pos;
+      }
+    }
+  }
+}
+
+// ---- values: per token over all channels --------------------------------------------
+__global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArgs a) {
+  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
+  __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
+  __shared__ float2 st[kGroup];
+  const int64_t job = blockIdx.x;
+  const int blk = (int)(job % a.n_blocks);
+  const int64_t bh = job / a.n_blocks;
+  const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
+  const int tid = threadIdx.x;
+  const Mids md = load_mids(a.lut);
+  {
+    const int t = tid >> 3, c = (tid & 7) * 16;
+    const uint4* p = reinterpret_cast<const uint4*>(a.v + b * a.sb + h * a.sh +
+                                                    ((int64_t)blk * kGroup + t) * a.st + c);
+    const uint4 u0 = p[0], u1 = p[1];
+    uint4* dd = reinterpret_cast<uint4*>(&tile[t][c]);
+    dd[0] = u0;
+    dd[1] = u1;
+  }
+  __syncthreads();
+  {
+    // 8 threads per token (same wave): min / max of 16 channels each, then combine
+    const int t = tid >> 3, part = tid & 7;
+    float mn = f16_bits_to_f32(tile[t][part * 16]), mx = mn;
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+      const float x = f16_bits_to_f32(tile[t][part * 16 + j]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (part == 0) {
+      uint32_t meta;
+      float m0, inv;
+      params3(mn, mx, &meta, &m0, &inv);
+      a.v_meta[bh * a.cap_tokens + a.tok0 + (int64_t)blk * kGroup + t] = meta;
+      st[t] = make_float2(m0, inv);
+    }
+  }
+  __syncthreads();
+  {
+    const int t = tid >> 3, c0 = (tid & 7) * 16;
+    const float2 g = st[t];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x = f16_bits_to_f32(tile[t][c0 + j]);
+      ct[t][c0 + j] = (uint8_t)(g.y == 0.0f ? 0u : nuq_code((x - g.x) * g.y, md));
+    }
+  }
+  __syncthreads();
+  const int64_t dst = bh * a.cap_blocks + a.tok0 / kGroup + blk;
+  for (int wi = tid; wi < kHeadDim * 3; wi += kThreads)
+    a.v_codes[dst * (kHeadDim * 3) + wi] = pack_nuq3_word(ct, wi / 3, wi % 3);
+}
+
+inline unsigned grid1(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
+  const int64_t bhd = (int64_t)a.bh_count * kHeadDim;
+  const unsigned jobs = (unsigned)((int64_t)a.bh_count * a.nchunks);
+  fill_u32_kernel<<<dim3(1024), dim3(kThreads), 0, s>>>(a.hist_hi, bhd * 256, 0u);
+  fill_u32_kernel<<<dim3(1024), dim3(kThreads), 0, s>>>(a.hist_lo, bhd * 128, 0u);
+  nuq_hist_kernel<false><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 0);
+  nuq_hist_kernel<true><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 1);
+  nuq_chunk_stats_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  nuq_finalize_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
+  nuq_quant_keys_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  if (a.rowptr != nullptr) {
+    csr_count_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+    csr_scan_kernel<<<dim3((unsigned)a.bh_count), dim3(kThreads), 0, s>>>(a);
+    csr_fill_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s) {
+  const int64_t jobs = (int64_t)a.bh_count * a.n_blocks;
+  if (jobs == 0) return hipSuccess;
+  nuq_quant_values_kernel<<<dim3((unsigned)jobs), dim3(kThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -194,34 +194,44 @@ def unpack_v_codes(words: np.ndarray, bits: int) -> np.ndarray:
     return np.swapaxes(c, -1, -2).reshape(*lead, nb * GROUP, d)
 
 
-def pack_nuq3_k(codes: np.ndarray) -> np.ndarray:
-    """nuq3 key codes [..., N, D] -> [..., N/32, 32, 3*D/32 words]: per token, the low two
-    bits of every channel as in the 2-bit layout (D/16 words), then the high bit of
-    every channel, channel d at bit d % 32 of word D/16 + d // 32."""
-    lo = pack_k_codes(codes & 3, 2)
-    hi = pack_k_codes(codes >> 2, 1)
-    return np.concatenate([lo, hi], axis=-1)
+def nuq3_bit_positions():
+    """Bit positions (word, low bit) of token j's code in a channel's three 3-bit-code words.
+
+    Word 0 holds the low two bits of tokens 0..15, word 1 those of tokens 16..31: token
+    j of the half sits at bit 8*(j % 4) + 2*(j // 4).  Word 2 holds the high bits of all
+    32 tokens: token j at bit 8*(j % 4) + j // 4.  (So a shift and one mask bring four
+    consecutive tokens' bits into the four bytes of a word.)"""
+    lo = [(j // 16, 8 * ((j % 16) % 4) + 2 * ((j % 16) // 4)) for j in range(32)]
+    hi = [(2, 8 * (j % 4) + j // 4) for j in range(32)]
+    return lo, hi
 
 
-def unpack_nuq3_k(words: np.ndarray, d: int) -> np.ndarray:
-    nlo = d // 16
-    lo = unpack_k_codes(words[..., :nlo], 2, d)
-    hi = unpack_k_codes(words[..., nlo:], 1, d)
-    return (lo | (hi << 2)).astype(np.uint8)
+def pack_nuq3(codes: np.ndarray) -> np.ndarray:
+    """3-bit codes [..., N, D] -> [..., N/32, D, 3 words] (per block, channel-major)."""
+    *lead, n, d = codes.shape
+    blk = np.swapaxes(codes.reshape(*lead, n // GROUP, GROUP, d), -1, -2).astype(np.uint64)
+    lo, hi = nuq3_bit_positions()
+    words = np.zeros((*blk.shape[:-1], 3), dtype=np.uint64)
+    for j in range(GROUP):
+        w, b = lo[j]
+        words[..., w] |= (blk[..., j] & np.uint64(3)) << np.uint64(b)
+        w, b = hi[j]
+        words[..., w] |= (blk[..., j] >> np.uint64(2)) << np.uint64(b)
+    return words.astype(np.uint32)
 
 
-def pack_nuq3_v(codes: np.ndarray) -> np.ndarray:
-    """nuq3 value codes [..., N, D] -> [..., N/32, D, 3 words]: per channel, words 0-1 hold the
-    low two bits of the block's 32 tokens (2-bit layout) and word 2 their high bits."""
-    lo = pack_v_codes(codes & 3, 2)
-    hi = pack_v_codes(codes >> 2, 1)
-    return np.concatenate([lo, hi], axis=-1)
-
-
-def unpack_nuq3_v(words: np.ndarray) -> np.ndarray:
-    lo = unpack_v_codes(words[..., :2], 2)
-    hi = unpack_v_codes(words[..., 2:], 1)
-    return (lo | (hi << 2)).astype(np.uint8)
+def unpack_nuq3(words: np.ndarray) -> np.ndarray:
+    *lead, nb, d, _ = words.shape
+    lo, hi = nuq3_bit_positions()
+    w64 = words.astype(np.uint64)
+    out = np.zeros((*lead, nb, d, GROUP), dtype=np.uint8)
+    for j in range(GROUP):
+        wl, bl = lo[j]
+        wh, bh = hi[j]
+        c = ((w64[..., wl] >> np.uint64(bl)) & np.uint64(3)) | \
+            (((w64[..., wh] >> np.uint64(bh)) & np.uint64(1)) << np.uint64(2))
+        out[..., j] = c.astype(np.uint8)
+    return np.swapaxes(out, -1, -2).reshape(*lead, nb * GROUP, d)
 
 
 # --------------------------------------------------------------------------
@@ -475,4 +485,37 @@ def uniform_cache(k_bits, v_bits, k_b, v_b, n_packed, n_resid):
         "v_meta": pack_meta(vs, vm),
         "k_hat": np.concatenate([kd, f16_to_f32(kr)], axis=2),
         "v_hat": np.concatenate([vd, f16_to_f32(vr)], axis=2),
+    }
+
+
+def rope_query_f16(q_bits: np.ndarray, position: int, theta: float) -> np.ndarray:
+    """The query of the token at ``position``, rotated in float64 and rounded to fp16 bits
+    (the decode call receives it already rotated)."""
+    q = f16_to_f32(q_bits).astype(np.float64)
+    shp = q.shape
+    r = rope_f64(q.reshape(-1, 1, shp[-1]), np.array([position]), theta)
+    return f32_to_f16_bits(r.reshape(shp).astype(np.float32))
+
+
+def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: np.ndarray,
+             outlier_bp: int, n_packed: int, n_resid: int, theta: float):
+    """One (batch, head) of a KVQuant-style cache: tokens [0, n_packed) quantized (keys per
+    channel with outliers, values per token), tokens [n_packed, n_packed + n_resid) kept in
+    fp16.  Returns the packed buffers and the float64 keys (RoPE applied at positions
+    0.. when theta > 0) and values attention reads."""
+    kp, vp = k_bits[:n_packed], v_bits[:n_packed]
+    kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp)
+    vc, vs, vm, vx = nuq_quantize_values(vp, lut_v)
+    kw = k_bits[n_packed:n_packed + n_resid]
+    vw = v_bits[n_packed:n_packed + n_resid]
+    k_hat = np.concatenate([kx, f16_to_f32(kw)], axis=0).astype(np.float64)
+    v_hat = np.concatenate([vx, f16_to_f32(vw)], axis=0).astype(np.float64)
+    if theta > 0:
+        k_hat = rope_f64(k_hat, np.arange(n_packed + n_resid), theta)
+    return {
+        "k_codes": pack_nuq3(kc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
+        "k_meta": pack_meta(ks, km),
+        "v_codes": pack_nuq3(vc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
+        "v_meta": pack_meta(vs, vm),
+        "rowptr": rp, "ent": ent, "k_hat": k_hat, "v_hat": v_hat,
     }

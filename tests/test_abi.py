@@ -177,7 +177,6 @@ def test_decode_argument_errors():
         (dict(scale=float("inf")), K.KVQ_ERR_INVALID_ARG),
         (dict(q=FAKE + 4), K.KVQ_ERR_ALIGNMENT),
         (dict(out=None), K.KVQ_ERR_INVALID_ARG),
-        (dict(ws=None), K.KVQ_ERR_INVALID_ARG),
     ]
     for kw, status in cases:
         a = dict(hq=3, theta=0.0, scale=0.1, q=FAKE, out=FAKE, ws=FAKE, wsb=1 << 20)
@@ -186,3 +185,17 @@ def test_decode_argument_errors():
             K.kvq_decode_attn(c, a["q"], a["hq"], a["scale"], a["theta"], a["out"], a["ws"],
                               a["wsb"], stream=0)
         assert e.value.status == status, kw
+
+
+def test_decode_needs_workspace_for_split_contexts():
+    """A long context over few heads is split across workgroups: the partials need the
+    workspace, so a missing or short one is rejected before any launch."""
+    c = _desc(B=1, H=1, cap=1 << 20)
+    _fake_buffers(c)
+    c.n_packed, c.n_resid = 1 << 20, 0
+    need = K.kvq_workspace_bytes(c, 1, K.KVQ_OP_DECODE_ATTN)
+    assert need > 0
+    for ws, wsb in [(None, need), (FAKE, need - 4)]:
+        with pytest.raises(K.KvqError) as e:
+            K.kvq_decode_attn(c, FAKE, 1, 0.1, 0.0, FAKE, ws, wsb, stream=0)
+        assert e.value.status == K.KVQ_ERR_INVALID_ARG

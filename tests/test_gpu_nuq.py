@@ -1,0 +1,137 @@
+"""GPU parity of the KVQuant-style path (nuq3 codes, per-channel pre-RoPE keys with
+dense-and-sparse outliers, per-token values, RoPE after dequantization) against the
+oracle, through the C ABI.  Codes, metadata and CSR must be bit-exact; attention
+outputs within |o - ref| <= 2e-3 + 1e-2 |ref|."""
+import numpy as np
+import pytest
+
+import kvq_synth as S
+from oracle import kvq_oracle as O
+from tests.kvq_testlib import assert_close, dev, host_words
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+K = pytest.importorskip("decode_attention_10_amd")
+
+IDENT = np.arange(8).astype(np.float16).view(np.uint16)
+
+
+def _kv(seed, B, H, T, D=128, n_out=3, gain=100.0):
+    g = S.key_gains(seed, H, D, n_out, gain)
+    return (S.gen_tensor(seed, S.TID_K, B, H, T, D, gains=g),
+            S.gen_tensor(seed, S.TID_V, B, H, T, D))
+
+
+def _nuq_cache(B, H, cap, R, bp, lut_k, lut_v):
+    lk, lv = dev(lut_k), dev(lut_v)
+    c = K.KVCache(B, H, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
+                  outlier_bp=bp)
+    c.c.vq.lut = lv.data_ptr()
+    c.luts = (lk, lv)
+    return c
+
+
+def _quantize(c, k, v, n):
+    B, H, T, D = k.shape
+    kd, vd = dev(k), dev(v)
+    wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    K.kvq_quantize_keys(c.c, kd, H * T * D, T * D, D, 0, n, ws, wsb)
+    K.kvq_quantize_values(c.c, vd, H * T * D, T * D, D, 0, n)
+    torch.cuda.synchronize()
+    return kd, vd
+
+
+def _check_head(c, b, h, ref, n, bp):
+    B, H = c.c.batch, c.c.kv_heads
+    cap = c.c.capacity_tokens
+    kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 128, 3)
+    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, 128, 3)
+    km = host_words(c.buf("k_meta")).reshape(B, H, 128)
+    vm = host_words(c.buf("v_meta")).reshape(B, H, cap)
+    assert np.array_equal(kw[b, h, :n // 32], ref["k_codes"]), "key codes"
+    assert np.array_equal(km[b, h], ref["k_meta"]), "key scale/min"
+    assert np.array_equal(vw[b, h, :n // 32], ref["v_codes"]), "value codes"
+    assert np.array_equal(vm[b, h, :n], ref["v_meta"]), "value scale/min"
+    if bp:
+        rp = c.buf("k_csr_rowptr").cpu().numpy().view(np.int32).reshape(B, H, cap + 1)
+        ent = host_words(c.buf("k_csr_ent")).reshape(B, H, -1)
+        assert np.array_equal(rp[b, h, :n + 1], ref["rowptr"]), "CSR row pointers"
+        nnz = int(ref["rowptr"][-1])
+        assert np.array_equal(ent[b, h, :nnz], ref["ent"]), "CSR entries"
+
+
+@pytest.mark.parametrize("B,H,n,bp,lut", [
+    (1, 1, 64, 0, "ident"), (2, 2, 96, 100, "nf"), (1, 3, 4160, 100, "nf"),
+    (1, 2, 2048 + 256, 250, "nf"), (1, 1, 64, 10000, "nf"), (2, 1, 320, 5000, "ident")])
+def test_nuq_quantize_bit_exact(B, H, n, bp, lut):
+    k, v = _kv(200 + n + bp, B, H, n)
+    L = IDENT if lut == "ident" else S.nuq3_lut()
+    c = _nuq_cache(B, H, n + 64, 0, bp, L, L)
+    _quantize(c, k, v, n)
+    for b in range(B):
+        for h in range(H):
+            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, n, 0, 0.0)
+            _check_head(c, b, h, ref, n, bp)
+
+
+def test_nuq_keys_many_ties_at_the_threshold():
+    """Values drawn from a few levels so that the k-th largest magnitude is shared by
+    many tokens: the earliest ones must become the outliers."""
+    B, H, n = 1, 2, 4096 + 64
+    rng = np.random.default_rng(9)
+    x = rng.choice([-2.0, -1.0, -0.5, 0.0, 0.25, 1.0, 2.0, 3.0], size=(B, H, n, 128))
+    k = x.astype(np.float16).view(np.uint16)
+    v = S.gen_tensor(9, S.TID_V, B, H, n, 128)
+    L = S.nuq3_lut()
+    c = _nuq_cache(B, H, n, 0, 150, L, L)
+    _quantize(c, k, v, n)
+    for h in range(H):
+        _check_head(c, 0, h, O.nuq_head(k[0, h], v[0, h], L, L, 150, n, 0, 0.0), n, 150)
+
+
+DECODE = [
+    # B, Hkv, GQ, n_packed, n_resid, R, bp, theta
+    (1, 1, 1, 512, 0, 0, 100, 1e4),
+    (1, 2, 1, 2048, 0, 0, 100, 1e4),
+    (2, 2, 2, 1024, 37, 64, 100, 1e4),
+    (1, 2, 4, 4096, 0, 0, 250, 1e4),
+    (1, 1, 1, 256, 5, 32, 0, 0.0),
+    (1, 2, 1, 0, 20, 32, 100, 1e4),
+    (1, 1, 8, 2048, 0, 0, 100, 500000.0),
+]
+
+
+@pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,theta", DECODE)
+def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
+    seed = 300 + N + r + GQ
+    k, v = _kv(seed, B, Hkv, N + r)
+    L = S.nuq3_lut()
+    cap = max(32, N)
+    c = _nuq_cache(B, Hkv, cap, R, bp, L, L)
+    if N:
+        _quantize(c, k, v, N)
+    if r:
+        kd, vd = dev(k), dev(v)
+        c.buf("k_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = kd[:, :, N:N + r]
+        c.buf("v_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = vd[:, :, N:N + r]
+    c.c.n_packed, c.c.n_resid = N, r
+    q0 = S.gen_tensor(seed, S.TID_Q, B, Hkv * GQ, 1, 128)[:, :, 0]
+    q = O.rope_query_f16(q0, N + r, theta) if theta > 0 else q0
+    out = torch.full((B, Hkv * GQ, 128), float("nan"), device="cuda")
+    wsb = K.kvq_workspace_bytes(c.c, Hkv * GQ, K.KVQ_OP_DECODE_ATTN)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    sm = O.default_sm_scale(128)
+    K.kvq_decode_attn(c.c, dev(q), Hkv * GQ, sm, theta, out, ws, wsb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    kh = np.zeros((B, Hkv, N + r, 128))
+    vh = np.zeros((B, Hkv, N + r, 128))
+    for b in range(B):
+        for h in range(Hkv):
+            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta)
+            kh[b, h], vh[b, h] = ref["k_hat"], ref["v_hat"]
+    want = O.decode_attention_f64(O.f16_to_f32(q), kh, vh, sm)
+    assert np.isfinite(got).all()
+    assert_close(got, want, f"nuq decode B{B} Hkv{Hkv} GQ{GQ} N{N} r{r} bp{bp} theta{theta}")

@@ -117,3 +117,22 @@ def test_all_outliers_degenerate():
     c, s, m, oi, xh = O.nuq_quantize_vector(x, S.nuq3_lut(), 3)
     assert s == 0 and m == 0 and not c.any()
     assert np.array_equal(xh, O.f16_to_f32(x))
+
+
+def test_nuq_head_identity_lut_no_outliers_is_per_channel_int3_over_context():
+    """With the identity code book, no outliers and no RoPE, a head's keys are the uniform
+    3-bit quantizer applied to each channel over the whole context."""
+    k = S.gen_tensor(31, S.TID_K, 1, 1, 96, 128)[0, 0]
+    v = S.gen_tensor(31, S.TID_V, 1, 1, 96, 128)[0, 0]
+    h = O.nuq_head(k, v, IDENT, IDENT, 0, 64, 32, 0.0)
+    cu, su, mu = O.uniform_quantize_groups(k[:64].T, 3)      # groups = channels over tokens
+    assert np.allclose(h["k_hat"][:64], O.uniform_dequant(cu, su, mu).T)
+    assert np.array_equal(h["k_hat"][64:], O.f16_to_f32(k[64:]))
+
+
+def test_rope_query_rounds_rotation():
+    q = S.gen_tensor(2, S.TID_Q, 1, 2, 1, 128)[:, :, 0]
+    r = O.rope_query_f16(q, 1000, 1e4)
+    ref = O.rope_f64(O.f16_to_f32(q).astype(np.float64)[0][:, None, :], np.array([1000]), 1e4)
+    assert np.array_equal(r[0], O.f32_to_f16_bits(ref[:, 0, :].astype(np.float32)))
+    assert np.array_equal(O.rope_query_f16(q, 0, 1e4), q)

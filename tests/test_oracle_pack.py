@@ -38,12 +38,31 @@ def test_v_pack_round_trip(bits):
 def test_nuq3_pack_round_trip():
     rng = np.random.default_rng(3)
     c = rng.integers(0, 8, (1, 2, 96, 128)).astype(np.uint8)
-    wk = O.pack_nuq3_k(c)
-    assert wk.shape == (1, 2, 3, 32, 12)
-    assert np.array_equal(O.unpack_nuq3_k(wk, 128), c)
-    wv = O.pack_nuq3_v(c)
-    assert wv.shape == (1, 2, 3, 128, 3)
-    assert np.array_equal(O.unpack_nuq3_v(wv), c)
+    w = O.pack_nuq3(c)
+    assert w.shape == (1, 2, 3, 128, 3)
+    assert np.array_equal(O.unpack_nuq3(w), c)
+
+
+def test_nuq3_layout_bit_positions_by_hand():
+    c = np.zeros((32, 128), np.uint8)
+    c[0, 3] = 7          # token 0: word 0 bits 0-1 (=3), word 2 bit 0
+    c[5, 3] = 2          # token 5: byte 1, bits 8+2 = 10..11 of word 0
+    c[21, 3] = 5         # token 21 (16 + 5): word 1 bits 10..11 (=1); high bit: byte 1, bit 5 -> 13
+    c[31, 4] = 4         # token 31: high bit only, byte 3, bit 7 -> bit 31 of word 2
+    w = O.pack_nuq3(c)[0]
+    assert int(w[3, 0]) == 0x3 | (2 << 10)
+    assert int(w[3, 1]) == (1 << 10)
+    assert int(w[3, 2]) == 1 | (1 << 13)
+    assert int(w[4, 2]) == 1 << 31 and int(w[4, 0]) == 0 and int(w[4, 1]) == 0
+    # one shift and mask give four consecutive tokens' low bits in the four bytes
+    rng = np.random.default_rng(4)
+    cc = rng.integers(0, 8, (32, 128)).astype(np.uint8)
+    ww = O.pack_nuq3(cc)[0]
+    for m in range(8):
+        lo = (int(ww[9, m // 4]) >> (2 * (m % 4))) & 0x03030303
+        hi = (int(ww[9, 2]) >> m) & 0x01010101
+        codes = lo | (hi << 2)
+        assert [(codes >> (8 * k)) & 0xFF for k in range(4)] == list(cc[4 * m:4 * m + 4, 9])
 
 
 def test_k_layout_bit_positions_by_hand():
@@ -85,7 +104,7 @@ def test_packed_bytes_per_element():
     for bits in (2, 4):
         assert O.pack_k_codes(c, bits).nbytes == 4096 * 128 * bits // 8
         assert O.pack_v_codes(c, bits).nbytes == 4096 * 128 * bits // 8
-    assert O.pack_nuq3_k(c).nbytes == 4096 * 128 * 3 // 8
+    assert O.pack_nuq3(c).nbytes == 4096 * 128 * 3 // 8
 
 
 def test_kvquant_table_byte_accounting():
