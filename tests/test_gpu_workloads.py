@@ -1,0 +1,205 @@
+"""The five synthetic workloads at their full sizes, on the GPU, through the C ABI in the
+launch configuration the benchmark uses.  The oracle checks sampled (batch, head)
+units one by one: packed bytes bit-exact, attention rows within the tolerance.
+Inputs are generated on the device; the oracle regenerates the sampled slices on the
+host from the same counter-based generator."""
+import numpy as np
+import pytest
+
+import kvq_synth as S
+from oracle import kvq_oracle as O
+from tests.kvq_testlib import assert_close, dev, host_words
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+K = pytest.importorskip("decode_attention_10_amd")
+
+
+def test_device_generator_matches_host_generator():
+    g = S.key_gains(5, 3, 128, 3, 100.0)
+    want = S.gen_tensor(5, S.TID_K, 2, 3, 70, 128, gains=g, t0=1000)
+    out = torch.empty((2, 3, 70, 128), dtype=torch.int16, device="cuda")
+    S.fill_device(out, 5, S.TID_K, 2, 3, 70, 128, gains=torch.from_numpy(g).cuda(), t0=1000)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), want)
+
+
+def _device_kv(w, T, extra=0):
+    gains = torch.from_numpy(w.gains()).cuda()
+    k = torch.empty((w.batch, w.kv_heads, T + extra, w.head_dim), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    S.fill_device(k, w.seed, S.TID_K, w.batch, w.kv_heads, T + extra, w.head_dim, gains=gains)
+    S.fill_device(v, w.seed, S.TID_V, w.batch, w.kv_heads, T + extra, w.head_dim)
+    return k, v
+
+
+def _host_head(w, b, h, T):
+    k = S.gen_tensor(w.seed, S.TID_K, w.batch, w.kv_heads, T, w.head_dim, gains=w.gains(),
+                     heads_sel=[h], batch_sel=[b])
+    v = S.gen_tensor(w.seed, S.TID_V, w.batch, w.kv_heads, T, w.head_dim,
+                     heads_sel=[h], batch_sel=[b])
+    return k, v
+
+
+def _uniform_prefill(w, N, r, extra=0):
+    T = N + r
+    kd, vd = _device_kv(w, T, extra)
+    Tt = T + extra
+    cap = N + w.residual_len * (1 + extra // w.residual_len + 1)
+    c = K.KVCache(w.batch, w.kv_heads, cap, k_bits=w.k_bits, v_bits=w.v_bits,
+                  residual_len=w.residual_len)
+    D = w.head_dim
+    K.kvq_quantize_keys(c.c, kd, w.kv_heads * Tt * D, Tt * D, D, 0, N)
+    K.kvq_quantize_values(c.c, vd, w.kv_heads * Tt * D, Tt * D, D, 0, N)
+    R = w.residual_len
+    c.buf("k_resid").view(torch.int16).view(w.batch, w.kv_heads, R, D)[:, :, :r] = kd[:, :, N:T]
+    c.buf("v_resid").view(torch.int16).view(w.batch, w.kv_heads, R, D)[:, :, :r] = vd[:, :, N:T]
+    c.c.n_packed, c.c.n_resid = N, r
+    torch.cuda.synchronize()
+    return c, kd, vd
+
+
+def _decode(c, w, q_bits):
+    out = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), device="cuda")
+    wsb = K.kvq_workspace_bytes(c.c, w.q_heads, K.KVQ_OP_DECODE_ATTN)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    K.kvq_decode_attn(c.c, dev(q_bits), w.q_heads, O.default_sm_scale(w.head_dim),
+                      w.rope_theta, out, ws, wsb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_uniform_head(c, w, b, h, N, r, out, q):
+    T = N + r
+    k, v = _host_head(w, b, h, T)
+    ref = O.uniform_cache(k, v, w.k_bits, w.v_bits, N, r)
+    B, H, D = w.batch, w.kv_heads, w.head_dim
+    cap = c.c.capacity_tokens
+    kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 32, D * w.k_bits // 32)
+    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, D, w.v_bits)
+    km = host_words(c.buf("k_meta")).reshape(B, H, cap // 32, D)
+    vm = host_words(c.buf("v_meta")).reshape(B, H, cap, D // 32)
+    nb = N // 32
+    assert np.array_equal(kw[b, h, :nb], ref["k_codes"][0, 0])
+    assert np.array_equal(km[b, h, :nb], ref["k_meta"][0, 0])
+    assert np.array_equal(vw[b, h, :nb], ref["v_codes"][0, 0])
+    assert np.array_equal(vm[b, h, :N], ref["v_meta"][0, 0])
+    g = w.q_heads // w.kv_heads
+    qh = q[b:b + 1, h * g:(h + 1) * g]
+    want = O.decode_attention_f64(O.f16_to_f32(qh), ref["k_hat"], ref["v_hat"],
+                                  O.default_sm_scale(D))
+    return assert_close(out[b:b + 1, h * g:(h + 1) * g], want, f"{w.name} b{b} h{h}")
+
+
+@pytest.mark.parametrize("name,units", [
+    ("tiny", [(0, 0)]),
+    ("llama2_7b", [(0, 0), (3, 17), (7, 31)]),
+    ("llama2_13b_k4v2", [(0, 5), (3, 39)]),
+])
+def test_uniform_workload_full_size(name, units):
+    w = S.WORKLOADS[name]
+    c, _, _ = _uniform_prefill(w, w.n_packed, w.n_resid)
+    q = S.gen_tensor(w.seed, S.TID_Q, w.batch, w.q_heads, 1, w.head_dim)[:, :, 0]
+    out = _decode(c, w, q)
+    assert np.isfinite(out).all()
+    for b, h in units:
+        _check_uniform_head(c, w, b, h, w.n_packed, w.n_resid, out, q)
+
+
+def test_tiny_workload_reached_by_streaming_from_empty():
+    """512 packed + 128 window tokens is the state after appending 640 tokens one by one."""
+    w = S.WORKLOADS["tiny"]
+    T = w.n_packed + w.n_resid
+    kd, vd = _device_kv(w, T)
+    c = K.KVCache(1, 1, w.n_packed + 128, residual_len=128)
+    steps = [(kd[:, :, t].contiguous(), vd[:, :, t].contiguous()) for t in range(T)]
+    for kn, vn in steps:
+        K.kvq_append_flush(c.c, kn, vn)
+    assert (c.n_packed, c.n_resid) == (w.n_packed, w.n_resid)
+    q = S.gen_tensor(w.seed, S.TID_Q, 1, 1, 1, 128)[:, :, 0]
+    out = _decode(c, w, q)
+    _check_uniform_head(c, w, 0, 0, w.n_packed, w.n_resid, out, q)
+
+
+def test_gqa_long_context_streaming_1024_appends():
+    """Prefill 131072 packed + 128 window tokens, then 1024 x (append; attend) with a
+    flush every 128 appends; sampled steps and kv heads checked against the oracle."""
+    w = S.WORKLOADS["llama3_8b_gqa"]
+    N0, r0 = w.n_packed, w.n_resid
+    c, kd, vd = _uniform_prefill(w, N0, r0, extra=w.stream_steps)
+    T0 = N0 + r0
+    check_steps = {0, 1, 129, w.stream_steps - 1}
+    got = {}
+    wsb = K.kvq_workspace_bytes(c.c, w.q_heads, K.KVQ_OP_DECODE_ATTN)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, w.q_heads, 128), device="cuda")
+    qs = torch.empty((1, w.q_heads, w.stream_steps, 128), dtype=torch.int16, device="cuda")
+    S.fill_device(qs, w.seed, S.TID_Q, 1, w.q_heads, w.stream_steps, 128, t0=1)
+    states = {}
+    for i in range(w.stream_steps):
+        K.kvq_append_flush(c.c, kd[:, :, T0 + i].contiguous(), vd[:, :, T0 + i].contiguous())
+        K.kvq_decode_attn(c.c, qs[:, :, i].contiguous(), w.q_heads,
+                          O.default_sm_scale(128), 0.0, out, ws, wsb)
+        if i in check_steps:
+            got[i] = out.cpu().numpy()
+            states[i] = (c.n_packed, c.n_resid)
+    assert (c.n_packed, c.n_resid) == (N0 + 8 * 128, 128)
+    g = w.q_heads // w.kv_heads
+    for h in (0, 5):
+        k, v = _host_head(w, 0, h, T0 + w.stream_steps)
+        for i in sorted(check_steps):
+            N, r = states[i]
+            ref = O.uniform_cache(k, v, w.k_bits, w.v_bits, N, r)
+            q = S.gen_tensor(w.seed, S.TID_Q, 1, w.q_heads, 1, 128, t0=1 + i,
+                             heads_sel=list(range(h * g, (h + 1) * g)))[:, :, 0]
+            want = O.decode_attention_f64(O.f16_to_f32(q), ref["k_hat"], ref["v_hat"],
+                                          O.default_sm_scale(128))
+            assert_close(got[i][:, h * g:(h + 1) * g], want, f"step {i} head {h}")
+    # the packed bytes after 8 flushes equal one-shot quantization (head 5)
+    N, r = c.n_packed, c.n_resid
+    ref = O.uniform_cache(k, v, w.k_bits, w.v_bits, N, r)
+    cap = c.c.capacity_tokens
+    kw = host_words(c.buf("k_codes")).reshape(1, w.kv_heads, cap // 32, 32, 8)
+    assert np.array_equal(kw[0, 5, :N // 32], ref["k_codes"][0, 0])
+
+
+def test_kvquant_1m_context_full_size():
+    """1,048,576 tokens x 32 heads: nuq3 keys with 1 % outliers per channel and nuq3
+    values, RoPE theta 1e4 after dequantization.  Head 7 is checked end to end."""
+    w = S.WORKLOADS["kvquant_1m"]
+    N = w.n_packed
+    h = 7
+    kd, vd = _device_kv(w, N)
+    L = S.nuq3_lut()
+    lut = dev(L)
+    c = K.KVCache(1, w.kv_heads, N, k_bits=3, v_bits=3, residual_len=0, kind=K.KVQ_NUQ,
+                  lut=lut, outlier_bp=w.outlier_bp)
+    wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    D = w.head_dim
+    K.kvq_quantize_keys(c.c, kd, w.kv_heads * N * D, N * D, D, 0, N, ws, wsb)
+    K.kvq_quantize_values(c.c, vd, w.kv_heads * N * D, N * D, D, 0, N)
+    c.c.n_packed, c.c.n_resid = N, 0
+    del ws, kd, vd
+    torch.cuda.synchronize()
+    q0 = S.gen_tensor(w.seed, S.TID_Q, 1, w.q_heads, 1, D)[:, :, 0]
+    q = O.rope_query_f16(q0, N, w.rope_theta)
+    out = _decode(c, w, q)
+    assert np.isfinite(out).all()
+    k, v = _host_head(w, 0, h, N)
+    ref = O.nuq_head(k[0, 0], v[0, 0], L, L, w.outlier_bp, N, 0, w.rope_theta)
+    kw = host_words(c.buf("k_codes")).reshape(w.kv_heads, N // 32, D, 3)
+    assert np.array_equal(kw[h], ref["k_codes"])
+    km = host_words(c.buf("k_meta")).reshape(w.kv_heads, D)
+    assert np.array_equal(km[h], ref["k_meta"])
+    vm = host_words(c.buf("v_meta")).reshape(w.kv_heads, N)
+    assert np.array_equal(vm[h], ref["v_meta"])
+    rp = c.buf("k_csr_rowptr").cpu().numpy().view(np.int32).reshape(w.kv_heads, N + 1)
+    assert np.array_equal(rp[h], ref["rowptr"])
+    assert int(rp[h, -1]) == D * O.outlier_count(N, w.outlier_bp)
+    ent = host_words(c.buf("k_csr_ent")).reshape(w.kv_heads, -1)
+    assert np.array_equal(ent[h, :rp[h, -1]], ref["ent"])
+    want = O.decode_attention_f64(O.f16_to_f32(q[:, h:h + 1]), ref["k_hat"][None, None],
+                                  ref["v_hat"][None, None], O.default_sm_scale(D))
+    assert_close(out[:, h:h + 1], want, "kvquant_1m head 7")
