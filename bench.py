@@ -48,6 +48,31 @@ def decode_bytes(w, n_packed: int, n_resid: int) -> int:
     return codes + meta + window + w.batch * w.q_heads * D * (2 + 4)
 
 
+def nuq_decode_bytes(w, n_packed: int) -> int:
+    """Algorithmic bytes of one decode over a nuq3 cache: 3-bit codes of K and V, per-channel
+    key metadata, per-token value metadata, the CSR of key outliers (row pointers and one
+    4-byte entry per outlier), q and out."""
+    bh = w.batch * w.kv_heads
+    D = w.head_dim
+    k_out = (n_packed * w.outlier_bp + 9999) // 10000
+    codes = 2 * bh * n_packed * D * 3 // 8
+    meta = bh * D * 4 + bh * n_packed * 4
+    csr = (bh * (n_packed + 1) * 4 + bh * D * k_out * 4) if w.outlier_bp else 0
+    return codes + meta + csr + w.batch * w.q_heads * D * (2 + 4)
+
+
+def nuq_quantize_bytes(w, n_tokens: int) -> int:
+    """One-shot nuq quantize: fp16 K and V read once, codes, metadata and CSR written."""
+    bh = w.batch * w.kv_heads
+    D = w.head_dim
+    k_out = (n_tokens * w.outlier_bp + 9999) // 10000
+    read = 2 * bh * n_tokens * D * 2
+    written = 2 * bh * n_tokens * D * 3 // 8 + bh * D * 4 + bh * n_tokens * 4
+    if w.outlier_bp:
+        written += bh * (n_tokens + 1) * 4 + bh * D * k_out * 4
+    return read + written
+
+
 def quantize_bytes(w, n_tokens: int) -> int:
     """Prefill quantize: fp16 K and V read, packed codes and metadata written."""
     bh = w.batch * w.kv_heads
@@ -111,6 +136,105 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
                       f"of {cpu_cores()} available"}
 
 
+def bench_nuq(w, args) -> dict:
+    """KVQuant-style workload: one-shot quantize of the whole context (timed as the
+    quantize rate), then decode steps over it (a step is one decode; there is no
+    streaming window), replayed from a HIP graph."""
+    import torch
+
+    import decode_attention_10_amd as K
+    import kvq_synth as S
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    B, Hkv, Hq, D, N = w.batch, w.kv_heads, w.q_heads, w.head_dim, w.n_packed
+    gains = torch.from_numpy(w.gains()).to(dev)
+    k_src = torch.empty((B, Hkv, N, D), dtype=torch.int16, device=dev)
+    v_src = torch.empty_like(k_src)
+    S.fill_device(k_src, w.seed, S.TID_K, B, Hkv, N, D, gains=gains)
+    S.fill_device(v_src, w.seed, S.TID_V, B, Hkv, N, D)
+    lut = torch.from_numpy(S.nuq3_lut().view(np.int16)).to(dev)
+    c = K.KVCache(B, Hkv, N, k_bits=3, v_bits=3, residual_len=0, kind=K.KVQ_NUQ, lut=lut,
+                  outlier_bp=w.outlier_bp)
+    wsq = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
+    ws_q = torch.empty(wsq, dtype=torch.uint8, device=dev)
+    sT = (Hkv * N * D, N * D, D)
+
+    def quantize():
+        K.kvq_quantize_keys(c.c, k_src, sT[0], sT[1], sT[2], 0, N, ws_q, wsq)
+        K.kvq_quantize_values(c.c, v_src, sT[0], sT[1], sT[2], 0, N)
+
+    quantize()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        quantize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = e0.elapsed_time(e1) / reps
+    quant_gbs = nuq_quantize_bytes(w, N) / (quant_ms * 1e-3) / 1e9
+    del ws_q, k_src, v_src
+    torch.cuda.empty_cache()
+    c.c.n_packed, c.c.n_resid = N, 0
+
+    q = torch.empty((B, Hq, 1, D), dtype=torch.int16, device=dev)
+    S.fill_device(q, w.seed, S.TID_Q, B, Hq, 1, D)    # any query: timing does not depend on it
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    wsd = K.kvq_workspace_bytes(c.c, Hq, K.KVQ_OP_DECODE_ATTN)
+    ws_d = torch.empty(max(wsd, 16), dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(D)
+
+    def decode():
+        K.kvq_decode_attn(c.c, q, Hq, sm, w.rope_theta, out, ws_d, wsd)
+
+    round_len = 16
+    for _ in range(2):
+        decode()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    with torch.cuda.stream(cap_stream):
+        with torch.cuda.graph(g, stream=cap_stream):
+            for _ in range(round_len):
+                decode()
+    torch.cuda.synchronize()
+    rounds = max(1, args.steps // round_len)
+    steps = rounds * round_len
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(rounds):
+        g.replay()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_dec_s = d0.elapsed_time(d1) * 1e-3 / steps
+    nbytes = nuq_decode_bytes(w, N)
+    gbs = nbytes / mean_dec_s / 1e9
+    return {
+        "metric": "decode-attn HBM GB/s on packed KV (% of peak); tokens*ctx/s; quantize GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {B}, {Hq} heads, head_dim {D}, {N} tokens, "
+                               f"nuq3 keys per channel pre-RoPE with {w.outlier_bp / 100:g}% "
+                               f"CSR outliers, nuq3 values per token, RoPE theta "
+                               f"{w.rope_theta:g}"},
+        "decode_us": round(mean_dec_s * 1e6, 3),
+        "decode_bytes": nbytes,
+        "tokens_ctx_per_s": round(B * N / mean_dec_s, 1),
+        "quantize_gbs": round(quant_gbs, 1),
+        "quantize_ms_prefill": round(quant_ms, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,8 +254,10 @@ def main() -> int:
     import decode_attention_10_amd as K
     import kvq_synth as S
     w = S.WORKLOADS[args.workload]
-    if w.kind != "uniform":
-        raise SystemExit(f"workload {w.name} is not a uniform cache")
+    if w.kind == "nuq":
+        res = bench_nuq(w, args)
+        print(json.dumps(res))
+        return 0
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()

@@ -102,18 +102,26 @@ __device__ __forceinline__ float wave_max(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// Lane l ends with the sum over all 64 lanes of v[l & 31] (transposed reduction).
-__device__ __forceinline__ float transpose_sum32(float (&v)[32], int lane) {
+// One stage of the transposed reduction: lanes with bit D set keep v[D..2D), the others
+// v[0..D), each adding the half its partner (lane ^ D) does not keep.
+template <int D>
+__device__ __forceinline__ void transpose_stage(float (&v)[32], int lane) {
+  const bool up = lane & D;
 #pragma unroll
-  for (int d = 16; d >= 1; d >>= 1) {
-    const bool up = lane & d;
-#pragma unroll
-    for (int i = 0; i < d; ++i) {
-      const float keep = up ? v[i + d] : v[i];
-      const float send = up ? v[i] : v[i + d];
-      v[i] = keep + __shfl_xor(send, d);
-    }
+  for (int i = 0; i < D; ++i) {
+    const float keep = up ? v[i + D] : v[i];
+    const float send = up ? v[i] : v[i + D];
+    v[i] = keep + __shfl_xor(send, D);
   }
+}
+
+// Lane l ends with the sum over all 64 lanes of v[l & 31].
+__device__ __forceinline__ float transpose_sum32(float (&v)[32], int lane) {
+  transpose_stage<16>(v, lane);
+  transpose_stage<8>(v, lane);
+  transpose_stage<4>(v, lane);
+  transpose_stage<2>(v, lane);
+  transpose_stage<1>(v, lane);
   return v[0] + __shfl_xor(v[0], 32);
 }
 
@@ -152,29 +160,62 @@ __device__ __forceinline__ void softmax_block(NuqState<GQ>& st, const float* s, 
   for (int j = 0; j < GQ; ++j) p[j] = softmax_step(s[j], st.m[j], st.l[j], alpha[j]);
 }
 
+// Block-invariant values shared by the waves of a workgroup (LDS).
 template <int GQ>
-__device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t blk, int64_t t0,
-                                  const PairConsts& pc, const Lut& lk, const Lut& lv,
-                                  NuqState<GQ>& st, float (*psL)[kGroup], int lane) {
+struct NuqShared {
+  float2 q[GQ][64];          // (q_2i, q_2i+1) per head and pair
+  double theta[64];          // theta_i
+  float ks[kHeadDim], km[kHeadDim];
+  float lutk[8];
+};
+
+// Per-wave scratch (LDS).
+template <int GQ>
+struct NuqWaveScratch {
+  float ps[GQ][kGroup];      // p_t * scale_t of the block's tokens
+  float2 base[64];           // e^(-i t0 theta_i) of the block
+  uint32_t kc[kHeadDim][3];  // the block's key code words, per channel
+  uint32_t ent[64];          // a window of the block's CSR entries
+};
+
+struct NuqBlockRegs {
+  uint32_t kw[6], vw[6];     // key / value code words of channels 2l, 2l+1
+  uint32_t vmeta;            // value scale / min of token t (lanes < 32)
+  int32_t r0, r1;            // CSR row of token t (lanes < 32)
+};
+
+__device__ __forceinline__ void load_nuq_block(NuqBlockRegs& r, const DecodeArgs& a, int64_t bh,
+                                               int64_t blk, int lane) {
   const int t = lane & 31;
   const int64_t gblk = bh * a.cap_blocks + blk;
-  uint32_t kw0[3], kw1[3], vw0[3], vw1[3];
-  {
-    const uint32_t* kp = a.k_codes + (gblk * kHeadDim + 2 * lane) * 3;
-    const uint32_t* vp = a.v_codes + (gblk * kHeadDim + 2 * lane) * 3;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      kw0[i] = kp[i]; kw1[i] = kp[3 + i];
-      vw0[i] = vp[i]; vw1[i] = vp[3 + i];
-    }
+  const int64_t t0 = blk * kGroup;
+  const uint32_t* kp = a.k_codes + (gblk * kHeadDim + 2 * lane) * 3;
+  const uint32_t* vp = a.v_codes + (gblk * kHeadDim + 2 * lane) * 3;
+  const uint2 k01 = *reinterpret_cast<const uint2*>(kp);
+  const uint4 k25 = *reinterpret_cast<const uint4*>(kp + 2);
+  const uint2 v01 = *reinterpret_cast<const uint2*>(vp);
+  const uint4 v25 = *reinterpret_cast<const uint4*>(vp + 2);
+  r.kw[0] = k01.x; r.kw[1] = k01.y; r.kw[2] = k25.x; r.kw[3] = k25.y; r.kw[4] = k25.z; r.kw[5] = k25.w;
+  r.vw[0] = v01.x; r.vw[1] = v01.y; r.vw[2] = v25.x; r.vw[3] = v25.y; r.vw[4] = v25.z; r.vw[5] = v25.w;
+  r.vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
+  r.r0 = r.r1 = 0;
+  if (a.csr_rowptr) {
+    const int32_t* rp = a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1);
+    r.r0 = rp[t0 + t];
+    r.r1 = rp[t0 + t + 1];
   }
-  const uint32_t vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
-  const int32_t* rp = a.csr_rowptr ? a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1) : nullptr;
-  int32_t r0 = 0, r1 = 0;
-  if (rp) {
-    r0 = rp[t0 + t];
-    r1 = rp[t0 + t + 1];
-  }
+}
+
+template <int GQ>
+__device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
+                                  const NuqBlockRegs& r, const PairConsts& pc, const Lut& lk,
+                                  const Lut& lv, NuqState<GQ>& st, const NuqShared<GQ>& sh,
+                                  NuqWaveScratch<GQ>& ws, int lane) {
+  const int t = lane & 31;
+  const uint32_t* kw0 = r.kw;
+  const uint32_t* kw1 = r.kw + 3;
+  const uint32_t* vw0 = r.vw;
+  const uint32_t* vw1 = r.vw + 3;
 
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
@@ -207,27 +248,38 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t blk, 
     s[j] = transpose_sum32(part, lane);
   }
 
-  // ---- outliers of token t: exact value instead of the dequantized code
-  if (rp && lane < 32) {
-    const int64_t e_end = min((int64_t)r1, a.csr_capacity);
-    for (int64_t e = max(r0, 0); e < e_end; ++e) {
-      const uint32_t ent = a.csr_ent[bh * a.csr_capacity + e];
-      const int col = (int)(ent & (kHeadDim - 1));
-      const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
-      const uint32_t* cw = a.k_codes + (gblk * kHeadDim + col) * 3;
-      const uint32_t cwr[3] = {cw[0], cw[1], cw[2]};
-      const uint32_t km = a.k_meta[bh * kHeadDim + col];
-      const float khat = fmaf(lut_value(a.lut_k, code_at(cwr, t)), lo_f16(km), hi_f16(km));
-      const double th = pow((double)a.rope_theta, -2.0 * (double)(col >> 1) / kHeadDim);
-      const float2 r = rot_at(t0 + t, th);
+  // ---- outliers: token t's CSR entries replace the dequantized code by the exact value.
+  // The block's entries, code words and rotations come from LDS; entries are taken in
+  // windows of 64 and each token adds its own in row order.
+  const int32_t e_begin = __builtin_amdgcn_readlane(r.r0, 0);
+  const int32_t e_end0 = __builtin_amdgcn_readlane(r.r1, 31);
+  const int64_t e_end = min((int64_t)e_end0, a.csr_capacity);
+  if (e_begin < e_end) {
+    ws.base[lane] = base;
+    ws.kc[2 * lane][0] = kw0[0]; ws.kc[2 * lane][1] = kw0[1]; ws.kc[2 * lane][2] = kw0[2];
+    ws.kc[2 * lane + 1][0] = kw1[0]; ws.kc[2 * lane + 1][1] = kw1[1]; ws.kc[2 * lane + 1][2] = kw1[2];
+    for (int64_t w0 = max(e_begin, 0); w0 < e_end; w0 += 64) {
+      if (w0 + lane < e_end) ws.ent[lane] = a.csr_ent[bh * a.csr_capacity + w0 + lane];
+      __builtin_amdgcn_wave_barrier();
+      if (lane < 32) {
+        const int64_t lo = max((int64_t)r.r0, w0), hi = min((int64_t)r.r1, min(e_end, w0 + 64));
+        for (int64_t e = lo; e < hi; ++e) {
+          const uint32_t ent = ws.ent[e - w0];
+          const int col = (int)(ent & (kHeadDim - 1));
+          const int pr = col >> 1;
+          const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
+          const float khat = fmaf(sh.lutk[code_at(ws.kc[col], t)], sh.ks[col], sh.km[col]);
+          float sn, cs;
+          sincosf((float)((double)t * sh.theta[pr]), &sn, &cs);
+          const float2 rt = cmul(ws.base[pr], make_float2(cs, -sn));
 #pragma unroll
-      for (int j = 0; j < GQ; ++j) {
-        const uint32_t qq = *reinterpret_cast<const uint32_t*>(
-            a.q + (((bh / a.kv_heads) * a.q_heads + (bh % a.kv_heads) * GQ + j) * kHeadDim +
-                   (col & ~1)));
-        const float2 aq = cmul(make_float2(lo_f16(qq), hi_f16(qq)), r);
-        s[j] += ((col & 1) ? aq.y : aq.x) * (x - khat);
+          for (int j = 0; j < GQ; ++j) {
+            const float2 aq = cmul(sh.q[j][pr], rt);
+            s[j] += ((col & 1) ? aq.y : aq.x) * (x - khat);
+          }
+        }
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 
@@ -238,16 +290,16 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t blk, 
   softmax_block<GQ>(st, s, p, alpha);
 
   // ---- values: p * scale per token into LDS, p * min per lane
-  const float vs = lo_f16(vmeta), vm = hi_f16(vmeta);
+  const float vs = lo_f16(r.vmeta), vm = hi_f16(r.vmeta);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    if (lane < 32) psL[j][t] = p[j] * vs;
+    if (lane < 32) ws.ps[j][t] = p[j] * vs;
     st.mv[j] = st.mv[j] * alpha[j] + (lane < 32 ? p[j] * vm : 0.0f);
   }
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
-    const float4* pp = reinterpret_cast<const float4*>(&psL[j][0]);
+    const float4* pp = reinterpret_cast<const float4*>(&ws.ps[j][0]);
 #pragma unroll
     for (int m4 = 0; m4 < 8; ++m4) {
       const float4 w4 = pp[m4];
@@ -320,7 +372,8 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
 template <int GQ, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   constexpr int NT = NW * kWave;
-  __shared__ __align__(16) float psL[NW][GQ][kGroup];
+  __shared__ NuqShared<GQ> sh;
+  __shared__ __align__(16) NuqWaveScratch<GQ> wsc[NW];
   __shared__ float wm[NW][GQ], wl[NW][GQ];
   __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
 
@@ -353,6 +406,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   }
   const Lut lk = load_lut(a.lut_k);
   const Lut lv = load_lut(a.lut_v);
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) sh.q[j][lane] = pc.q[j];
+    sh.theta[lane] = pc.theta;
+    sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
+    sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
+    if (lane < 8) sh.lutk[lane] = lut_value(a.lut_k, lane);
+  }
+  __syncthreads();
 
   NuqState<GQ> st;
 #pragma unroll
@@ -371,10 +433,24 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   const int w1 = s0 + (int)((int64_t)(s1 - s0) * (wave + 1) / NW);
   for (int c = 0; c < nchunks; ++c) {
     const int u = a.n_blocks + kWindowUnits * c;
-    if (u >= w0 && u < w1) process_nuq_window<GQ>(a, bh, c, pc, st, psL[wave], lane);
+    if (u >= w0 && u < w1) process_nuq_window<GQ>(a, bh, c, pc, st, wsc[wave].ps, lane);
   }
-  for (int i = w0; i < min(w1, a.n_blocks); ++i)
-    process_nuq_block<GQ>(a, bh, i, (int64_t)i * kGroup, pc, lk, lv, st, psL[wave], lane);
+  const int b0 = w0, b1 = min(w1, a.n_blocks);
+  if (b0 < b1) {
+    // One block in flight ahead of the one being processed (clamped index, unrolled by
+    // two so no register copy waits on the loads just issued).
+    const int last = b1 - 1;
+    NuqBlockRegs r0, r1;
+    load_nuq_block(r0, a, bh, b0, lane);
+    for (int i = b0; i < b1; i += 2) {
+      load_nuq_block(r1, a, bh, min(i + 1, last), lane);
+      process_nuq_block<GQ>(a, bh, (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave], lane);
+      if (i + 1 >= b1) break;
+      load_nuq_block(r0, a, bh, min(i + 2, last), lane);
+      process_nuq_block<GQ>(a, bh, (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh, wsc[wave],
+                            lane);
+    }
+  }
 
   // ---- wave totals and the workgroup merge
 #pragma unroll

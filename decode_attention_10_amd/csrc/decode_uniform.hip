@@ -445,23 +445,58 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
 
 // Combines the per-split (max, sum, output) partials of one (batch, query head) row.
 // A separate launch: the kernel boundary makes every split's stores visible, which
-// costs far less than device-scope fences in each workgroup of the main kernel.
-__global__ __launch_bounds__(kHeadDim) void merge_splits_kernel(const float* partials,
-                                                               float* out, int splits) {
-  const int64_t row = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* P = partials + row * splits * kPartialStride;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, P[s * kPartialStride + kHeadDim]);
-  float L = 0.f, O = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < splits; ++s) {
-      const float e = exp2f(P[s * kPartialStride + kHeadDim] - M);
-      L += P[s * kPartialStride + kHeadDim + 1] * e;
-      O += P[s * kPartialStride + d] * e;
-    }
+// costs far less than device-scope fences in each workgroup of the main kernel.  The
+// split weights are computed in parallel into LDS; each output channel then sums its
+// splits with independent loads.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float y = __shfl_xor(x, o);
+    x = is_max ? fmaxf(x, y) : x + y;
   }
-  out[row * kHeadDim + d] = L > 0.f ? O / L : 0.f;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / kWave; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float* partials,
+                                                                    float* out, int splits) {
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[kMergeThreads / kWave];
+  __shared__ float half_o[kHeadDim];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* P = partials + row * splits * kPartialStride;
+  float m = kNegInf;
+  for (int s = tid; s < splits; s += kMergeThreads) m = fmaxf(m, P[s * kPartialStride + kHeadDim]);
+  const float M = block_reduce(m, red, true);
+  float l = 0.f;
+  for (int s = tid; s < splits; s += kMergeThreads) {
+    const float e = M == kNegInf ? 0.f : exp2f(P[s * kPartialStride + kHeadDim] - M);
+    wgt[s] = e;
+    l += P[s * kPartialStride + kHeadDim + 1] * e;
+  }
+  const float L = block_reduce(l, red, false);     // its barrier also publishes wgt[]
+  const int d = tid & (kHeadDim - 1), part = tid >> 7;
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  int s = part;
+  for (; s + 6 < splits; s += 8) {
+    o0 += P[s * kPartialStride + d] * wgt[s];
+    o1 += P[(s + 2) * kPartialStride + d] * wgt[s + 2];
+    o2 += P[(s + 4) * kPartialStride + d] * wgt[s + 4];
+    o3 += P[(s + 6) * kPartialStride + d] * wgt[s + 6];
+  }
+  for (; s < splits; s += 2) o0 += P[s * kPartialStride + d] * wgt[s];
+  const float o = (o0 + o1) + (o2 + o3);
+  if (part == 1) half_o[d] = o;
+  __syncthreads();
+  if (part == 0) out[row * kHeadDim + d] = L > 0.f ? (o + half_o[d]) / L : 0.f;
 }
 
 }  // namespace
@@ -490,8 +525,8 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
 
 hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.q_heads;
-  merge_splits_kernel<<<dim3((unsigned)rows), dim3(kHeadDim), 0, s>>>(a.partials, a.out,
-                                                                       a.splits);
+  merge_splits_kernel<<<dim3((unsigned)rows), dim3(kMergeThreads), 0, s>>>(a.partials, a.out,
+                                                                           a.splits);
   return hipGetLastError();
 }
 

@@ -79,6 +79,7 @@ struct DecodeArgs {
 };
 
 constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
+constexpr int kMaxSplits = 2048;               // workgroups per (batch, kv head) at most
 constexpr int kNuqChunk = 2048;                // tokens per chunk in the nuq key passes
 
 struct NuqKeysArgs {
