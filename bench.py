@@ -23,6 +23,7 @@ decode kernel and the oracle timed on a bounded host sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +36,50 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "decode_attention_10_amd", "csrc")
+KERNEL_SOURCES = {"decode_uniform_kernel": ("decode_uniform.hip", "kvq_common.h"),
+                  "decode_nuq_kernel": ("decode_nuq.hip", "kvq_common.h")}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the committed counter summary
+    ``profiles/<kernel>_<workload>_traffic.txt``: rocprofv3 FETCH_SIZE and WRITE_SIZE of the
+    kernel's dispatches, each scaled by what the same counter reads for a plain copy of known
+    size.  None when there is no summary or it was taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_source_digest(kernel):
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def copy_calibration(mib: int) -> dict:
+    """A plain device-to-device copy of ``mib`` MiB, five times: the known-size reference
+    for the FETCH_SIZE and WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}
 
 
 def decode_bytes(w, n_packed: int, n_resid: int) -> int:
@@ -231,7 +276,9 @@ def bench_nuq(w, args) -> dict:
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_ms_prefill": round(quant_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_nuq_kernel", w.name),
+                     "kernel": "decode_nuq_kernel", "bytes_per_launch": nbytes},
     }
 
 
@@ -243,11 +290,17 @@ def main() -> int:
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--min-rotation-mb", type=float, default=768.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain copy of this size (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU design is "
-              f"described in DESIGN.md and not built", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): the path shards by "
+              f"(batch, kv head) with no communication, and no multi-GPU run is built",
+              file=sys.stderr)
         return 2
+    if args.copy_calibration_mib:
+        print(json.dumps(copy_calibration(args.copy_calibration_mib)))
+        return 0
 
     import torch
 
@@ -394,7 +447,9 @@ def main() -> int:
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_ms_prefill": round(quant_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_uniform_kernel", w.name),
+                     "kernel": "decode_uniform_kernel", "bytes_per_launch": dec_bytes},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)

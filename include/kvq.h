@@ -59,18 +59,18 @@
  *    v_codes [batch][kv_heads][nb][D][Bv words]: token j of the block at bit
  *      (Bv*j) % 32 of word (Bv*j) / 32 of its channel's row.
  *    v_meta  [batch][kv_heads][nb*32 tokens][D/32] words.
- *  NUQ keys (3 bits, per channel over all quantized tokens):
- *    k_codes [batch][kv_heads][nb][32][3*D/32 words]: first D/16 words hold the
- *      low two bits in the 2-bit key layout, then D/32 words hold the high bit,
- *      channel d at bit d % 32 of word D/16 + d / 32.
+ *  NUQ codes (3 bits), keys and values alike:
+ *    [batch][kv_heads][nb][D][3 words]: per block and channel, word 0 holds the
+ *      low two bits of tokens 0..15 and word 1 those of tokens 16..31 (token j
+ *      of its half at bit 8*(j%4) + 2*(j/4)); word 2 holds the high bits of all
+ *      32 tokens (token j at bit 8*(j%4) + j/4).
+ *  NUQ keys (per channel over all quantized tokens):
  *    k_meta  [batch][kv_heads][D] words (one scale/min per channel).
  *    k_csr_rowptr [batch][kv_heads][capacity_tokens + 1] int32, rows = tokens,
  *      offsets relative to the head's segment of k_csr_ent;
  *    k_csr_ent [batch][kv_heads][csr_capacity] uint32: channel in bits 0..15,
  *      fp16 value in bits 16..31, channels ascending within a row.
- *  NUQ values (3 bits, per token over all D channels):
- *    v_codes [batch][kv_heads][nb][D][3 words]: words 0-1 hold the low two bits
- *      in the 2-bit value layout, word 2 the high bits, token j at bit j.
+ *  NUQ values (per token over all D channels):
  *    v_meta  [batch][kv_heads][capacity_tokens] words.
  *  Window: k_resid, v_resid [batch][kv_heads][residual_len][D] fp16.
  *
