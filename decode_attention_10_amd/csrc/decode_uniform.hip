@@ -107,231 +107,281 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kRowBcast31, 0xC>(kNegInf, x));
   return readlane63(x);
 }
-__device__ __forceinline__ float sum32(float x) {   // over lane bits 0..4
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-  return x;
+
+// acc[T] += w0 * code(even token, channel T) + w1 * code(odd token, channel T) over the
+// channels of one word of the tiled value layout (8 channels for 2-bit codes, 4 for
+// 4-bit codes).  Each accumulator keeps the 2^(pos - 24) factor of its field position,
+// which is undone once at the end.
+template <int B>
+__device__ __forceinline__ void vdot_word(uint32_t w, float w0, float w1, float* acc) {
+  if constexpr (B == 2) {
+    const uint32_t w10 = w >> 10;
+    uint32_t x;
+    x = w & 0x00030003u;   acc[0] = fmaf(w0, lo_f16(x), acc[0]);  acc[0] = fmaf(w1, hi_f16(x), acc[0]);
+    x = w & 0x000C000Cu;   acc[1] = fmaf(w0, lo_f16(x), acc[1]);  acc[1] = fmaf(w1, hi_f16(x), acc[1]);
+    x = w & 0x00300030u;   acc[2] = fmaf(w0, lo_f16(x), acc[2]);  acc[2] = fmaf(w1, hi_f16(x), acc[2]);
+    x = w & 0x00C000C0u;   acc[3] = fmaf(w0, lo_f16(x), acc[3]);  acc[3] = fmaf(w1, hi_f16(x), acc[3]);
+    x = w & 0x03000300u;   acc[4] = fmaf(w0, lo_f16(x), acc[4]);  acc[4] = fmaf(w1, hi_f16(x), acc[4]);
+    x = w10 & 0x00030003u; acc[5] = fmaf(w0, lo_f16(x), acc[5]);  acc[5] = fmaf(w1, hi_f16(x), acc[5]);
+    x = w10 & 0x000C000Cu; acc[6] = fmaf(w0, lo_f16(x), acc[6]);  acc[6] = fmaf(w1, hi_f16(x), acc[6]);
+    x = w10 & 0x00300030u; acc[7] = fmaf(w0, lo_f16(x), acc[7]);  acc[7] = fmaf(w1, hi_f16(x), acc[7]);
+  } else {
+    const uint32_t w8 = w >> 8;
+    uint32_t x;
+    x = w & 0x000F000Fu;  acc[0] = fmaf(w0, lo_f16(x), acc[0]);  acc[0] = fmaf(w1, hi_f16(x), acc[0]);
+    x = w & 0x00F000F0u;  acc[1] = fmaf(w0, lo_f16(x), acc[1]);  acc[1] = fmaf(w1, hi_f16(x), acc[1]);
+    x = w8 & 0x000F000Fu; acc[2] = fmaf(w0, lo_f16(x), acc[2]);  acc[2] = fmaf(w1, hi_f16(x), acc[2]);
+    x = w8 & 0x00F000F0u; acc[3] = fmaf(w0, lo_f16(x), acc[3]);  acc[3] = fmaf(w1, hi_f16(x), acc[3]);
+  }
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS rows of the per-block weights: 32 floats padded to 40, so that rows read by the
+// lanes of one 8-lane LDS cycle start on different banks.
+constexpr int kRow = 40;
+
+// Lane roles inside a wave for one 32-token block:
+//   keys   : lane = 4 * tp + q: tokens tp and tp + 16, channels 32q .. 32q + 31 (the
+//            four lanes of a quad share a token pair and sum their partial scores);
+//   values : lane = 16 * o + n: tokens 8o .. 8o + 7, channels 8n .. 8n + 7 (one tile);
+//   meta   : key scale/min of channels 2*lane, 2*lane + 1; value scale/min of tokens
+//            tp and tp + 16 in group q.
 template <int KB, int VB>
 struct BlockRegs {
-  uint32_t kc[kHeadDim * KB / 64];   // this lane's half of a token row
-  uint32_t km[2];                    // key meta of channels 2l, 2l+1
-  uint32_t vc[2 * VB];               // value rows of channels 2l, 2l+1
-  uint32_t vm[2];                    // value meta of token t, groups 2h, 2h+1
+  uint32_t ka[KB];     // token tp, channel quarter q
+  uint32_t kb[KB];     // token tp + 16
+  uint32_t km[2];      // key meta of channels 2l, 2l+1
+  uint32_t vc[2 * VB]; // value tile
+  uint32_t vm[2];      // value meta (tp, q), (tp + 16, q)
 };
 
+// Base pointers of one (batch, kv head) cache segment.
+struct HeadPtrs {
+  const uint32_t* kc;
+  const uint32_t* km;
+  const uint32_t* vc;
+  const uint32_t* vm;
+};
+
+// Loads of block `blk` (wave-uniform) of a segment: the block's base address is scalar
+// arithmetic, each lane adds a fixed 32-bit offset.
 template <int KB, int VB>
-__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& r, const DecodeArgs& a,
-                                           int64_t blk, int lane) {
-  constexpr int WK = kHeadDim * KB / 32;
-  const int t = lane & 31, half = lane >> 5;
-  const uint4* kp = reinterpret_cast<const uint4*>(a.k_codes + blk * (kGroup * WK) +
-                                                   t * WK + half * (WK / 2));
-#pragma unroll
-  for (int i = 0; i < WK / 8; ++i) {
-    const uint4 u = kp[i];
-    r.kc[4 * i] = u.x; r.kc[4 * i + 1] = u.y; r.kc[4 * i + 2] = u.z; r.kc[4 * i + 3] = u.w;
+__device__ __forceinline__ void load_block(BlockRegs<KB, VB>& r, const HeadPtrs& hp, int blk,
+                                           int lane) {
+  constexpr int WK = kHeadDim * KB / 32;            // words per token row
+  const int tp = lane >> 2, q = lane & 3;
+  const uint32_t* kp = hp.kc + (uint32_t)blk * (kGroup * WK);
+  const uint32_t ka_off = (uint32_t)(tp * WK + q * KB), kb_off = ka_off + 16 * WK;
+  if constexpr (KB == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(kp + ka_off);
+    const uint2 y = *reinterpret_cast<const uint2*>(kp + kb_off);
+    r.ka[0] = x.x; r.ka[1] = x.y; r.kb[0] = y.x; r.kb[1] = y.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(kp + ka_off);
+    const uint4 y = *reinterpret_cast<const uint4*>(kp + kb_off);
+    r.ka[0] = x.x; r.ka[1] = x.y; r.ka[2] = x.z; r.ka[3] = x.w;
+    r.kb[0] = y.x; r.kb[1] = y.y; r.kb[2] = y.z; r.kb[3] = y.w;
   }
-  const uint2 km = *reinterpret_cast<const uint2*>(a.k_meta + blk * kHeadDim + 2 * lane);
+  const uint2 km = *reinterpret_cast<const uint2*>(hp.km + (uint32_t)blk * kHeadDim +
+                                                   (uint32_t)(2 * lane));
   r.km[0] = km.x; r.km[1] = km.y;
-  const uint4* vp = reinterpret_cast<const uint4*>(a.v_codes + blk * (kHeadDim * VB) +
-                                                   2 * lane * VB);
+  const uint4* vp = reinterpret_cast<const uint4*>(hp.vc + (uint32_t)blk * (kHeadDim * VB) +
+                                                   (uint32_t)(lane * 2 * VB));
 #pragma unroll
   for (int i = 0; i < VB / 2; ++i) {
     const uint4 u = vp[i];
     r.vc[4 * i] = u.x; r.vc[4 * i + 1] = u.y; r.vc[4 * i + 2] = u.z; r.vc[4 * i + 3] = u.w;
   }
-  const uint2 vm = *reinterpret_cast<const uint2*>(a.v_meta + (blk * kGroup + t) * 4 + 2 * half);
-  r.vm[0] = vm.x; r.vm[1] = vm.y;
+  const uint32_t* vm = hp.vm + (uint32_t)blk * (kGroup * 4);
+  r.vm[0] = vm[(uint32_t)lane];
+  r.vm[1] = vm[(uint32_t)lane + 64];
 }
 
 template <int GQ>
 struct WaveState {
-  float m[GQ];        // running max (log2 domain), wave-uniform
-  float l[GQ];        // this lane's sum of p over its tokens
-  float o[GQ][2];     // output accumulators of channels 2l, 2l+1
-  float mv[GQ][2];    // sum_t p_t * min_tg for groups 2h, 2h+1 (token lanes)
+  float m[GQ];          // running max (log2 domain), wave-uniform
+  float l[GQ];          // this lane's sum of p (every token counted by 4 lanes)
+  float mv[GQ];         // sum of p * min over this lane's two tokens, group q
+  float acc[GQ][8];     // packed values, channels 8n + T (field-scaled)
+  float ow[GQ][8];      // fp16 window values, channels 8n + T
 };
 
-// Online softmax update for one head; s is this lane's token score (log2 units; the
-// two lane halves hold the same tokens).  The block maximum is only reduced when some
-// score exceeds the running maximum, which after the first blocks is rare.
-__device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
-  alpha = 1.0f;
-  if (__any(s > m)) {
-    const float mn = fmaxf(m, wave_max(s));
-    alpha = exp2f(m - mn);
-    m = mn;
-    l *= alpha;
+// Online softmax for one head over this lane's two scores; the running maximum is only
+// reduced over the wave when some score exceeds it (after the first blocks: rarely).
+template <int GQ>
+__device__ __forceinline__ void softmax_pair(WaveState<GQ>& st, int j, float sA, float sB,
+                                             float& pA, float& pB) {
+  const float smax = fmaxf(sA, sB);
+  if (__any(smax > st.m[j])) {
+    const float mn = fmaxf(st.m[j], wave_max(smax));
+    const float alpha = fast_exp2(st.m[j] - mn);     // 0 while m = -inf
+    st.m[j] = mn;
+    st.l[j] *= alpha;
+    st.mv[j] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      st.acc[j][t] *= alpha;
+      st.ow[j][t] *= alpha;
+    }
   }
-  const float p = exp2f(s - m);
-  l += p;
-  return p;
+  pA = fast_exp2(sA - st.m[j]);
+  pB = fast_exp2(sB - st.m[j]);
+  st.l[j] += pA + pB;
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<kQuadSwap1>(0.f, x);
+  x += dpp<kQuadSwap2>(0.f, x);
+  return x;
 }
 
 template <int KB, int VB, int GQ>
 __device__ __forceinline__ void process_block(const BlockRegs<KB, VB>& r, WaveState<GQ>& st,
-                                              const uint32_t* qreg, float (*qsL)[kHeadDim],
-                                              float (*psL)[4][kGroup], float scale_log2,
-                                              int lane) {
-  constexpr int WK = kHeadDim * KB / 32;
-  constexpr int CPW = 32 / KB;
-  constexpr int TPW = 32 / VB;
-  const int t = lane & 31, half = lane >> 5;
+                                              const uint32_t* qreg, const float (*qf)[2],
+                                              float cscale, float (*qsL)[4][kRow],
+                                              float (*psL)[4][kRow], int lane) {
+  constexpr int CPW = 32 / KB;                       // key channels per word
+  const int tp = lane >> 2, q = lane & 3;
+  const int n = lane & 15, o = lane >> 4;
 
-  // ---- keys: q*scale per channel into LDS, q.min reduced over the wave
-  const float ks0 = lo_f16(r.km[0]), kn0 = hi_f16(r.km[0]);
-  const float ks1 = lo_f16(r.km[1]), kn1 = hi_f16(r.km[1]);
-  const float f0 = field_scale(KB, (2 * lane) % CPW), f1 = field_scale(KB, (2 * lane + 1) % CPW);
+  // ---- keys: q * scale of channels 2l, 2l+1 into LDS; q . min reduced over the wave
+  const uint32_t kmin2 = __builtin_amdgcn_perm(r.km[1], r.km[0], 0x07060302u);
   float cmin[GQ];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    const float q0 = lo_f16(qreg[j]), q1 = hi_f16(qreg[j]);
-    *reinterpret_cast<float2*>(&qsL[j][2 * lane]) = make_float2(q0 * ks0 * f0, q1 * ks1 * f1);
-    cmin[j] = q0 * kn0 + q1 * kn1;
+    *reinterpret_cast<float2*>(&qsL[j][lane >> 4][(2 * lane) & 31]) =
+        make_float2(qf[j][0] * lo_f16(r.km[0]), qf[j][1] * lo_f16(r.km[1]));
+    cmin[j] = __builtin_amdgcn_fdot2(as_h2(qreg[j]), as_h2(kmin2), 0.0f, false);
   }
 #pragma unroll
-  for (int j = 0; j < GQ; ++j) cmin[j] = wave_sum(cmin[j]);
+  for (int j = 0; j < GQ; ++j) cmin[j] = wave_sum(cmin[j]) * cscale;
 
-  float s[GQ];
+  const float vsA = lo_f16(r.vm[0]), vnA = hi_f16(r.vm[0]);
+  const float vsB = lo_f16(r.vm[1]), vnB = hi_f16(r.vm[1]);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    float acc = 0.f;
+    float wt[32];
+    const float4* qp = reinterpret_cast<const float4*>(&qsL[j][q][0]);
 #pragma unroll
-    for (int wi = 0; wi < WK / 2; ++wi) {
-      float wt[CPW];
-      const float4* qp = reinterpret_cast<const float4*>(&qsL[j][half * 64 + wi * CPW]);
-#pragma unroll
-      for (int k = 0; k < CPW / 4; ++k) {
-        const float4 v = qp[k];
-        wt[4 * k] = v.x; wt[4 * k + 1] = v.y; wt[4 * k + 2] = v.z; wt[4 * k + 3] = v.w;
-      }
-      acc = dot_word<KB>(r.kc[wi], wt, acc);
-    }
-    acc += __shfl_xor(acc, 32);
-    s[j] = (acc + cmin[j]) * scale_log2;
-  }
-
-  // ---- softmax
-  float p[GQ], alpha[GQ];
-#pragma unroll
-  for (int j = 0; j < GQ; ++j) p[j] = softmax_step(s[j], st.m[j], st.l[j], alpha[j]);
-
-  // ---- values: p*scale per token into LDS, p*min accumulated per lane
-  const float vs0 = lo_f16(r.vm[0]), vn0 = hi_f16(r.vm[0]);
-  const float vs1 = lo_f16(r.vm[1]), vn1 = hi_f16(r.vm[1]);
-  const float ft = field_scale(VB, t % TPW);
-#pragma unroll
-  for (int j = 0; j < GQ; ++j) {
-    psL[j][2 * half][t] = p[j] * vs0 * ft;
-    psL[j][2 * half + 1][t] = p[j] * vs1 * ft;
-    st.mv[j][0] = st.mv[j][0] * alpha[j] + p[j] * vn0;
-    st.mv[j][1] = st.mv[j][1] * alpha[j] + p[j] * vn1;
-  }
-  const int gi = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < GQ; ++j) {
-    float wt[kGroup];
-    const float4* pp = reinterpret_cast<const float4*>(&psL[j][gi][0]);
-#pragma unroll
-    for (int k = 0; k < kGroup / 4; ++k) {
-      const float4 v = pp[k];
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = qp[k];
       wt[4 * k] = v.x; wt[4 * k + 1] = v.y; wt[4 * k + 2] = v.z; wt[4 * k + 3] = v.w;
     }
-    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < VB; ++w) {
-      o0 = dot_word<VB>(r.vc[w], wt + w * TPW, o0);
-      o1 = dot_word<VB>(r.vc[VB + w], wt + w * TPW, o1);
+    for (int e = 0; e < KB; e += 2) {
+      a0 = dot_word<KB>(r.ka[e], wt + e * CPW, a0);
+      a1 = dot_word<KB>(r.ka[e + 1], wt + (e + 1) * CPW, a1);
+      b0 = dot_word<KB>(r.kb[e], wt + e * CPW, b0);
+      b1 = dot_word<KB>(r.kb[e + 1], wt + (e + 1) * CPW, b1);
     }
-    st.o[j][0] = o0;
-    st.o[j][1] = o1;
+    const float sA = quad_sum(a0 + a1) + cmin[j];
+    const float sB = quad_sum(b0 + b1) + cmin[j];
+
+    float pA, pB;
+    softmax_pair<GQ>(st, j, sA, sB, pA, pB);
+
+    // ---- values: p * scale of tokens tp, tp + 16 (group q) into LDS, p * min per lane
+    psL[j][q][tp] = pA * vsA;
+    psL[j][q][tp + 16] = pB * vsB;
+    st.mv[j] = fmaf(pA, vnA, fmaf(pB, vnB, st.mv[j]));
+
+    float wv[8];
+    const float4* pp = reinterpret_cast<const float4*>(&psL[j][n >> 2][8 * o]);
+    const float4 u0 = pp[0], u1 = pp[1];
+    wv[0] = u0.x; wv[1] = u0.y; wv[2] = u0.z; wv[3] = u0.w;
+    wv[4] = u1.x; wv[5] = u1.y; wv[6] = u1.z; wv[7] = u1.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (VB == 2) {
+        vdot_word<2>(r.vc[i], wv[2 * i], wv[2 * i + 1], st.acc[j]);
+      } else {
+        vdot_word<4>(r.vc[i], wv[2 * i], wv[2 * i + 1], st.acc[j]);
+        vdot_word<4>(r.vc[i + 4], wv[2 * i], wv[2 * i + 1], st.acc[j] + 4);
+      }
+    }
   }
 }
 
-// One chunk of up to 32 fp16 window tokens.
+// One chunk of up to 32 fp16 window tokens, with the same lane roles as a packed block.
 template <int GQ>
 __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, int c,
                                                WaveState<GQ>& st, const uint32_t (*qh)[64],
                                                float (*pL)[kGroup], int lane) {
-  const int t = lane & 31, half = lane >> 5;
+  const int tp = lane >> 2, q = lane & 3;
+  const int n = lane & 15, o = lane >> 4;
   const int tok0 = c * kGroup;
   const int nvalid = min(kGroup, a.n_resid - tok0);
-  const bool valid = t < nvalid;
-  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim;
-  uint32_t kw[32];
-  if (valid) {
-    const uint4* kp = reinterpret_cast<const uint4*>(kr + t * kHeadDim + half * 64);
+  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim + 32 * q;
+  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 8 * n;
+  uint32_t ka[16], kb[16];
+  {
+    const uint4* pa = reinterpret_cast<const uint4*>(kr + min(tp, nvalid - 1) * kHeadDim);
+    const uint4* pb = reinterpret_cast<const uint4*>(kr + min(tp + 16, nvalid - 1) * kHeadDim);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 u = kp[i];
-      kw[4 * i] = u.x; kw[4 * i + 1] = u.y; kw[4 * i + 2] = u.z; kw[4 * i + 3] = u.w;
+    for (int i = 0; i < 4; ++i) {
+      const uint4 x = pa[i], y = pb[i];
+      ka[4 * i] = x.x; ka[4 * i + 1] = x.y; ka[4 * i + 2] = x.z; ka[4 * i + 3] = x.w;
+      kb[4 * i] = y.x; kb[4 * i + 1] = y.y; kb[4 * i + 2] = y.z; kb[4 * i + 3] = y.w;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) kw[i] = 0;
   }
-  float p[GQ], alpha[GQ];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    float acc = 0.f;
-    const uint4* qp = reinterpret_cast<const uint4*>(&qh[j][half * 32]);
+    float accA = 0.f, accB = 0.f;
+    const uint4* qp = reinterpret_cast<const uint4*>(&qh[j][16 * q]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const uint4 u = qp[i];
-      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i]), as_h2(u.x), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 1]), as_h2(u.y), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 2]), as_h2(u.z), acc, false);
-      acc = __builtin_amdgcn_fdot2(as_h2(kw[4 * i + 3]), as_h2(u.w), acc, false);
-    }
-    acc += __shfl_xor(acc, 32);
-    const float s = valid ? acc * a.scale_log2 : kNegInf;
-    p[j] = softmax_step(s, st.m[j], st.l[j], alpha[j]);
-    if (half == 0) pL[j][t] = p[j];
-  }
-  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
+      const uint32_t qw[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int j = 0; j < GQ; ++j) {
-    st.o[j][0] *= alpha[j];
-    st.o[j][1] *= alpha[j];
-    st.mv[j][0] *= alpha[j];
-    st.mv[j][1] *= alpha[j];
-  }
-  uint32_t vw[kGroup];
-#pragma unroll
-  for (int k = 0; k < kGroup; ++k)
-    vw[k] = *reinterpret_cast<const uint32_t*>(vr + min(k, nvalid - 1) * kHeadDim);
-#pragma unroll
-  for (int j = 0; j < GQ; ++j) {
-    const float4* pp = reinterpret_cast<const float4*>(&pL[j][0]);
-    float o0 = st.o[j][0], o1 = st.o[j][1];
-#pragma unroll
-    for (int k4 = 0; k4 < kGroup / 4; ++k4) {
-      const float4 p4 = pp[k4];
-      const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o0 = fmaf(pk[u], lo_f16(vw[4 * k4 + u]), o0);
-        o1 = fmaf(pk[u], hi_f16(vw[4 * k4 + u]), o1);
+      for (int k = 0; k < 4; ++k) {
+        accA = __builtin_amdgcn_fdot2(as_h2(ka[4 * i + k]), as_h2(qw[k]), accA, false);
+        accB = __builtin_amdgcn_fdot2(as_h2(kb[4 * i + k]), as_h2(qw[k]), accB, false);
       }
     }
-    st.o[j][0] = o0;
-    st.o[j][1] = o1;
+    const float sA = tp < nvalid ? quad_sum(accA) * a.scale_log2 : kNegInf;
+    const float sB = tp + 16 < nvalid ? quad_sum(accB) * a.scale_log2 : kNegInf;
+    float pA, pB;
+    softmax_pair<GQ>(st, j, sA, sB, pA, pB);
+    pL[j][tp] = pA;
+    pL[j][tp + 16] = pB;
+  }
+  // the value rows are requested once the keys are consumed (fewer live registers)
+  uint32_t vw[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint4 u =
+        *reinterpret_cast<const uint4*>(vr + min(8 * o + t, nvalid - 1) * kHeadDim);
+    vw[t][0] = u.x; vw[t][1] = u.y; vw[t][2] = u.z; vw[t][3] = u.w;
+  }
+#pragma unroll
+  for (int j = 0; j < GQ; ++j) {
+    const float4* pp = reinterpret_cast<const float4*>(&pL[j][8 * o]);
+    const float4 u0 = pp[0], u1 = pp[1];
+    const float pw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st.ow[j][2 * k] = fmaf(pw[t], lo_f16(vw[t][k]), st.ow[j][2 * k]);
+        st.ow[j][2 * k + 1] = fmaf(pw[t], hi_f16(vw[t][k]), st.ow[j][2 * k + 1]);
+      }
+    }
   }
 }
 
 // Work units: packed block i is unit i (0 <= i < n_blocks); window chunk c (32 fp16
 // tokens) is units [n_blocks + kWindowUnits*c, n_blocks + kWindowUnits*(c+1)), weighted
-// by its larger byte count.  A split covers a contiguous unit range; each wave of the
-// split covers a contiguous sub-range: the packed blocks in it, and every window
-// chunk whose first unit falls in it.
+// by its larger byte count.  A split covers a contiguous unit range: the packed blocks
+// in it and every window chunk whose first unit falls in it.
 template <int KB, int VB, int GQ, int NW>
 __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a) {
   constexpr int NT = NW * kWave;
+  constexpr int CPW = 32 / KB;
   __shared__ __align__(16) uint32_t qh[GQ][64];
-  __shared__ __align__(16) float qsL[NW][GQ][kHeadDim];
-  __shared__ __align__(16) float psL[NW][GQ][4][kGroup];
+  __shared__ __align__(16) float qsL[NW][GQ][4][kRow];
+  __shared__ __align__(16) float psL[NW][GQ][4][kRow];
   __shared__ float wm[NW][GQ], wl[NW][GQ];
   __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
 
@@ -343,74 +393,105 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   const int hkv = (int)(bh % a.kv_heads);
   const int hq0 = hkv * GQ;
 
+  // query pair (channels 2l, 2l+1) per head, and the same times the key field scale and
+  // the softmax scale (scores are kept in log2 units)
   uint32_t qreg[GQ];
+  float qf[GQ][2];
+  const float f0 = field_scale(KB, (2 * lane) % CPW), f1 = field_scale(KB, (2 * lane + 1) % CPW);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     qreg[j] = *reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.q_heads + hq0 + j) *
                                                            kHeadDim + 2 * lane);
+    qf[j][0] = lo_f16(qreg[j]) * f0 * a.scale_log2;
+    qf[j][1] = hi_f16(qreg[j]) * f1 * a.scale_log2;
     if (wave == 0) qh[j][lane] = qreg[j];
   }
   __syncthreads();
 
+  const float cscale = a.scale_log2;
   WaveState<GQ> st;
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     st.m[j] = kNegInf;
     st.l[j] = 0.f;
-    st.o[j][0] = st.o[j][1] = 0.f;
-    st.mv[j][0] = st.mv[j][1] = 0.f;
+    st.mv[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.acc[j][t] = st.ow[j][t] = 0.f;
   }
 
   const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
   const int units = a.n_blocks + kWindowUnits * nchunks;
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
-  const int w0 = s0 + (int)((int64_t)(s1 - s0) * wave / NW);
-  const int w1 = s0 + (int)((int64_t)(s1 - s0) * (wave + 1) / NW);
+  // Packed blocks of the split are dealt round-robin to the waves, so that at any time
+  // the workgroup streams one contiguous stretch of each cache array; window chunks go
+  // to the last waves (which get no more packed blocks than the others).
+  const int bend = min(s1, a.n_blocks);
+  const int first = s0 + wave;
+  const int cnt = first < bend ? (bend - first + NW - 1) / NW : 0;
 
   // ---- window chunks first (their loads are short), then the packed blocks
   for (int c = 0; c < nchunks; ++c) {
     const int u = a.n_blocks + kWindowUnits * c;
-    if (u >= w0 && u < w1)
+    if (u >= s0 && u < s1 && NW - 1 - (c % NW) == wave)
       process_window<GQ>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
   }
-  const int b0 = w0, b1 = min(w1, a.n_blocks);
-  if (b0 < b1) {
-    const int64_t base = bh * a.cap_blocks;
+  if (cnt > 0) {
+    const int64_t seg = bh * a.cap_blocks;
+    const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
+                         a.k_meta + seg * kHeadDim, a.v_codes + seg * (kHeadDim * VB),
+                         a.v_meta + seg * (kGroup * 4)};
     // Two blocks in flight ahead of the one being processed.  The prefetch index is
     // clamped rather than guarded so every iteration issues the same loads, and the
     // loop is unrolled by three with rotating roles so no register copy has to wait
     // for the loads just issued.
-    const int last = b1 - 1;
+    const int last = cnt - 1;
     BlockRegs<KB, VB> r0, r1, r2;
-    load_block<KB, VB>(r0, a, base + b0, lane);
-    load_block<KB, VB>(r1, a, base + min(b0 + 1, last), lane);
-    for (int i = b0; i < b1; i += 3) {
-      load_block<KB, VB>(r2, a, base + min(i + 2, last), lane);
-      process_block<KB, VB, GQ>(r0, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-      if (i + 1 >= b1) break;
-      load_block<KB, VB>(r0, a, base + min(i + 3, last), lane);
-      process_block<KB, VB, GQ>(r1, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
-      if (i + 2 >= b1) break;
-      load_block<KB, VB>(r1, a, base + min(i + 4, last), lane);
-      process_block<KB, VB, GQ>(r2, st, qreg, qsL[wave], psL[wave], a.scale_log2, lane);
+    load_block<KB, VB>(r0, hp, first, lane);
+    load_block<KB, VB>(r1, hp, first + min(1, last) * NW, lane);
+    for (int k = 0; k < cnt; k += 3) {
+      load_block<KB, VB>(r2, hp, first + min(k + 2, last) * NW, lane);
+      process_block<KB, VB, GQ>(r0, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
+      if (k + 1 >= cnt) break;
+      load_block<KB, VB>(r0, hp, first + min(k + 3, last) * NW, lane);
+      process_block<KB, VB, GQ>(r1, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
+      if (k + 2 >= cnt) break;
+      load_block<KB, VB>(r1, hp, first + min(k + 4, last) * NW, lane);
+      process_block<KB, VB, GQ>(r2, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
     }
   }
 
-  // ---- finish the wave: totals of l and of the min terms, then the WG merge
-  const int k_sel = (lane >> 4) & 1;
+  // ---- finish the wave: totals of l and of the min terms, value accumulators reduced
+  // over the four token octets, then the WG merge
+  const int n = lane & 15;
+  float fs[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) fs[t] = field_scale(VB, VB == 2 ? t : (t & 3));
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    const float lt = sum32(st.l[j]);
-    const float mv0 = sum32(st.mv[j][0]);
-    const float mv1 = sum32(st.mv[j][1]);
-    const float mvg = k_sel ? mv1 : mv0;
+    const float lt = wave_sum(st.l[j]) * 0.25f;      // each token counted by four lanes
+    float mvq = st.mv[j];                             // over the 16 lanes sharing q
+    mvq += __shfl_xor(mvq, 4);
+    mvq += __shfl_xor(mvq, 8);
+    mvq += __shfl_xor(mvq, 16);
+    mvq += __shfl_xor(mvq, 32);
+    const float mvg = __shfl(mvq, n >> 2);            // group of channels 8n .. 8n + 7
+    float ov[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float x = fmaf(st.acc[j][t], fs[t], st.ow[j][t]);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      ov[t] = x + mvg;
+    }
     if (lane == 0) {
       wm[wave][j] = st.m[j];
       wl[wave][j] = lt;
     }
-    *reinterpret_cast<float2*>(&wo[wave][j][2 * lane]) =
-        make_float2(st.o[j][0] + mvg, st.o[j][1] + mvg);
+    if (lane < 16) {
+      *reinterpret_cast<float4*>(&wo[wave][j][8 * n]) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      *reinterpret_cast<float4*>(&wo[wave][j][8 * n + 4]) = make_float4(ov[4], ov[5], ov[6], ov[7]);
+    }
   }
   __syncthreads();
 
@@ -516,8 +597,7 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
 #define KVQ_DLB(G_, NW_) KVQ_DL(2, 2, G_, NW_) KVQ_DL(2, 4, G_, NW_) KVQ_DL(4, 2, G_, NW_) \
   KVQ_DL(4, 4, G_, NW_)
   KVQ_DLB(1, 4) KVQ_DLB(2, 4) KVQ_DLB(4, 4) KVQ_DLB(8, 4)
-  KVQ_DLB(1, 8) KVQ_DLB(2, 8) KVQ_DLB(4, 8) KVQ_DLB(8, 8)
-  KVQ_DLB(1, 16)
+  KVQ_DLB(1, 8) KVQ_DLB(1, 16)
 #undef KVQ_DLB
 #undef KVQ_DL
   return hipErrorInvalidValue;

@@ -113,7 +113,6 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
   if constexpr (VB != 0) {
    if (a.v != nullptr) {
     constexpr float L = (float)((1 << VB) - 1);
-    constexpr int TPW = 32 / VB;                // tokens per word
     load_tile(tile, a.v + b * a.vs_b + h * a.vs_h + (int64_t)blk * kGroup * a.vs_t, a.vs_t);
     __syncthreads();
     if (tid < kGroup * (kHeadDim / kGroup)) {   // one thread per (token, group)
@@ -143,18 +142,28 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
       st[g4 * kGroup + t] = make_float2(g.mn, g.inv);
     }
     __syncthreads();
+    // Tiled value layout: 8-token x 8-channel tiles in (token octet, channel octet)
+    // order, 2*VB words each.  Word i (and i + 4 for 4-bit codes) of a tile holds token
+    // pair i: the even token in bits 0..15, the odd one in bits 16..31, the tile's
+    // channels VB bits apart from bit 0 of each half.
+    constexpr int F = 16 / VB;                  // channels per half word
+    constexpr int WT = 2 * VB;                  // words per tile
 #pragma unroll
     for (int i = 0; i < (kHeadDim * VB) / kThreads; ++i) {
-      const int wi = tid + i * kThreads;        // word index in [D][VB]
-      const int d = wi / VB;
-      const int t0 = (wi % VB) * TPW;
-      const int g4 = d / kGroup;
+      const int wi = tid + i * kThreads;        // word index within the block
+      const int tl = wi / WT, m = wi % WT;
+      const int t0 = 8 * (tl / (kHeadDim / 8)) + 2 * (m & 3);
+      const int c0 = 8 * (tl % (kHeadDim / 8)) + F * (m >> 2);
+      const int g4 = c0 / kGroup;
       uint32_t word = 0;
 #pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const float2 g = st[g4 * kGroup + t0 + j];
-        const uint32_t q = code_of(f16_bits_to_f32(tile[t0 + j][d]), g.x, g.y, L);
-        word |= q << (VB * j);
+      for (int hh = 0; hh < 2; ++hh) {
+        const float2 g = st[g4 * kGroup + t0 + hh];
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+          const uint32_t q = code_of(f16_bits_to_f32(tile[t0 + hh][c0 + j]), g.x, g.y, L);
+          word |= q << (16 * hh + VB * j);
+        }
       }
       a.v_codes[dst * (kHeadDim * VB) + wi] = word;
     }

@@ -56,8 +56,12 @@
  *      token at bit (Bk*d) % 32 of word (Bk*d) / 32 of that token's row.
  *    k_meta  [batch][kv_heads][nb][D] words: scale_h | min_h << 16 of (block, d).
  *  UNIFORM values, bits Bv (2 or 4), per-token groups of 32 channels:
- *    v_codes [batch][kv_heads][nb][D][Bv words]: token j of the block at bit
- *      (Bv*j) % 32 of word (Bv*j) / 32 of its channel's row.
+ *    v_codes [batch][kv_heads][nb][D*Bv words]: each block is cut into tiles of
+ *      8 tokens x 8 channels, stored in (token octet, channel octet) order with
+ *      2*Bv words per tile.  Token pair i of a tile (tokens 2i, 2i+1 of the octet)
+ *      owns word i (Bv = 2) or words i and i + 4 (Bv = 4: channels 0..3 of the
+ *      octet, then 4..7); the even token fills bits 0..15 and the odd token bits
+ *      16..31, the channels Bv bits apart from bit 0 of each half.
  *    v_meta  [batch][kv_heads][nb*32 tokens][D/32] words.
  *  NUQ codes (3 bits), keys and values alike:
  *    [batch][kv_heads][nb][D][3 words]: per block and channel, word 0 holds the

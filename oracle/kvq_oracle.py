@@ -179,19 +179,47 @@ def unpack_k_codes(words: np.ndarray, bits: int, d: int) -> np.ndarray:
     return _unpack_fields(words, bits, d).reshape(*lead, nb * g, d)
 
 
+def v_code_positions(bits: int, d: int = 128):
+    """Word index within a block and bit position of the code of (token j, channel c),
+    for every j in 0..31 and c in 0..d-1 of a per-token value block.
+
+    A block is cut into tiles of 8 tokens x 8 channels, stored tile after tile in the
+    order (token octet, channel octet), 2*bits words per tile.  Inside a tile, token pair
+    i (tokens 2i, 2i+1 of the octet) owns words i and, for 4-bit codes, i + 4; the even
+    token of the pair fills the low 16 bits of those words and the odd token the high 16
+    bits; the tile's channels follow one another from bit 0 of each half, ``bits`` bits
+    apart (2 bits: 8 channels in one half word; 4 bits: channels 0..3 in word i, 4..7 in
+    word i + 4).  Returns int arrays ``word[j, c]`` and ``bit[j, c]``."""
+    j = np.arange(GROUP)[:, None]
+    c = np.arange(d)[None, :]
+    per_half = 16 // bits                                # channels in one half word
+    tile = (j // 8) * (d // 8) + c // 8
+    pair, odd = (j % 8) // 2, j % 2
+    word = tile * (2 * bits) + pair + 4 * ((c % 8) // per_half)
+    bit = 16 * odd + bits * ((c % 8) % per_half)
+    return np.broadcast_to(word, (GROUP, d)), np.broadcast_to(bit, (GROUP, d))
+
+
 def pack_v_codes(codes: np.ndarray, bits: int) -> np.ndarray:
-    """[..., N, D] -> [..., N/32, D, bits words]: channel-major within a block; token j of
-    the block sits at bit (bits*j) % 32 of word (bits*j) // 32 of its channel."""
+    """[..., N, D] -> [..., N/32, D*bits words]: per block of 32 tokens, the tiled layout
+    of v_code_positions."""
     *lead, n, d = codes.shape
-    blk = codes.reshape(*lead, n // GROUP, GROUP, d)
-    blk = np.swapaxes(blk, -1, -2)                         # [..., nb, D, 32]
-    return _pack_fields(blk, bits)                          # [..., nb, D, bits]
+    blk = codes.reshape(*lead, n // GROUP, GROUP, d).astype(np.uint64)
+    word, bit = v_code_positions(bits, d)
+    out = np.zeros((*lead, n // GROUP, d * bits), dtype=np.uint64)
+    for jj in range(GROUP):
+        for cc in range(d):
+            out[..., word[jj, cc]] |= blk[..., jj, cc] << np.uint64(bit[jj, cc])
+    return out.astype(np.uint32)
 
 
 def unpack_v_codes(words: np.ndarray, bits: int) -> np.ndarray:
-    *lead, nb, d, _ = words.shape
-    c = _unpack_fields(words, bits, GROUP)                 # [..., nb, D, 32]
-    return np.swapaxes(c, -1, -2).reshape(*lead, nb * GROUP, d)
+    *lead, nb, nw = words.shape
+    d = nw // bits
+    word, bit = v_code_positions(bits, d)
+    w = words.astype(np.uint64)[..., word]                # [..., nb, 32, D]
+    c = (w >> bit.astype(np.uint64)) & np.uint64((1 << bits) - 1)
+    return c.reshape(*lead, nb * GROUP, d).astype(np.uint8)
 
 
 def nuq3_bit_positions():

@@ -34,7 +34,7 @@ def test_quantize_bit_exact_with_offset_and_strides(kb, vb):
     K.kvq_quantize_values(cache.c, vd[:, :, off:], H * T * 128, T * 128, 128, off, n)
     kw = host_words(cache.buf("k_codes")).reshape(B, H, cap // 32, 32, 128 * kb // 32)
     km = host_words(cache.buf("k_meta")).reshape(B, H, cap // 32, 128)
-    vw = host_words(cache.buf("v_codes")).reshape(B, H, cap // 32, 128, vb)
+    vw = host_words(cache.buf("v_codes")).reshape(B, H, cap // 32, 128 * vb)
     vm = host_words(cache.buf("v_meta")).reshape(B, H, cap, 4)
     kc, ks, kmn = O.quantize_keys_per_channel(k[:, :, off:off + n], kb)
     vc, vs, vmn = O.quantize_values_per_token(v[:, :, off:off + n], vb)
@@ -95,7 +95,7 @@ def test_streaming_append_bit_exact(R, n, kb, vb):
     N = ref.n_packed
     nb = N // 32
     kw = host_words(cache.buf("k_codes")).reshape(B, H, cap // 32, 32, 128 * kb // 32)
-    vw = host_words(cache.buf("v_codes")).reshape(B, H, cap // 32, 128, vb)
+    vw = host_words(cache.buf("v_codes")).reshape(B, H, cap // 32, 128 * vb)
     km = host_words(cache.buf("k_meta")).reshape(B, H, cap // 32, 128)
     vm = host_words(cache.buf("v_meta")).reshape(B, H, cap, 4)
     assert np.array_equal(kw[:, :, :nb], O.pack_k_codes(ref.k_codes, kb))

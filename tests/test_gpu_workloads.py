@@ -77,7 +77,7 @@ def _check_uniform_head(c, w, b, h, N, r, out, q):
     B, H, D = w.batch, w.kv_heads, w.head_dim
     cap = c.c.capacity_tokens
     kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 32, D * w.k_bits // 32)
-    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, D, w.v_bits)
+    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, D * w.v_bits)
     km = host_words(c.buf("k_meta")).reshape(B, H, cap // 32, D)
     vm = host_words(c.buf("v_meta")).reshape(B, H, cap, D // 32)
     nb = N // 32

@@ -26,13 +26,22 @@ def test_k_pack_round_trip(bits):
     assert np.array_equal(O.unpack_k_codes(w, bits, 128), c)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 4])
+@pytest.mark.parametrize("bits", [2, 4])
 def test_v_pack_round_trip(bits):
     rng = np.random.default_rng(10 + bits)
     c = rng.integers(0, 2 ** bits, (2, 3, 64, 128)).astype(np.uint8)
     w = O.pack_v_codes(c, bits)
-    assert w.shape == (2, 3, 2, 128, bits)
+    assert w.shape == (2, 3, 2, 128 * bits)
     assert np.array_equal(O.unpack_v_codes(w, bits), c)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_v_positions_are_a_bijection(bits):
+    word, bit = O.v_code_positions(bits)
+    slots = word.astype(np.int64) * 32 + bit
+    assert np.unique(slots).size == 32 * 128
+    assert slots.min() == 0 and slots.max() == 32 * 128 * bits - bits
+    assert np.all(slots % bits == 0)
 
 
 def test_nuq3_pack_round_trip():
@@ -80,13 +89,35 @@ def test_k_layout_bit_positions_by_hand():
 
 def test_v_layout_bit_positions_by_hand():
     c = np.zeros((64, 128), np.uint8)
-    c[0, 9] = 3          # block 0, token 0, channel 9 -> word 0 bits 0-1
-    c[17, 9] = 1         # token 17 -> word 1 (34 // 32), bits 2-3
-    c[63, 100] = 2       # block 1, token 31, channel 100 -> word 1 bits 30-31
+    c[0, 9] = 3          # tile (octet 0, channel octet 1) = 1: word 4*1 + pair 0; channel 1 -> bits 2-3
+    c[17, 9] = 1         # token octet 2 -> tile 33, pair 0, odd token -> word 132, bits 16 + 2
+    c[63, 100] = 2       # block 1, token 31: tile 3*16 + 12 = 60, pair 3, odd; ch 4 -> word 243, bit 24
     w = O.pack_v_codes(c, 2)
-    assert w[0, 9, 0] == 3 and w[0, 9, 1] == (1 << 2)
-    assert w[1, 100, 1] == (2 << 30)
+    assert w[0, 4] == 3 << 2 and w[0, 132] == 1 << 18 and w[1, 243] == 2 << 24
     assert int(np.count_nonzero(w)) == 3
+    c4 = np.zeros((32, 128), np.uint8)
+    c4[0, 9] = 3         # 4-bit: 8 words per tile; channel 1 of the octet -> word 8, bits 4-7
+    c4[0, 13] = 5        # channel 5 -> second word of the pair (8 + 4), bits 4-7
+    c4[7, 8] = 15        # token 7 = pair 3, odd -> word 11, bits 16-19
+    w4 = O.pack_v_codes(c4, 4)
+    assert w4[0, 8] == 3 << 4 and w4[0, 12] == 5 << 4 and w4[0, 11] == 15 << 16
+    assert int(np.count_nonzero(w4)) == 3
+
+
+def test_v_layout_one_mask_gives_a_token_pair_of_one_channel():
+    """In a tile word, the two 16-bit halves hold the two tokens of a pair for the same
+    channels at the same bit positions, so one AND isolates that channel for both."""
+    rng = np.random.default_rng(7)
+    c = rng.integers(0, 4, (32, 128)).astype(np.uint8)
+    w = O.pack_v_codes(c, 2)[0]
+    for tile in (0, 17, 63):
+        o, n = divmod(tile, 16)
+        for i in range(4):
+            x = int(w[tile * 4 + i])
+            for ch in range(8):
+                f = (x >> (2 * ch)) & 0x00030003
+                assert f & 0xFFFF == c[8 * o + 2 * i, 8 * n + ch]
+                assert f >> 16 == c[8 * o + 2 * i + 1, 8 * n + ch]
 
 
 def test_meta_word():
