@@ -6,7 +6,8 @@ libkvq.so       <- decode_attention_10_amd/csrc/*.hip   (the C ABI of include/kv
 libkvq_synth.so <- kvq_synth/synth.hip                 (seeded input generator)
 
 Flags: contraction off (the quantizer's fp32 arithmetic must be one rounding per
-operation), packed-fp32 instructions disabled, IEEE divide (hipcc's default).
+operation), packed-fp32 instructions disabled, IEEE divide (hipcc's default), matrix
+instructions writing ordinary VGPRs (no accumulator-register copies).
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

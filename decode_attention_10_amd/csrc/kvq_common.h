@@ -126,6 +126,8 @@ hipError_t launch_quant_uniform(const QuantArgs& a, int batch, int k_bits, int v
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s);
+hipError_t launch_decode_gqa(const DecodeArgs& a, int k_bits, int v_bits, int gq,
+                             hipStream_t s);
 hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s);
 hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s);

@@ -120,6 +120,13 @@ DECODE_CASES = [
     (1, 3, 2, 2048, 1, 4, 2, 64),
     (2, 1, 4, 8192, 0, 2, 2, 0),        # no window at all, many splits
     (1, 4, 1, 160, 1000, 2, 2, 1024),   # long window: 32 chunks
+    # grouped queries on the matrix cores: every bit pair, one head per workgroup
+    # (heads >= CUs) and split heads with the window in a middle split
+    (1, 2, 2, 3072, 77, 4, 4, 128),
+    (2, 3, 4, 1536, 128, 4, 4, 128),
+    (1, 1, 4, 40960, 100, 2, 2, 128),
+    (64, 5, 4, 96, 5, 2, 2, 128),
+    (48, 6, 2, 64, 31, 2, 4, 128),
 ]
 
 
