@@ -9,7 +9,7 @@
 // so one lane owns a channel pair i, keeps a_i for the current token and advances it
 // by e^(-i th_i) per token (a complex product); each block restarts it from an angle
 // t0 * th_i reduced modulo 2 pi in fp64.  Per-pair partial scores of the block's 32
-// tokens are then summed across lanes.  Outliers: the dense pass uses the stored code
+// tokens are then summed across lanes (lanes 2t and 2t+1 end with token t).  Outliers: the dense pass uses the stored code
 // everywhere; the lane of token t then walks the token's CSR row and adds
 // a_col(t) * (x - dequant(code)) for each entry, in row order.
 //
@@ -77,7 +77,7 @@ __device__ __forceinline__ float2 rot_at(int64_t t, double theta) {
 }
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
-  return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+  return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
 }
 
 __device__ __forceinline__ float sum32(float x) {
@@ -102,27 +102,42 @@ __device__ __forceinline__ float wave_max(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-// One stage of the transposed reduction: lanes with bit D set keep v[D..2D), the others
-// v[0..D), each adding the half its partner (lane ^ D) does not keep.
-template <int D>
-__device__ __forceinline__ void transpose_stage(float (&v)[32], int lane) {
-  const bool up = lane & D;
+// One in-row stage of the transposed reduction: DPP partner lanes hold the same token
+// subsets; the lane with `high` set keeps v[H..2H), the other v[0..H), each adding the
+// half its partner gives away.
+template <int H, int CTRL>
+__device__ __forceinline__ void row_stage(float (&v)[32], bool high) {
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    const float keep = up ? v[i + D] : v[i];
-    const float send = up ? v[i] : v[i + D];
-    v[i] = keep + __shfl_xor(send, D);
+  for (int i = 0; i < H; ++i) {
+    const float keep = high ? v[i + H] : v[i];
+    const float send = high ? v[i] : v[i + H];
+    v[i] = keep + dpp<CTRL>(0.f, send);
   }
 }
 
-// Lane l ends with the sum over all 64 lanes of v[l & 31].
+__device__ __forceinline__ float bits_f(uint32_t x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ uint32_t f_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Sum over the 64 lanes of v[t] for the 32 tokens t: lane l ends with token l >> 1.
+// Halves of the wave swap with v_permlane32_swap, rows with v_permlane16_swap (one
+// instruction per pair of values), then mirror / half-mirror / quad DPP stages.
 __device__ __forceinline__ float transpose_sum32(float (&v)[32], int lane) {
-  transpose_stage<16>(v, lane);
-  transpose_stage<8>(v, lane);
-  transpose_stage<4>(v, lane);
-  transpose_stage<2>(v, lane);
-  transpose_stage<1>(v, lane);
-  return v[0] + __shfl_xor(v[0], 32);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {               // lanes < 32 keep tokens 0..15
+    const auto r = __builtin_amdgcn_permlane32_swap(f_bits(v[i]), f_bits(v[i + 16]), false,
+                                                    false);
+    v[i] = bits_f(r[0]) + bits_f(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {                // even rows keep 8 of them, odd rows the rest
+    const auto r = __builtin_amdgcn_permlane16_swap(f_bits(v[i]), f_bits(v[i + 8]), false,
+                                                    false);
+    v[i] = bits_f(r[0]) + bits_f(r[1]);
+  }
+  row_stage<4, 0x140>(v, lane & 8);            // row mirror: partner 15 - i
+  row_stage<2, 0x141>(v, lane & 4);            // half-row mirror: partner 7 - i
+  row_stage<1, 0x4E>(v, lane & 2);             // quad_perm [2,3,0,1]
+  return v[0] + dpp<0xB1>(0.f, v[0]);          // quad_perm [1,0,3,2]
 }
 
 template <int GQ>
@@ -132,7 +147,7 @@ struct NuqState {
 
 __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
   alpha = 1.0f;
-  if (__any(s > m)) {
+  if (__any(s > m + 8.0f)) {               // the max may lag by 8 (log2): p < 2^8
     const float mn = fmaxf(m, wave_max(s));
     alpha = exp2f(m - mn);
     m = mn;
@@ -151,8 +166,8 @@ struct PairConsts {
 };
 
 // Softmax over the block's scores and the value accumulation shared by packed blocks
-// and window chunks: s[] holds this lane's token (lane & 31) score per head (log2
-// units, -inf for missing tokens); vw[] the lane's value weights source.
+// and window chunks: s[] holds this lane's token (lane >> 1) score per head (log2
+// units, -inf for missing tokens).
 template <int GQ>
 __device__ __forceinline__ void softmax_block(NuqState<GQ>& st, const float* s, float* p,
                                               float* alpha) {
@@ -180,13 +195,13 @@ struct NuqWaveScratch {
 
 struct NuqBlockRegs {
   uint32_t kw[6], vw[6];     // key / value code words of channels 2l, 2l+1
-  uint32_t vmeta;            // value scale / min of token t (lanes < 32)
-  int32_t r0, r1;            // CSR row of token t (lanes < 32)
+  uint32_t vmeta;            // value scale / min of token lane >> 1
+  int32_t r0, r1;            // CSR row of token lane >> 1
 };
 
 __device__ __forceinline__ void load_nuq_block(NuqBlockRegs& r, const DecodeArgs& a, int64_t bh,
                                                int64_t blk, int lane) {
-  const int t = lane & 31;
+  const int t = lane >> 1;
   const int64_t gblk = bh * a.cap_blocks + blk;
   const int64_t t0 = blk * kGroup;
   const uint32_t* kp = a.k_codes + (gblk * kHeadDim + 2 * lane) * 3;
@@ -211,7 +226,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
                                   const NuqBlockRegs& r, const PairConsts& pc, const Lut& lk,
                                   const Lut& lv, NuqState<GQ>& st, const NuqShared<GQ>& sh,
                                   NuqWaveScratch<GQ>& ws, int lane) {
-  const int t = lane & 31;
+  const int t = lane >> 1;                  // this lane's token after the reduction
   const uint32_t* kw0 = r.kw;
   const uint32_t* kw1 = r.kw + 3;
   const uint32_t* vw0 = r.vw;
@@ -252,7 +267,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   // The block's entries, code words and rotations come from LDS; entries are taken in
   // windows of 64 and each token adds its own in row order.
   const int32_t e_begin = __builtin_amdgcn_readlane(r.r0, 0);
-  const int32_t e_end0 = __builtin_amdgcn_readlane(r.r1, 31);
+  const int32_t e_end0 = __builtin_amdgcn_readlane(r.r1, 63);
   const int64_t e_end = min((int64_t)e_end0, a.csr_capacity);
   if (e_begin < e_end) {
     ws.base[lane] = base;
@@ -261,7 +276,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     for (int64_t w0 = max(e_begin, 0); w0 < e_end; w0 += 64) {
       if (w0 + lane < e_end) ws.ent[lane] = a.csr_ent[bh * a.csr_capacity + w0 + lane];
       __builtin_amdgcn_wave_barrier();
-      if (lane < 32) {
+      {
         const int64_t lo = max((int64_t)r.r0, w0), hi = min((int64_t)r.r1, min(e_end, w0 + 64));
         for (int64_t e = lo; e < hi; ++e) {
           const uint32_t ent = ws.ent[e - w0];
@@ -283,18 +298,18 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     }
   }
 
-  // ---- softmax (both lane halves carry the corrected score of token t)
+  // ---- softmax (lanes 2t and 2t+1 both carry the corrected score of token t)
   float p[GQ], alpha[GQ];
 #pragma unroll
-  for (int j = 0; j < GQ; ++j) s[j] = __shfl(s[j], t) * a.scale_log2;
+  for (int j = 0; j < GQ; ++j) s[j] *= a.scale_log2;
   softmax_block<GQ>(st, s, p, alpha);
 
   // ---- values: p * scale per token into LDS, p * min per lane
   const float vs = lo_f16(r.vmeta), vm = hi_f16(r.vmeta);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    if (lane < 32) ws.ps[j][t] = p[j] * vs;
-    st.mv[j] = st.mv[j] * alpha[j] + (lane < 32 ? p[j] * vm : 0.0f);
+    ws.ps[j][t] = p[j] * vs;
+    st.mv[j] = fmaf(p[j], vm, st.mv[j] * alpha[j]);     // every token counted twice
   }
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
@@ -321,7 +336,7 @@ template <int GQ>
 __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
                                    const PairConsts& pc, NuqState<GQ>& st,
                                    float (*psL)[kGroup], int lane) {
-  const int t = lane & 31;
+  const int t = lane >> 1;                  // this lane's token after the reduction
   const int tok0 = c * kGroup;
   const int nvalid = min(kGroup, a.n_resid - tok0);
   const int64_t pos0 = (int64_t)a.n_blocks * kGroup + tok0;
@@ -348,7 +363,7 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
   softmax_block<GQ>(st, s, p, alpha);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    if (lane < 32) psL[j][t] = p[j];
+    psL[j][t] = p[j];
     st.mv[j] *= alpha[j];
   }
   uint32_t vv[32];
@@ -455,10 +470,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   // ---- wave totals and the workgroup merge
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    const float lt = sum32(lane < 32 ? st.l[j] : 0.0f);
-    const float mvt = sum32(lane < 32 ? st.mv[j] : 0.0f);
-    const float mvall = __shfl(mvt, 0);
-    const float ltall = __shfl(lt, 0);
+    float ltall = sum32(st.l[j]), mvall = sum32(st.mv[j]);
+    ltall = (ltall + __shfl_xor(ltall, 32)) * 0.5f;      // every token counted by two lanes
+    mvall = (mvall + __shfl_xor(mvall, 32)) * 0.5f;
     if (lane == 0) {
       wm[wave][j] = st.m[j];
       wl[wave][j] = ltall;

@@ -246,58 +246,71 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
 
 // Combines the per-split (max, sum, output) partials of one (batch, query head) row.
 // A separate launch: the kernel boundary makes every split's stores visible, which
-// costs far less than device-scope fences in each workgroup of the main kernel.  The
-// split weights are computed in parallel into LDS; each output channel then sums its
-// splits with independent loads.
-constexpr int kMergeThreads = 256;
-
-__device__ __forceinline__ float block_reduce(float x, float* red, bool is_max) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float y = __shfl_xor(x, o);
-    x = is_max ? fmaxf(x, y) : x + y;
-  }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / kWave; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();
-  return r;
-}
+// costs far less than device-scope fences in each workgroup of the main kernel.  Each
+// thread owns one output channel and every 4th split; it issues the loads of a chunk of
+// splits at once and folds them into a running (max, sum, output) (one memory round
+// per chunk); the four split classes are combined in LDS.
+constexpr int kMergeParts = 4;
+constexpr int kMergeThreads = kMergeParts * kHeadDim;
+constexpr int kMergeChunk = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float* partials,
                                                                     float* out, int splits) {
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float red[kMergeThreads / kWave];
-  __shared__ float half_o[kHeadDim];
+  __shared__ float pm[kMergeParts], pl[kMergeParts];
+  __shared__ float po[kMergeParts][kHeadDim];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int d = threadIdx.x & (kHeadDim - 1), part = threadIdx.x >> 7;
   const float* P = partials + row * splits * kPartialStride;
-  float m = kNegInf;
-  for (int s = tid; s < splits; s += kMergeThreads) m = fmaxf(m, P[s * kPartialStride + kHeadDim]);
-  const float M = block_reduce(m, red, true);
-  float l = 0.f;
-  for (int s = tid; s < splits; s += kMergeThreads) {
-    const float e = M == kNegInf ? 0.f : exp2f(P[s * kPartialStride + kHeadDim] - M);
-    wgt[s] = e;
-    l += P[s * kPartialStride + kHeadDim + 1] * e;
+  float M = kNegInf, L = 0.f, O = 0.f;
+  for (int s0 = part; s0 < splits; s0 += kMergeParts * kMergeChunk) {
+    float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const int sp = min(s0 + c * kMergeParts, splits - 1);   // clamped: loads stay uniform
+      const float* p = P + (int64_t)sp * kPartialStride;
+      m[c] = p[kHeadDim];
+      l[c] = p[kHeadDim + 1];
+      o[c] = p[d];
+    }
+    float cm = M;
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c)
+      if (s0 + c * kMergeParts < splits) cm = fmaxf(cm, m[c]);
+    if (cm == kNegInf) continue;                  // nothing but empty splits so far
+    const float sc = exp2f(M - cm);               // 0 while M = -inf
+    L *= sc;
+    O *= sc;
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      if (s0 + c * kMergeParts < splits) {
+        const float e = exp2f(m[c] - cm);
+        L = fmaf(l[c], e, L);
+        O = fmaf(o[c], e, O);
+      }
+    }
+    M = cm;
   }
-  const float L = block_reduce(l, red, false);     // its barrier also publishes wgt[]
-  const int d = tid & (kHeadDim - 1), part = tid >> 7;
-  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-  int s = part;
-  for (; s + 6 < splits; s += 8) {
-    o0 += P[s * kPartialStride + d] * wgt[s];
-    o1 += P[(s + 2) * kPartialStride + d] * wgt[s + 2];
-    o2 += P[(s + 4) * kPartialStride + d] * wgt[s + 4];
-    o3 += P[(s + 6) * kPartialStride + d] * wgt[s + 6];
+  if (d == 0) {
+    pm[part] = M;
+    pl[part] = L;
   }
-  for (; s < splits; s += 2) o0 += P[s * kPartialStride + d] * wgt[s];
-  const float o = (o0 + o1) + (o2 + o3);
-  if (part == 1) half_o[d] = o;
+  po[part][d] = O;
   __syncthreads();
-  if (part == 0) out[row * kHeadDim + d] = L > 0.f ? (o + half_o[d]) / L : 0.f;
+  if (part == 0) {
+    float Mt = kNegInf;
+#pragma unroll
+    for (int q = 0; q < kMergeParts; ++q) Mt = fmaxf(Mt, pm[q]);
+    float Lt = 0.f, Ot = 0.f;
+    if (Mt != kNegInf) {
+#pragma unroll
+      for (int q = 0; q < kMergeParts; ++q) {
+        const float e = exp2f(pm[q] - Mt);
+        Lt = fmaf(pl[q], e, Lt);
+        Ot = fmaf(po[q][d], e, Ot);
+      }
+    }
+    out[row * kHeadDim + d] = Lt > 0.f ? Ot / Lt : 0.f;
+  }
 }
 
 }  // namespace
