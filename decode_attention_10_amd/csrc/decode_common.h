@@ -131,8 +131,7 @@ struct WaveState {
   float m[GQ];          // running max (log2 domain), wave-uniform
   float l[GQ];          // this lane's sum of p (every token counted by 4 lanes)
   float mv[GQ];         // sum of p * min over this lane's two tokens, group q
-  float acc[GQ][8];     // packed values, channels 8n + T (field-scaled)
-  float ow[GQ][8];      // fp16 window values, channels 8n + T
+  float acc[GQ][8];     // values, channels 8n + T, in units of the packed fields' scale
 };
 
 // Online softmax for one head over this lane's two scores; the running maximum is only
@@ -148,10 +147,7 @@ __device__ __forceinline__ void softmax_pair(WaveState<GQ>& st, int j, float sA,
     st.l[j] *= alpha;
     st.mv[j] *= alpha;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      st.acc[j][t] *= alpha;
-      st.ow[j][t] *= alpha;
-    }
+    for (int t = 0; t < 8; ++t) st.acc[j][t] *= alpha;
   }
   pA = fast_exp2(sA - st.m[j]);
   pB = fast_exp2(sB - st.m[j]);
@@ -165,7 +161,9 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // One chunk of up to 32 fp16 window tokens, with the same lane roles as a packed block.
-template <int GQ>
+// Its value sums are folded into the packed accumulators, which carry the factor
+// 2^(pos - 24) of the packed fields (VB-bit codes): a power of two, so exactly.
+template <int GQ, int VB>
 __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, int c,
                                                WaveState<GQ>& st, const uint32_t (*qh)[64],
                                                float (*pL)[kGroup], int lane) {
@@ -220,14 +218,20 @@ __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, 
     const float4* pp = reinterpret_cast<const float4*>(&pL[j][8 * o]);
     const float4 u0 = pp[0], u1 = pp[1];
     const float pw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float ow[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ow[t] = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        st.ow[j][2 * k] = fmaf(pw[t], lo_f16(vw[t][k]), st.ow[j][2 * k]);
-        st.ow[j][2 * k + 1] = fmaf(pw[t], hi_f16(vw[t][k]), st.ow[j][2 * k + 1]);
+        ow[2 * k] = fmaf(pw[t], lo_f16(vw[t][k]), ow[2 * k]);
+        ow[2 * k + 1] = fmaf(pw[t], hi_f16(vw[t][k]), ow[2 * k + 1]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      st.acc[j][t] = fmaf(ow[t], 1.0f / field_scale(VB, VB == 2 ? t : (t & 3)), st.acc[j][t]);
   }
 }
 
@@ -252,7 +256,7 @@ __device__ __forceinline__ void finish_wave_state(const WaveState<GQ>& st, float
     float ov[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      float x = fmaf(st.acc[j][t], fs[t], st.ow[j][t]);
+      float x = st.acc[j][t] * fs[t];
       x += __shfl_xor(x, 16);
       x += __shfl_xor(x, 32);
       ov[t] = x + mvg;
@@ -276,7 +280,7 @@ __device__ __forceinline__ void init_wave_state(WaveState<GQ>& st) {
     st.l[j] = 0.f;
     st.mv[j] = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) st.acc[j][t] = st.ow[j][t] = 0.f;
+    for (int t = 0; t < 8; ++t) st.acc[j][t] = 0.f;
   }
 }
 

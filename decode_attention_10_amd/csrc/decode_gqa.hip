@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kGqWaves * kWave) void decode_gqa_kernel(DecodeArgs
     for (int c = 0; c < nchunks; ++c) {
       const int u = a.n_blocks + kWindowUnits * c;
       if (u >= s0 && u < s1 && NW - 1 - (c % NW) == wave)
-        process_window<GQ>(a, bh, c, ws, qh, reinterpret_cast<float(*)[kGroup]>(winp[wave]), lane);
+        process_window<GQ, VB>(a, bh, c, ws, qh, reinterpret_cast<float(*)[kGroup]>(winp[wave]), lane);
     }
     finish_wave_state<GQ, VB>(ws, wm[NW + wave], wl[NW + wave], wo[NW + wave], lane);
   }

@@ -211,7 +211,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   for (int c = 0; c < nchunks; ++c) {
     const int u = a.n_blocks + kWindowUnits * c;
     if (u >= s0 && u < s1 && NW - 1 - (c % NW) == wave)
-      process_window<GQ>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
+      process_window<GQ, VB>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
   }
   if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
