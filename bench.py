@@ -38,8 +38,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "decode_attention_10_amd", "csrc")
-KERNEL_SOURCES = {"decode_uniform_kernel": ("decode_uniform.hip", "kvq_common.h"),
-                  "decode_nuq_kernel": ("decode_nuq.hip", "kvq_common.h")}
+KERNEL_SOURCES = {
+    "decode_uniform_kernel": ("decode_uniform.hip", "decode_common.h", "kvq_common.h"),
+    "decode_gqa_kernel": ("decode_gqa.hip", "decode_common.h", "kvq_common.h"),
+    "decode_nuq_kernel": ("decode_nuq.hip", "kvq_common.h"),
+}
+
+
+def uniform_decode_kernel(w) -> str:
+    """The decode kernel the library runs for a uniform cache: the matrix-core kernel for 2
+    or 4 query heads per kv head, else the vector kernel."""
+    return "decode_gqa_kernel" if w.q_heads // w.kv_heads in (2, 4) else "decode_uniform_kernel"
 
 
 def kernel_source_digest(kernel: str) -> str:
@@ -448,8 +457,8 @@ def main() -> int:
         "quantize_ms_prefill": round(quant_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("decode_uniform_kernel", w.name),
-                     "kernel": "decode_uniform_kernel", "bytes_per_launch": dec_bytes},
+                     "traffic": measured_traffic(uniform_decode_kernel(w), w.name),
+                     "kernel": uniform_decode_kernel(w), "bytes_per_launch": dec_bytes},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
