@@ -501,4 +501,14 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, int k_bits, int v_bits, int gq
   return hipErrorInvalidValue;
 }
 
+const void* decode_gqa_fn(int k_bits, int v_bits, int gq) {
+#define KVQ_GF(KB_, VB_, G_)                                                        \
+  if (k_bits == KB_ && v_bits == VB_ && gq == G_)                                   \
+    return reinterpret_cast<const void*>(&decode_gqa_kernel<KB_, VB_, G_>);
+  KVQ_GF(2, 2, 2) KVQ_GF(2, 4, 2) KVQ_GF(4, 2, 2) KVQ_GF(4, 4, 2)
+  KVQ_GF(2, 2, 4) KVQ_GF(2, 4, 4) KVQ_GF(4, 2, 4) KVQ_GF(4, 4, 4)
+#undef KVQ_GF
+  return nullptr;
+}
+
 }  // namespace kvq

@@ -527,4 +527,13 @@ hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+const void* decode_nuq_fn(int gq, int nw) {
+  if (nw != 4) return nullptr;
+  if (gq == 1) return reinterpret_cast<const void*>(&decode_nuq_kernel<1, 4>);
+  if (gq == 2) return reinterpret_cast<const void*>(&decode_nuq_kernel<2, 4>);
+  if (gq == 4) return reinterpret_cast<const void*>(&decode_nuq_kernel<4, 4>);
+  if (gq == 8) return reinterpret_cast<const void*>(&decode_nuq_kernel<8, 4>);
+  return nullptr;
+}
+
 }  // namespace kvq

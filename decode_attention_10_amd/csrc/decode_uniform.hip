@@ -336,6 +336,19 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
   return hipErrorInvalidValue;
 }
 
+const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw) {
+#define KVQ_DF(KB_, VB_, G_, NW_)                                                   \
+  if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_)                      \
+    return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_>);
+#define KVQ_DFB(G_, NW_) KVQ_DF(2, 2, G_, NW_) KVQ_DF(2, 4, G_, NW_) KVQ_DF(4, 2, G_, NW_) \
+  KVQ_DF(4, 4, G_, NW_)
+  KVQ_DFB(1, 4) KVQ_DFB(2, 4) KVQ_DFB(4, 4) KVQ_DFB(8, 4)
+  KVQ_DFB(1, 8) KVQ_DFB(1, 16)
+#undef KVQ_DFB
+#undef KVQ_DF
+  return nullptr;
+}
+
 hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.q_heads;
   merge_splits_kernel<<<dim3((unsigned)rows), dim3(kMergeThreads), 0, s>>>(a.partials, a.out,
