@@ -9,9 +9,10 @@
 // so one lane owns a channel pair i, keeps a_i for the current token and advances it
 // by e^(-i th_i) per token (a complex product); each block restarts it from an angle
 // t0 * th_i reduced modulo 2 pi in fp64.  Per-pair partial scores of the block's 32
-// tokens are then summed across lanes (lanes 2t and 2t+1 end with token t).  Outliers: the dense pass uses the stored code
-// everywhere; the lane of token t then walks the token's CSR row and adds
-// a_col(t) * (x - dequant(code)) for each entry, in row order.
+// tokens are then summed across lanes (lanes 2t and 2t+1 end with token t).
+// Outliers: the dense pass uses the stored code everywhere; one lane per CSR entry
+// then computes a_col(t) * (x - dequant(code)) and token t adds its row's
+// corrections in row order.
 //
 // Values: one lane per channel pair as well; o_d += (p_t * s_t) * lut[c_td] plus the
 // per-token minimum term sum_t p_t m_t, identical for every channel.
@@ -178,8 +179,7 @@ __device__ __forceinline__ void softmax_block(NuqState<GQ>& st, const float* s, 
 // Block-invariant values shared by the waves of a workgroup (LDS).
 template <int GQ>
 struct NuqShared {
-  float2 q[GQ][64];          // (q_2i, q_2i+1) per head and pair
-  double theta[64];          // theta_i
+  float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
   float lutk[8];
 };
@@ -188,9 +188,10 @@ struct NuqShared {
 template <int GQ>
 struct NuqWaveScratch {
   float ps[GQ][kGroup];      // p_t * scale_t of the block's tokens
-  float2 base[64];           // e^(-i t0 theta_i) of the block
+  float2 qb[GQ][64];         // q e^(-i t0 theta_i) per head and pair: the block's first token
   uint32_t kc[kHeadDim][3];  // the block's key code words, per channel
-  uint32_t ent[64];          // a window of the block's CSR entries
+  float corr[GQ][64];        // per CSR entry of the window: its score correction
+  uint8_t tok[64];           // per CSR entry of the window: its token in the block
 };
 
 struct NuqBlockRegs {
@@ -232,6 +233,14 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   const uint32_t* vw0 = r.vw;
   const uint32_t* vw1 = r.vw + 3;
 
+  // The block's CSR entries [e_begin, e_end): the first 64 are loaded now, one per
+  // lane, so that the dense work below covers the load.
+  const int64_t e_begin = max((int64_t)__builtin_amdgcn_readlane(r.r0, 0), (int64_t)0);
+  const int64_t e_end =
+      min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), a.csr_capacity);
+  uint32_t ent_first = 0;
+  if (e_begin + lane < e_end) ent_first = a.csr_ent[bh * a.csr_capacity + e_begin + lane];
+
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
   float kd0[32], kd1[32];
@@ -251,10 +260,12 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   }
   const float2 base = rot_at(t0, pc.theta);
   float s[GQ];
+  float2 qb[GQ];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     float part[32];
-    float2 ar = cmul(pc.q[j], base);
+    qb[j] = cmul(pc.q[j], base);
+    float2 ar = qb[j];
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       part[k] = fmaf(ar.x, kd0[k], ar.y * kd1[k]);
@@ -264,35 +275,44 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   }
 
   // ---- outliers: token t's CSR entries replace the dequantized code by the exact value.
-  // The block's entries, code words and rotations come from LDS; entries are taken in
-  // windows of 64 and each token adds its own in row order.
-  const int32_t e_begin = __builtin_amdgcn_readlane(r.r0, 0);
-  const int32_t e_end0 = __builtin_amdgcn_readlane(r.r1, 63);
-  const int64_t e_end = min((int64_t)e_end0, a.csr_capacity);
+  // Entries are taken in windows of 64, one per lane: the lanes of each token mark its
+  // row's slots with the token, every entry lane computes its correction
+  // comp(q e^(-i (t0 + t) theta)) * (x - dequant(code)) (the real part for an even
+  // channel, the imaginary part for an odd one), and the lanes of token t add their
+  // row's corrections in row order.
   if (e_begin < e_end) {
-    ws.base[lane] = base;
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
     ws.kc[2 * lane][0] = kw0[0]; ws.kc[2 * lane][1] = kw0[1]; ws.kc[2 * lane][2] = kw0[2];
     ws.kc[2 * lane + 1][0] = kw1[0]; ws.kc[2 * lane + 1][1] = kw1[1]; ws.kc[2 * lane + 1][2] = kw1[2];
-    for (int64_t w0 = max(e_begin, 0); w0 < e_end; w0 += 64) {
-      if (w0 + lane < e_end) ws.ent[lane] = a.csr_ent[bh * a.csr_capacity + w0 + lane];
+    for (int64_t w0 = e_begin; w0 < e_end; w0 += 64) {
+      const bool has = w0 + lane < e_end;
+      uint32_t ent = ent_first;
+      if (w0 != e_begin) ent = has ? a.csr_ent[bh * a.csr_capacity + w0 + lane] : 0u;
+      const int64_t lo = max((int64_t)r.r0, w0), hi = min((int64_t)r.r1, min(e_end, w0 + 64));
+      if (!(lane & 1))
+        for (int64_t e = lo; e < hi; ++e) ws.tok[e - w0] = (uint8_t)t;
       __builtin_amdgcn_wave_barrier();
-      {
-        const int64_t lo = max((int64_t)r.r0, w0), hi = min((int64_t)r.r1, min(e_end, w0 + 64));
-        for (int64_t e = lo; e < hi; ++e) {
-          const uint32_t ent = ws.ent[e - w0];
-          const int col = (int)(ent & (kHeadDim - 1));
-          const int pr = col >> 1;
-          const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
-          const float khat = fmaf(sh.lutk[code_at(ws.kc[col], t)], sh.ks[col], sh.km[col]);
-          float sn, cs;
-          sincosf((float)((double)t * sh.theta[pr]), &sn, &cs);
-          const float2 rt = cmul(ws.base[pr], make_float2(cs, -sn));
+      if (has) {
+        const int te = ws.tok[lane] & (kGroup - 1);
+        const int col = (int)(ent & (kHeadDim - 1));
+        const int pr = col >> 1;
+        const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
+        const float khat = fmaf(sh.lutk[code_at(ws.kc[col], te)], sh.ks[col], sh.km[col]);
+        const float d = x - khat;
+        const float2 e = sh.rot[te][pr];
+        const bool odd = col & 1;
+        const float u = odd ? e.y : e.x, v = odd ? e.x : -e.y;
 #pragma unroll
-          for (int j = 0; j < GQ; ++j) {
-            const float2 aq = cmul(sh.q[j][pr], rt);
-            s[j] += ((col & 1) ? aq.y : aq.x) * (x - khat);
-          }
+        for (int j = 0; j < GQ; ++j) {
+          const float2 b = ws.qb[j][pr];
+          ws.corr[j][lane] = fmaf(b.x, u, b.y * v) * d;
         }
+      }
+      __builtin_amdgcn_wave_barrier();
+      for (int64_t e = lo; e < hi; ++e) {
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) s[j] += ws.corr[j][e - w0];
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -421,10 +441,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   }
   const Lut lk = load_lut(a.lut_k);
   const Lut lv = load_lut(a.lut_v);
+  for (int j = wave; j < kGroup; j += NW) sh.rot[j][lane] = rot_at(j, pc.theta);
   if (wave == 0) {
-#pragma unroll
-    for (int j = 0; j < GQ; ++j) sh.q[j][lane] = pc.q[j];
-    sh.theta[lane] = pc.theta;
     sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
     sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
     if (lane < 8) sh.lutk[lane] = lut_value(a.lut_k, lane);
