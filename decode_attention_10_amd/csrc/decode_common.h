@@ -321,4 +321,55 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, const float 
 }
 
 }  // namespace
+// Packed blocks of a split dealt to the NW waves of a workgroup when `chunks` window
+// chunks (kWindowUnits each) go to the waves from the last one down, cyclically: the
+// waves with one chunk fewer get kWindowUnits more blocks, the remainder goes one
+// each to the first waves.  Counts never increase with the wave index, so round k of
+// the deal is taken by waves 0..P_k-1 and the k-th block of wave w is block
+// sum_v min(count_v, k) + w.  The counts form four runs: n0 waves of count c0, then
+// n1 of c1, n2 of c2, n3 of c3 (plain scalars: no array the compiler would place in
+// memory).
+struct Deal {
+  int n0, n1, n2, n3, c0, c1, c2, c3;
+  __device__ __forceinline__ int count(int w) const {
+    return c3 + (w < n0 + n1 + n2 ? c2 - c3 : 0) + (w < n0 + n1 ? c1 - c2 : 0) +
+           (w < n0 ? c0 - c1 : 0);
+  }
+  __device__ __forceinline__ int index(int k, int w) const {
+    return w + n0 * min(c0, k) + n1 * min(c1, k) + n2 * min(c2, k) + n3 * min(c3, k);
+  }
+};
+
+// Block of round k (clamped to the wave's last round) for wave w of a split that
+// starts at unit s0; wave-uniform.
+__device__ __forceinline__ int block_of(const Deal d, int s0, int k, int last, int w) {
+  return __builtin_amdgcn_readfirstlane(s0 + d.index(min(k, last), w));
+}
+
+__device__ __forceinline__ Deal deal_blocks(int nb, int chunks, int nw) {
+  const int rem = chunks % nw;                  // waves with one chunk more than the rest
+  const int na = nw - rem;                      // ... and those without it
+  int ca = nb / nw, cb = ca, r = nb % nw;
+  if (rem > 0) {
+    const int extra = kWindowUnits * na;        // blocks that even out the extra chunk
+    if (nb >= extra) {
+      cb = (nb - extra) / nw;
+      ca = cb + kWindowUnits;
+      r = nb - extra - cb * nw;
+    } else {
+      cb = 0;
+      ca = nb / na;
+      r = nb % na;
+    }
+  }
+  // the first r waves get one block more: all of class a first, then class b
+  const int ra = min(r, na), rb = r - ra;
+  Deal d;
+  d.n0 = ra;           d.c0 = ca + 1;
+  d.n1 = na - ra;      d.c1 = ca;
+  d.n2 = rb;           d.c2 = cb + 1;
+  d.n3 = nw - na - rb; d.c3 = cb;
+  return d;
+}
+
 }  // namespace kvq

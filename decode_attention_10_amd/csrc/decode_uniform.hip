@@ -200,19 +200,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   const int units = a.n_blocks + kWindowUnits * nchunks;
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
-  // Packed blocks of the split are dealt round-robin to the waves, so that at any time
-  // the workgroup streams one contiguous stretch of each cache array; window chunks go
-  // to the last waves (which get no more packed blocks than the others).
+  // Window chunks of the split go to the waves from the last one down, cyclically;
+  // packed blocks are dealt in rounds so that every wave ends with about the same
+  // work: in round k the waves with more than k blocks take the next consecutive
+  // blocks (the workgroup streams one contiguous stretch of each cache array).
   const int bend = min(s1, a.n_blocks);
-  const int first = s0 + wave;
-  const int cnt = first < bend ? (bend - first + NW - 1) / NW : 0;
+  const int nb = max(bend - s0, 0);
+  const int c_first = max(s0 - a.n_blocks + kWindowUnits - 1, 0) / kWindowUnits;
+  const int c_end = min(nchunks, max(s1 - a.n_blocks + kWindowUnits - 1, 0) / kWindowUnits);
+  const Deal deal = deal_blocks(nb, max(c_end - c_first, 0), NW);
+  const int cnt = __builtin_amdgcn_readfirstlane(deal.count(wave));
 
   // ---- window chunks first (their loads are short), then the packed blocks
-  for (int c = 0; c < nchunks; ++c) {
-    const int u = a.n_blocks + kWindowUnits * c;
-    if (u >= s0 && u < s1 && NW - 1 - (c % NW) == wave)
+  for (int c = c_first; c < c_end; ++c)
+    if (NW - 1 - ((c - c_first) % NW) == wave)
       process_window<GQ, VB>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
-  }
   if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
     const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
@@ -224,16 +226,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
     // for the loads just issued.
     const int last = cnt - 1;
     BlockRegs<KB, VB> r0, r1, r2;
-    load_block<KB, VB>(r0, hp, first, lane);
-    load_block<KB, VB>(r1, hp, first + min(1, last) * NW, lane);
+    load_block<KB, VB>(r0, hp, block_of(deal, s0, 0, last, wave), lane);
+    load_block<KB, VB>(r1, hp, block_of(deal, s0, 1, last, wave), lane);
     for (int k = 0; k < cnt; k += 3) {
-      load_block<KB, VB>(r2, hp, first + min(k + 2, last) * NW, lane);
+      load_block<KB, VB>(r2, hp, block_of(deal, s0, k + 2, last, wave), lane);
       process_block<KB, VB, GQ>(r0, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
       if (k + 1 >= cnt) break;
-      load_block<KB, VB>(r0, hp, first + min(k + 3, last) * NW, lane);
+      load_block<KB, VB>(r0, hp, block_of(deal, s0, k + 3, last, wave), lane);
       process_block<KB, VB, GQ>(r1, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
       if (k + 2 >= cnt) break;
-      load_block<KB, VB>(r1, hp, first + min(k + 4, last) * NW, lane);
+      load_block<KB, VB>(r1, hp, block_of(deal, s0, k + 4, last, wave), lane);
       process_block<KB, VB, GQ>(r2, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
     }
   }
