@@ -19,13 +19,14 @@
 // half by an fp32 operand.  The power of two 2^(24 - pos) is folded into the staged
 // q*scale / p*scale values.  Products are exact; sums are fp32.
 //
-// Work split: a workgroup of 4 waves handles one (batch, kv head) and a range of
-// blocks (split-K over the context, as in flash-decoding); a wave streams one
-// 32-token block at a time (lane = token x channel half for keys, lane = channel
-// pair for values), with the next block's loads in flight.  The fp16 window is an
-// extra split.  Waves merge in LDS.  With one split per (batch, kv head) the
-// workgroup writes the output; otherwise it writes a (max, sum, output) partial and a
-// second small launch merges the splits.
+// Work split: a workgroup of 4, 8 or 16 waves handles one (batch, kv head) and a
+// range of work units (split-K over the context, as in flash-decoding); a wave
+// streams one 32-token block at a time (keys: a lane covers two tokens x 32
+// channels; values: one 8-token x 8-channel tile), with the next two blocks' loads
+// in flight.  Blocks are dealt to the waves in rounds and the fp16 window chunks go
+// to the last waves, which take correspondingly fewer blocks.  Waves merge in LDS.
+// With one split per (batch, kv head) the workgroup writes the output; otherwise it
+// writes a (max, sum, output) partial and a second small launch merges the splits.
 #include "decode_common.h"
 
 namespace kvq {
