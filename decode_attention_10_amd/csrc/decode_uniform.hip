@@ -250,10 +250,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
 // Combines the per-split (max, sum, output) partials of one (batch, query head) row.
 // A separate launch: the kernel boundary makes every split's stores visible, which
 // costs far less than device-scope fences in each workgroup of the main kernel.  Each
-// thread owns one output channel and every 4th split; it issues the loads of a chunk of
+// thread owns one output channel and every 8th split; it issues the loads of a chunk of
 // splits at once and folds them into a running (max, sum, output) (one memory round
-// per chunk); the four split classes are combined in LDS.
-constexpr int kMergeParts = 4;
+// per chunk, so 64 splits take one round); the eight split classes are combined in LDS.
+constexpr int kMergeParts = 8;
 constexpr int kMergeThreads = kMergeParts * kHeadDim;
 constexpr int kMergeChunk = 8;
 
