@@ -281,12 +281,22 @@ def kv_cache_bytes(layers: int, hidden: int, tokens: int, bits_per_elem: float,
 # (it happens when a token arrives and the window is already full).
 # --------------------------------------------------------------------------
 class StreamingCache:
-    """Per-channel keys / per-token values, one window shared by K and V."""
+    """Per-channel keys / per-token values, one window shared by K and V.
 
-    def __init__(self, batch, heads, head_dim, k_bits, v_bits, residual_len=128):
+    With ``sink_len`` > 0 the first ``sink_len`` tokens of the sequence are kept in fp16
+    for good and never quantized ([GEOM] "Where research goes": InnerQ keeps
+    full-precision windows for both the recent tokens and the attention-sink tokens).
+    Reading: the sink is the sequence's leading tokens, filled before anything else;
+    token order is sink, packed, window."""
+
+    def __init__(self, batch, heads, head_dim, k_bits, v_bits, residual_len=128, sink_len=0):
         assert residual_len % GROUP == 0
         self.B, self.H, self.D = batch, heads, head_dim
         self.kb, self.vb, self.R = k_bits, v_bits, residual_len
+        self.S = sink_len
+        self.k_sink = np.zeros((batch, heads, sink_len, head_dim), np.uint16)
+        self.v_sink = np.zeros((batch, heads, sink_len, head_dim), np.uint16)
+        self.n_sink = 0
         self.k_res = np.zeros((batch, heads, residual_len, head_dim), np.uint16)
         self.v_res = np.zeros((batch, heads, residual_len, head_dim), np.uint16)
         self.k_codes = np.zeros((batch, heads, 0, head_dim), np.uint8)
@@ -312,6 +322,11 @@ class StreamingCache:
 
     def append(self, k_new: np.ndarray, v_new: np.ndarray):
         """k_new, v_new: fp16 bits [B][H][D] for one new token."""
+        if self.n_sink < self.S:
+            self.k_sink[:, :, self.n_sink] = k_new
+            self.v_sink[:, :, self.n_sink] = v_new
+            self.n_sink += 1
+            return
         if self.R == 0:
             raise ValueError("streaming needs a residual window")
         if self.n_resid == self.R:
@@ -321,12 +336,15 @@ class StreamingCache:
         self.n_resid += 1
 
     def dequant(self):
-        """(K_hat, V_hat) float32 [B][H][N + r][D]: packed part dequantized, window as fp16."""
+        """(K_hat, V_hat) float32 [B][H][n_sink + N + r][D]: the sink as fp16, the packed
+        part dequantized, the window as fp16."""
         kd = dequant_keys_per_channel(self.k_codes, self.k_scale, self.k_min)
         vd = dequant_values_per_token(self.v_codes, self.v_scale, self.v_min)
-        r = self.n_resid
-        kd = np.concatenate([kd, f16_to_f32(self.k_res[:, :, :r])], axis=2)
-        vd = np.concatenate([vd, f16_to_f32(self.v_res[:, :, :r])], axis=2)
+        r, ns = self.n_resid, self.n_sink
+        kd = np.concatenate([f16_to_f32(self.k_sink[:, :, :ns]), kd,
+                             f16_to_f32(self.k_res[:, :, :r])], axis=2)
+        vd = np.concatenate([f16_to_f32(self.v_sink[:, :, :ns]), vd,
+                             f16_to_f32(self.v_res[:, :, :r])], axis=2)
         return kd, vd
 
 
@@ -494,25 +512,27 @@ def default_sm_scale(head_dim: int) -> float:
 # --------------------------------------------------------------------------
 # Whole-cache helpers used by the tests (compositions of the functions above).
 # --------------------------------------------------------------------------
-def uniform_cache(k_bits, v_bits, k_b, v_b, n_packed, n_resid):
-    """One-shot cache for tokens [0, n_packed + n_resid): packed prefix and fp16 window.
+def uniform_cache(k_bits, v_bits, k_b, v_b, n_packed, n_resid, n_sink=0):
+    """One-shot cache for tokens [0, n_sink + n_packed + n_resid): an fp16 sink of the first
+    n_sink tokens, the packed part, the fp16 window.
 
-    k_bits/v_bits: fp16 bits [B][H][T][D] with T >= n_packed + n_resid.
+    k_bits/v_bits: fp16 bits [B][H][T][D] with T >= n_sink + n_packed + n_resid.
     Returns a dict of the packed buffers (library layouts) and the dequantized K/V."""
-    kp, vp = k_bits[:, :, :n_packed], v_bits[:, :, :n_packed]
+    p0, p1 = n_sink, n_sink + n_packed
+    kp, vp = k_bits[:, :, p0:p1], v_bits[:, :, p0:p1]
     kc, ks, km = quantize_keys_per_channel(kp, k_b)
     vc, vs, vm = quantize_values_per_token(vp, v_b)
     kd = dequant_keys_per_channel(kc, ks, km)
     vd = dequant_values_per_token(vc, vs, vm)
-    kr = k_bits[:, :, n_packed:n_packed + n_resid]
-    vr = v_bits[:, :, n_packed:n_packed + n_resid]
+    kr = k_bits[:, :, p1:p1 + n_resid]
+    vr = v_bits[:, :, p1:p1 + n_resid]
     return {
         "k_codes": pack_k_codes(kc, k_b),
         "k_meta": pack_meta(ks, km),
         "v_codes": pack_v_codes(vc, v_b),
         "v_meta": pack_meta(vs, vm),
-        "k_hat": np.concatenate([kd, f16_to_f32(kr)], axis=2),
-        "v_hat": np.concatenate([vd, f16_to_f32(vr)], axis=2),
+        "k_hat": np.concatenate([f16_to_f32(k_bits[:, :, :p0]), kd, f16_to_f32(kr)], axis=2),
+        "v_hat": np.concatenate([f16_to_f32(v_bits[:, :, :p0]), vd, f16_to_f32(vr)], axis=2),
     }
 
 
@@ -526,20 +546,24 @@ def rope_query_f16(q_bits: np.ndarray, position: int, theta: float) -> np.ndarra
 
 
 def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: np.ndarray,
-             outlier_bp: int, n_packed: int, n_resid: int, theta: float):
-    """One (batch, head) of a KVQuant-style cache: tokens [0, n_packed) quantized (keys per
-    channel with outliers, values per token), tokens [n_packed, n_packed + n_resid) kept in
-    fp16.  Returns the packed buffers and the float64 keys (RoPE applied at positions
-    0.. when theta > 0) and values attention reads."""
-    kp, vp = k_bits[:n_packed], v_bits[:n_packed]
+             outlier_bp: int, n_packed: int, n_resid: int, theta: float, n_sink: int = 0):
+    """One (batch, head) of a KVQuant-style cache: tokens [0, n_sink) kept in fp16 (the
+    sink), tokens [n_sink, n_sink + n_packed) quantized (keys per channel with outliers over
+    the quantized tokens only, values per token), the next n_resid tokens kept in fp16.
+    Returns the packed buffers and the float64 keys (RoPE applied at positions 0.. in that
+    order when theta > 0) and values attention reads."""
+    p0, p1 = n_sink, n_sink + n_packed
+    kp, vp = k_bits[p0:p1], v_bits[p0:p1]
     kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp)
     vc, vs, vm, vx = nuq_quantize_values(vp, lut_v)
-    kw = k_bits[n_packed:n_packed + n_resid]
-    vw = v_bits[n_packed:n_packed + n_resid]
-    k_hat = np.concatenate([kx, f16_to_f32(kw)], axis=0).astype(np.float64)
-    v_hat = np.concatenate([vx, f16_to_f32(vw)], axis=0).astype(np.float64)
+    kw = k_bits[p1:p1 + n_resid]
+    vw = v_bits[p1:p1 + n_resid]
+    k_hat = np.concatenate([f16_to_f32(k_bits[:p0]), kx, f16_to_f32(kw)],
+                           axis=0).astype(np.float64)
+    v_hat = np.concatenate([f16_to_f32(v_bits[:p0]), vx, f16_to_f32(vw)],
+                           axis=0).astype(np.float64)
     if theta > 0:
-        k_hat = rope_f64(k_hat, np.arange(n_packed + n_resid), theta)
+        k_hat = rope_f64(k_hat, np.arange(p1 + n_resid), theta)
     return {
         "k_codes": pack_nuq3(kc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
         "k_meta": pack_meta(ks, km),
