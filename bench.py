@@ -93,12 +93,12 @@ def copy_calibration(mib: int) -> dict:
 
 def decode_bytes(w, n_packed: int, n_resid: int) -> int:
     """Algorithmic bytes one decode launch must move: packed codes and metadata, the fp16
-    window, q and the fp32 output."""
+    window and attention-sink tokens, q and the fp32 output."""
     bh = w.batch * w.kv_heads
     D = w.head_dim
     codes = bh * n_packed * D * (w.k_bits + w.v_bits) // 8
     meta = bh * (n_packed // 32) * D * 4 + bh * n_packed * (D // 32) * 4
-    window = 2 * bh * n_resid * D * 2
+    window = 2 * bh * (n_resid + w.sink_len) * D * 2
     return codes + meta + window + w.batch * w.q_heads * D * (2 + 4)
 
 
@@ -153,7 +153,8 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
 
     import kvq_synth as S
     from oracle import kvq_oracle as O
-    T = w.n_packed + w.n_resid
+    T = w.ctx
+    S0, S1 = w.sink_len, w.sink_len + w.n_packed
     g = w.gains()
     sm = O.default_sm_scale(w.head_dim)
     gq = w.q_heads // w.kv_heads
@@ -169,7 +170,8 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
                              heads_sel=[h], batch_sel=[b])
             q = S.gen_tensor(w.seed, S.TID_Q, w.batch, w.q_heads, 1, w.head_dim,
                              heads_sel=list(range(h * gq, (h + 1) * gq)), batch_sel=[b])[:, :, 0]
-            c = O.uniform_cache(k, v, w.k_bits, w.v_bits, w.n_packed, w.n_resid)
+            c = O.uniform_cache(k, v, w.k_bits, w.v_bits, w.n_packed, w.n_resid,
+                                n_sink=w.sink_len)
             t0 = time.perf_counter()
             kc = O.unpack_k_codes(c["k_codes"], w.k_bits, w.head_dim)
             vc = O.unpack_v_codes(c["v_codes"], w.v_bits)
@@ -177,8 +179,10 @@ def cpu_baseline(w, budget_s: float = 20.0) -> dict:
             vs, vm = O.unpack_meta(c["v_meta"])
             kd = O.dequant_keys_per_channel(kc, ks, km)
             vd = O.dequant_values_per_token(vc, vs, vm)
-            kd = np.concatenate([kd, O.f16_to_f32(k[:, :, w.n_packed:])], axis=2)
-            vd = np.concatenate([vd, O.f16_to_f32(v[:, :, w.n_packed:])], axis=2)
+            kd = np.concatenate([O.f16_to_f32(k[:, :, :S0]), kd, O.f16_to_f32(k[:, :, S1:])],
+                                axis=2)
+            vd = np.concatenate([O.f16_to_f32(v[:, :, :S0]), vd, O.f16_to_f32(v[:, :, S1:])],
+                                axis=2)
             O.decode_attention_f64(O.f16_to_f32(q), kd, vd, sm)
             t_used += time.perf_counter() - t0
             nbytes += per_unit
@@ -324,7 +328,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     B, Hkv, Hq, D, N, R = w.batch, w.kv_heads, w.q_heads, w.head_dim, w.n_packed, w.residual_len
-    T = N + w.n_resid
+    S0 = w.sink_len                      # tokens [0, S0) in the fp16 sink, packed from S0
+    T = w.ctx
     cap = N + R
 
     # ---- inputs on the device (generator kernel), prefill into the layer copies
@@ -342,14 +347,20 @@ def main() -> int:
     layers = max(1, math.ceil(args.min_rotation_mb * 1e6 / per_layer))
     caches = []
     sT = (B, Hkv * (T + 1) * D, (T + 1) * D, D)
+    k_pk, v_pk = k_src[:, :, S0:], v_src[:, :, S0:]      # first packed token
     for _ in range(layers):
-        c = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R)
-        K.kvq_quantize_keys(c.c, k_src, sT[1], sT[2], sT[3], 0, N)
-        K.kvq_quantize_values(c.c, v_src, sT[1], sT[2], sT[3], 0, N)
+        c = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R,
+                      sink_len=S0)
+        K.kvq_quantize_keys(c.c, k_pk, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(c.c, v_pk, sT[1], sT[2], sT[3], 0, N)
         kr = c.buf("k_resid").view(torch.int16).view(B, Hkv, R, D)
         vr = c.buf("v_resid").view(torch.int16).view(B, Hkv, R, D)
-        kr[:, :, :w.n_resid] = k_src[:, :, N:T]
-        vr[:, :, :w.n_resid] = v_src[:, :, N:T]
+        kr[:, :, :w.n_resid] = k_src[:, :, S0 + N:T]
+        vr[:, :, :w.n_resid] = v_src[:, :, S0 + N:T]
+        if S0:
+            c.buf("k_sink").view(torch.int16).view(B, Hkv, S0, D)[:] = k_src[:, :, :S0]
+            c.buf("v_sink").view(torch.int16).view(B, Hkv, S0, D)[:] = v_src[:, :, :S0]
+            c.c.n_sink = S0
         caches.append(c)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws_bytes = K.kvq_workspace_bytes(caches[0].c, Hq, K.KVQ_OP_DECODE_ATTN)
@@ -361,8 +372,8 @@ def main() -> int:
     qc = K.KVCache(B, Hkv, cap, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=R)
 
     def prefill():
-        K.kvq_quantize_keys(qc.c, k_src, sT[1], sT[2], sT[3], 0, N)
-        K.kvq_quantize_values(qc.c, v_src, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_keys(qc.c, k_pk, sT[1], sT[2], sT[3], 0, N)
+        K.kvq_quantize_values(qc.c, v_pk, sT[1], sT[2], sT[3], 0, N)
 
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(3):
@@ -447,7 +458,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {B}, {Hq} q / {Hkv} kv heads, head_dim {D}, "
-                               f"{N} packed + {w.n_resid} fp16 window tokens, K int{w.k_bits} "
+                               + (f"{S0} fp16 sink + " if S0 else "")
+                               + f"{N} packed + {w.n_resid} fp16 window tokens, K int{w.k_bits} "
                                f"per-channel / V int{w.v_bits} per-token, group 32",
                    "layers_rotated": layers, "flush_every": R},
         "decode_us": round(mean_dec_s * 1e6, 3),

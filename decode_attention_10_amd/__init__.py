@@ -29,8 +29,9 @@ KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_ALIG
 KVQ_AXIS_CHANNEL, KVQ_AXIS_TOKEN = 0, 1
 KVQ_UNIFORM, KVQ_NUQ = 0, 1
 (KVQ_BUF_K_CODES, KVQ_BUF_K_META, KVQ_BUF_V_CODES, KVQ_BUF_V_META, KVQ_BUF_K_RESID,
- KVQ_BUF_V_RESID, KVQ_BUF_K_CSR_ROWPTR, KVQ_BUF_K_CSR_ENT) = range(8)
-KVQ_NUM_BUFS = 8
+ KVQ_BUF_V_RESID, KVQ_BUF_K_CSR_ROWPTR, KVQ_BUF_K_CSR_ENT, KVQ_BUF_K_SINK,
+ KVQ_BUF_V_SINK) = range(10)
+KVQ_NUM_BUFS = 10
 KVQ_OP_QUANTIZE_KEYS, KVQ_OP_DECODE_ATTN = 0, 1
 
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED",
@@ -51,7 +52,8 @@ class kvq_cache(C.Structure):
                 ("v_meta", C.c_void_p), ("k_resid", C.c_void_p), ("v_resid", C.c_void_p),
                 ("k_csr_rowptr", C.c_void_p), ("k_csr_ent", C.c_void_p),
                 ("csr_capacity", C.c_int64), ("n_packed", C.c_int64), ("n_resid", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("sink_len", C.c_int32), ("k_sink", C.c_void_p), ("v_sink", C.c_void_p),
+                ("n_sink", C.c_int32), ("reserved", C.c_int32)]
 
 
 _P = C.POINTER(kvq_cache)
@@ -161,12 +163,13 @@ class KVCache:
     def __init__(self, batch: int, kv_heads: int, capacity_tokens: int, k_bits: int = 2,
                  v_bits: int = 2, residual_len: int = 128, head_dim: int = 128,
                  kind: int = KVQ_UNIFORM, lut=None, outlier_bp: int = 0,
-                 csr_capacity: int | None = None, device="cuda"):
+                 csr_capacity: int | None = None, sink_len: int = 0, device="cuda"):
         import torch
         self.lut = lut
         c = kvq_cache()
         c.batch, c.kv_heads, c.head_dim = batch, kv_heads, head_dim
         c.residual_len, c.capacity_tokens = residual_len, capacity_tokens
+        c.sink_len = sink_len
         c.kq = make_qparams(kind, k_bits, KVQ_AXIS_CHANNEL, lut, outlier_bp)
         c.vq = make_qparams(kind, v_bits, KVQ_AXIS_TOKEN, lut, 0)
         if csr_capacity is None:
@@ -175,7 +178,7 @@ class KVCache:
         sizes = kvq_layout_bytes(c)
         self.bufs = {}
         names = ["k_codes", "k_meta", "v_codes", "v_meta", "k_resid", "v_resid",
-                 "k_csr_rowptr", "k_csr_ent"]
+                 "k_csr_rowptr", "k_csr_ent", "k_sink", "v_sink"]
         for i, n in enumerate(names):
             if sizes[i]:
                 t = torch.zeros(sizes[i], dtype=torch.uint8, device=device)
@@ -196,3 +199,7 @@ class KVCache:
     @property
     def n_resid(self) -> int:
         return int(self.c.n_resid)
+
+    @property
+    def n_sink(self) -> int:
+        return int(self.c.n_sink)

@@ -169,10 +169,10 @@ __device__ __forceinline__ void process_window(const DecodeArgs& a, int64_t bh, 
                                                float (*pL)[kGroup], int lane) {
   const int tp = lane >> 2, q = lane & 3;
   const int n = lane & 15, o = lane >> 4;
-  const int tok0 = c * kGroup;
-  const int nvalid = min(kGroup, a.n_resid - tok0);
-  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim + 32 * q;
-  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 8 * n;
+  const Fp16Chunk ch = fp16_chunk(a, bh, c);
+  const int nvalid = ch.nvalid;
+  const uint16_t* kr = ch.k + 32 * q;
+  const uint16_t* vr = ch.v + 8 * n;
   uint32_t ka[16], kb[16];
   {
     const uint4* pa = reinterpret_cast<const uint4*>(kr + min(tp, nvalid - 1) * kHeadDim);

@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kGqWaves * kWave) void decode_gqa_kernel(DecodeArgs
     reinterpret_cast<uint32_t*>(&sh.aw[2 * GQ][0])[i] = 0u;
   __syncthreads();
 
-  const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+  const int nchunks = fp16_chunks(a);
   const int units = a.n_blocks + kWindowUnits * nchunks;
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);

@@ -357,11 +357,11 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
                                    const PairConsts& pc, NuqState<GQ>& st,
                                    float (*psL)[kGroup], int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
-  const int tok0 = c * kGroup;
-  const int nvalid = min(kGroup, a.n_resid - tok0);
-  const int64_t pos0 = (int64_t)a.n_blocks * kGroup + tok0;
-  const uint16_t* kr = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
-  const uint16_t* vr = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim + 2 * lane;
+  const Fp16Chunk ch = fp16_chunk(a, bh, c);
+  const int nvalid = ch.nvalid;
+  const int64_t pos0 = ch.pos0;
+  const uint16_t* kr = ch.k + 2 * lane;
+  const uint16_t* vr = ch.v + 2 * lane;
   uint32_t kv[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k)
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     st.mv[j] = 0.f;
   }
 
-  const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+  const int nchunks = fp16_chunks(a);
   const int units = a.n_blocks + kWindowUnits * nchunks;
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
@@ -477,11 +477,12 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     load_nuq_block(r0, a, bh, b0, lane);
     for (int i = b0; i < b1; i += 2) {
       load_nuq_block(r1, a, bh, min(i + 1, last), lane);
-      process_nuq_block<GQ>(a, bh, (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave], lane);
+      process_nuq_block<GQ>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave],
+                            lane);
       if (i + 1 >= b1) break;
       load_nuq_block(r0, a, bh, min(i + 2, last), lane);
-      process_nuq_block<GQ>(a, bh, (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh, wsc[wave],
-                            lane);
+      process_nuq_block<GQ>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh,
+                            wsc[wave], lane);
     }
   }
 

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   WaveState<GQ> st;
   init_wave_state<GQ>(st);
 
-  const int nchunks = (a.n_resid + kGroup - 1) / kGroup;
+  const int nchunks = fp16_chunks(a);
   const int units = a.n_blocks + kWindowUnits * nchunks;
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);

@@ -58,6 +58,8 @@ struct DecodeArgs {
   const uint32_t* v_meta;
   const uint16_t* k_resid;
   const uint16_t* v_resid;
+  const uint16_t* k_sink;   // attention-sink window (the sequence's first tokens, fp16)
+  const uint16_t* v_sink;
   const uint16_t* q;
   float* out;
   float* partials;          // [batch][q_heads][splits][kPartialStride]
@@ -70,6 +72,7 @@ struct DecodeArgs {
   float rope_theta;
   int32_t batch, kv_heads, q_heads;
   int32_t residual_len;
+  int32_t sink_len, n_sink;
   int64_t cap_blocks;
   int32_t n_blocks;         // packed blocks (n_packed / 32)
   int32_t n_resid;
@@ -77,6 +80,38 @@ struct DecodeArgs {
   int32_t waves_per_group;  // 4, 8 or 16
   float scale_log2;         // sm_scale * log2(e)
 };
+
+// fp16 tokens of a decode come in chunks of 32: the sink's chunks first (positions
+// 0 .. n_sink-1), then the window's (positions n_sink + n_packed ..).
+__device__ __forceinline__ int fp16_chunks(const DecodeArgs& a) {
+  return (a.n_sink + kGroup - 1) / kGroup + (a.n_resid + kGroup - 1) / kGroup;
+}
+
+struct Fp16Chunk {
+  const uint16_t* k;        // token 0 of the chunk, channel 0 (rows of kHeadDim)
+  const uint16_t* v;
+  int nvalid;               // tokens present, 1..32
+  int64_t pos0;             // sequence position of token 0
+};
+
+__device__ __forceinline__ Fp16Chunk fp16_chunk(const DecodeArgs& a, int64_t bh, int c) {
+  const int sink_chunks = (a.n_sink + kGroup - 1) / kGroup;
+  Fp16Chunk r;
+  if (c < sink_chunks) {
+    const int tok0 = c * kGroup;
+    r.k = a.k_sink + (bh * a.sink_len + tok0) * kHeadDim;
+    r.v = a.v_sink + (bh * a.sink_len + tok0) * kHeadDim;
+    r.nvalid = min(kGroup, a.n_sink - tok0);
+    r.pos0 = tok0;
+  } else {
+    const int tok0 = (c - sink_chunks) * kGroup;
+    r.k = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim;
+    r.v = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim;
+    r.nvalid = min(kGroup, a.n_resid - tok0);
+    r.pos0 = a.n_sink + (int64_t)a.n_blocks * kGroup + tok0;
+  }
+  return r;
+}
 
 constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
 constexpr int kMaxSplits = 2048;               // workgroups per (batch, kv head) at most

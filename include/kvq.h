@@ -42,12 +42,17 @@
  *    n quantized tokens (ties: lower token first) are kept exactly in a CSR
  *    matrix and excluded from the channel's min/max.  A code is still stored
  *    for them; attention uses the exact value.
- *  - Attention: s_t = sm_scale * q . k_t over every cached token (packed tokens
- *    0..n_packed-1 dequantized, window tokens n_packed..n_packed+n_resid-1 in
- *    fp16), softmax over all of them, out = sum_t p_t v_t / sum_t p_t, fp32.
- *    With rope_theta > 0 (nuq caches only) key t is rotated by RoPE at position
- *    t (interleaved pairs (2i, 2i+1), frequency theta^(-2i/D)); the query is
- *    passed already rotated.  GQA: query head h reads kv head h / (Hq / Hkv).
+ *  - Sequence order: the attention-sink tokens (positions 0..n_sink-1, fp16;
+ *    "The KV cache has a geometry problem", section on where research goes:
+ *    full-precision windows for the recent tokens and for the attention-sink
+ *    tokens), then the packed tokens (positions n_sink..n_sink+n_packed-1), then
+ *    the window (the next n_resid positions, fp16).  The sink fills first.
+ *  - Attention: s_t = sm_scale * q . k_t over every cached token (sink and
+ *    window in fp16, packed tokens dequantized), softmax over all of them,
+ *    out = sum_t p_t v_t / sum_t p_t, fp32.  With rope_theta > 0 (nuq caches
+ *    only) key t is rotated by RoPE at its position t (interleaved pairs
+ *    (2i, 2i+1), frequency theta^(-2i/D)); the query is passed already rotated.
+ *    GQA: query head h reads kv head h / (Hq / Hkv).
  *
  * Packed layouts (little-endian 32-bit words, codes least-significant first;
  * G = 32 tokens per block, D = head_dim, nb = capacity_tokens / 32):
@@ -77,6 +82,7 @@
  *  NUQ values (per token over all D channels):
  *    v_meta  [batch][kv_heads][capacity_tokens] words.
  *  Window: k_resid, v_resid [batch][kv_heads][residual_len][D] fp16.
+ *  Sink: k_sink, v_sink [batch][kv_heads][sink_len][D] fp16.
  *
  * Conventions:
  *  - fp16 values travel as uint16_t bit patterns.
@@ -117,7 +123,7 @@ enum { KVQ_UNIFORM = 0, KVQ_NUQ = 1 };
 enum {
   KVQ_BUF_K_CODES = 0, KVQ_BUF_K_META = 1, KVQ_BUF_V_CODES = 2, KVQ_BUF_V_META = 3,
   KVQ_BUF_K_RESID = 4, KVQ_BUF_V_RESID = 5, KVQ_BUF_K_CSR_ROWPTR = 6,
-  KVQ_BUF_K_CSR_ENT = 7, KVQ_NUM_BUFS = 8
+  KVQ_BUF_K_CSR_ENT = 7, KVQ_BUF_K_SINK = 8, KVQ_BUF_V_SINK = 9, KVQ_NUM_BUFS = 10
 };
 
 /* Operations for kvq_workspace_bytes. */
@@ -156,6 +162,12 @@ typedef struct {
   int64_t csr_capacity;    /* entries per (batch, head) segment of k_csr_ent */
   int64_t n_packed;        /* tokens in the packed part (multiple of 32) */
   int32_t n_resid;         /* tokens in the window, 0..residual_len */
+  int32_t sink_len;        /* attention-sink window: the sequence's first sink_len
+                              tokens stay in fp16 and are never quantized; 0..1024 */
+  uint16_t* k_sink;        /* [batch][kv_heads][sink_len][D] fp16 (NULL when sink_len
+                              == 0); written by kvq_append_flush or by the caller */
+  uint16_t* v_sink;
+  int32_t n_sink;          /* tokens in the sink, 0..sink_len */
   int32_t reserved;        /* 0 */
 } kvq_cache;
 
@@ -195,12 +207,17 @@ kvq_status kvq_quantize_values(const kvq_cache* c, const uint16_t* v, int64_t st
                                int64_t n_tokens, void* stream);
 
 /* Append one token per (batch, kv head): k_new, v_new are fp16 [batch][kv_heads][D],
- * contiguous.  If the window is full (n_resid == residual_len) it is first
+ * contiguous.  While the sink has room (n_sink < sink_len) the token goes to sink
+ * slot n_sink and n_sink += 1; nothing else changes.  Otherwise, if the window is
+ * full (n_resid == residual_len) it is first
  * quantized into the packed part at token n_packed (KVQ_ERR_CAPACITY if that
  * would pass capacity_tokens) and n_packed += residual_len, n_resid = 0; then the
  * token is written at window slot n_resid and n_resid += 1.  UNIFORM only, and
- * residual_len > 0.  The counters are updated on the host when the work is
- * enqueued. */
+ * residual_len > 0 once the sink is full.  The counters are updated on the host
+ * when the work is enqueued.  A prefill that starts with a sink copies the first
+ * sink tokens into k_sink/v_sink itself, sets n_sink, and quantizes the following
+ * tokens with the calls above (their token offsets count from the first packed
+ * token). */
 kvq_status kvq_append_flush(kvq_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                             void* stream);
 

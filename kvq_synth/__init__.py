@@ -168,10 +168,11 @@ class Workload:
     outlier_bp: int = 0    # dense-and-sparse: outliers per key channel, basis points
     rope_theta: float = 0.0
     stream_steps: int = 0  # appends (each followed by attention) after the prefill
+    sink_len: int = 0      # fp16 attention-sink tokens at the sequence start (kept full)
 
     @property
     def ctx(self) -> int:
-        return self.n_packed + self.n_resid
+        return self.sink_len + self.n_packed + self.n_resid
 
     def gains(self) -> np.ndarray:
         return key_gains(self.seed, self.kv_heads, self.head_dim, self.n_outlier_ch,
@@ -184,6 +185,8 @@ WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 1, 128, 512, 128, 2, 2, "uniform", SEED_BASE + 1, 4, 50.0),
     "llama2_7b": Workload("llama2_7b", 8, 32, 32, 128, 4096, 128, 2, 2, "uniform",
                           SEED_BASE + 2, 3, 100.0),
+    "llama2_7b_sink": Workload("llama2_7b_sink", 8, 32, 32, 128, 4096, 128, 2, 2, "uniform",
+                               SEED_BASE + 6, 3, 100.0, sink_len=32),
     "llama2_13b_k4v2": Workload("llama2_13b_k4v2", 4, 40, 40, 128, 32768, 128, 4, 2, "uniform",
                                 SEED_BASE + 3, 3, 100.0),
     "llama3_8b_gqa": Workload("llama3_8b_gqa", 1, 32, 8, 128, 131072, 128, 2, 2, "uniform",

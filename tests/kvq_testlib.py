@@ -35,24 +35,33 @@ def assert_close(o: np.ndarray, ref: np.ndarray, what: str = ""):
 
 
 def build_uniform_cache(K, k: np.ndarray, v: np.ndarray, n_packed: int, n_resid: int,
-                        kb: int, vb: int, R: int, cap: int | None = None):
-    """Quantize tokens [0, n_packed) of host K/V ([B][H][T][D] fp16 bits) on the GPU and copy
-    tokens [n_packed, n_packed + n_resid) into the window.  Returns the KVCache."""
+                        kb: int, vb: int, R: int, cap: int | None = None, n_sink: int = 0,
+                        sink_len: int = 0):
+    """Copy tokens [0, n_sink) of host K/V ([B][H][T][D] fp16 bits) into the sink, quantize
+    the next n_packed tokens on the GPU and copy the n_resid after them into the window.
+    Returns the KVCache."""
     import torch
     B, H, T, D = k.shape
     cap = cap if cap is not None else max(32, n_packed)
-    cache = K.KVCache(B, H, cap, k_bits=kb, v_bits=vb, residual_len=R)
+    cache = K.KVCache(B, H, cap, k_bits=kb, v_bits=vb, residual_len=R, sink_len=sink_len)
     kd, vd = dev(k), dev(v)
+    p0, p1 = n_sink, n_sink + n_packed
+    if n_sink:
+        ks = cache.buf("k_sink").view(torch.int16).view(B, H, sink_len, D)
+        vs = cache.buf("v_sink").view(torch.int16).view(B, H, sink_len, D)
+        ks[:, :, :n_sink] = kd[:, :, :n_sink]
+        vs[:, :, :n_sink] = vd[:, :, :n_sink]
     if n_packed:
-        K.kvq_quantize_keys(cache.c, kd, H * T * D, T * D, D, 0, n_packed)
-        K.kvq_quantize_values(cache.c, vd, H * T * D, T * D, D, 0, n_packed)
+        K.kvq_quantize_keys(cache.c, kd[:, :, p0:], H * T * D, T * D, D, 0, n_packed)
+        K.kvq_quantize_values(cache.c, vd[:, :, p0:], H * T * D, T * D, D, 0, n_packed)
     if n_resid:
         kr = cache.buf("k_resid").view(torch.int16).view(B, H, R, D)
         vr = cache.buf("v_resid").view(torch.int16).view(B, H, R, D)
-        kr[:, :, :n_resid] = kd[:, :, n_packed:n_packed + n_resid]
-        vr[:, :, :n_resid] = vd[:, :, n_packed:n_packed + n_resid]
+        kr[:, :, :n_resid] = kd[:, :, p1:p1 + n_resid]
+        vr[:, :, :n_resid] = vd[:, :, p1:p1 + n_resid]
     cache.c.n_packed = n_packed
     cache.c.n_resid = n_resid
+    cache.c.n_sink = n_sink
     torch.cuda.synchronize()
     return cache
 
@@ -70,8 +79,8 @@ def decode(K, cache, q: np.ndarray, sm_scale: float, rope_theta: float = 0.0):
     return out.cpu().numpy(), ws
 
 
-def oracle_uniform_attention(k, v, q, n_packed, n_resid, kb, vb, sm_scale):
-    c = O.uniform_cache(k, v, kb, vb, n_packed, n_resid)
+def oracle_uniform_attention(k, v, q, n_packed, n_resid, kb, vb, sm_scale, n_sink=0):
+    c = O.uniform_cache(k, v, kb, vb, n_packed, n_resid, n_sink=n_sink)
     return O.decode_attention_f64(O.f16_to_f32(q), c["k_hat"], c["v_hat"], sm_scale), c
 
 

@@ -36,9 +36,10 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "kvq.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(kvq_cache), sizeof(kvq_qparams),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(kvq_cache), sizeof(kvq_qparams),
          offsetof(kvq_cache, kq), offsetof(kvq_cache, k_codes), offsetof(kvq_cache, csr_capacity),
-         offsetof(kvq_cache, n_resid), offsetof(kvq_qparams, lut));
+         offsetof(kvq_cache, n_resid), offsetof(kvq_qparams, lut), offsetof(kvq_cache, sink_len),
+         offsetof(kvq_cache, k_sink), offsetof(kvq_cache, v_sink), offsetof(kvq_cache, n_sink));
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -48,7 +49,8 @@ int main(void) {
                                        check=True).stdout.split()))
     want = [C.sizeof(K.kvq_cache), C.sizeof(K.kvq_qparams), K.kvq_cache.kq.offset,
             K.kvq_cache.k_codes.offset, K.kvq_cache.csr_capacity.offset,
-            K.kvq_cache.n_resid.offset, K.kvq_qparams.lut.offset]
+            K.kvq_cache.n_resid.offset, K.kvq_qparams.lut.offset, K.kvq_cache.sink_len.offset,
+            K.kvq_cache.k_sink.offset, K.kvq_cache.v_sink.offset, K.kvq_cache.n_sink.offset]
     assert got == want
 
 
@@ -71,6 +73,10 @@ def test_layout_bytes_uniform():
     assert s[K.KVQ_BUF_V_META] == bh * cap * (D // 32) * 4
     assert s[K.KVQ_BUF_K_RESID] == s[K.KVQ_BUF_V_RESID] == bh * 128 * D * 2
     assert s[K.KVQ_BUF_K_CSR_ROWPTR] == s[K.KVQ_BUF_K_CSR_ENT] == 0
+    assert s[K.KVQ_BUF_K_SINK] == s[K.KVQ_BUF_V_SINK] == 0
+    c.sink_len = 20
+    s = K.kvq_layout_bytes(c)
+    assert s[K.KVQ_BUF_K_SINK] == s[K.KVQ_BUF_V_SINK] == bh * 20 * D * 2
 
 
 def test_layout_bytes_nuq_and_csr_capacity():
@@ -99,6 +105,8 @@ def test_layout_bytes_nuq_and_csr_capacity():
     (lambda c: setattr(c, "capacity_tokens", 100), K.KVQ_ERR_INVALID_ARG),
     (lambda c: setattr(c, "batch", 0), K.KVQ_ERR_INVALID_ARG),
     (lambda c: setattr(c.vq, "kind", K.KVQ_NUQ), K.KVQ_ERR_UNSUPPORTED),
+    (lambda c: setattr(c, "sink_len", -1), K.KVQ_ERR_INVALID_ARG),
+    (lambda c: setattr(c, "sink_len", 1025), K.KVQ_ERR_INVALID_ARG),
 ])
 def test_descriptor_errors(mutate, status):
     c = _desc()
@@ -199,3 +207,28 @@ def test_decode_needs_workspace_for_split_contexts():
         with pytest.raises(K.KvqError) as e:
             K.kvq_decode_attn(c, FAKE, 1, 0.1, 0.0, FAKE, ws, wsb, stream=0)
         assert e.value.status == K.KVQ_ERR_INVALID_ARG
+
+
+def test_sink_errors_leave_state_unchanged():
+    """The sink fills first: an append while it has room needs its buffers; counters
+    outside [0, sink_len] are rejected by append and decode alike."""
+    c = _desc(R=128)
+    _fake_buffers(c)
+    c.sink_len = 4
+    c.k_sink = c.v_sink = None
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_append_flush(c, FAKE, FAKE, stream=0)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    assert (c.n_sink, c.n_packed, c.n_resid) == (0, 0, 0)
+    c.n_sink = 5
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_append_flush(c, FAKE, FAKE, stream=0)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_decode_attn(c, FAKE, 3, 0.1, 0.0, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    c.n_sink = 2                                 # tokens in the sink but no sink buffers
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_decode_attn(c, FAKE, 3, 0.1, 0.0, FAKE, FAKE, 1 << 20, stream=0)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    assert "sink" in K.kvq_last_error()

@@ -103,22 +103,34 @@ DECODE = [
 ]
 
 
-@pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,theta", DECODE)
-def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
-    seed = 300 + N + r + GQ
-    k, v = _kv(seed, B, Hkv, N + r)
+def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0):
+    """Sink tokens [0, ns) in fp16, the next N quantized, the r after them in the window;
+    the query sits at position ns + N + r."""
+    seed = 300 + N + r + GQ + 7 * ns
+    k, v = _kv(seed, B, Hkv, ns + N + r)
     L = S.nuq3_lut()
     cap = max(32, N)
-    c = _nuq_cache(B, Hkv, cap, R, bp, L, L)
+    lk, lv = dev(L), dev(L)
+    c = K.KVCache(B, Hkv, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
+                  outlier_bp=bp, sink_len=S_len)
+    c.c.vq.lut = lv.data_ptr()
+    kd, vd = dev(k), dev(v)
     if N:
-        _quantize(c, k, v, N)
+        wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
+        wq = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        T = ns + N + r
+        K.kvq_quantize_keys(c.c, kd[:, :, ns:], Hkv * T * 128, T * 128, 128, 0, N, wq, wsb)
+        K.kvq_quantize_values(c.c, vd[:, :, ns:], Hkv * T * 128, T * 128, 128, 0, N)
     if r:
-        kd, vd = dev(k), dev(v)
-        c.buf("k_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = kd[:, :, N:N + r]
-        c.buf("v_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = vd[:, :, N:N + r]
-    c.c.n_packed, c.c.n_resid = N, r
+        p1 = ns + N
+        c.buf("k_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = kd[:, :, p1:p1 + r]
+        c.buf("v_resid").view(torch.int16).view(B, Hkv, R, 128)[:, :, :r] = vd[:, :, p1:p1 + r]
+    if ns:
+        c.buf("k_sink").view(torch.int16).view(B, Hkv, S_len, 128)[:, :, :ns] = kd[:, :, :ns]
+        c.buf("v_sink").view(torch.int16).view(B, Hkv, S_len, 128)[:, :, :ns] = vd[:, :, :ns]
+    c.c.n_packed, c.c.n_resid, c.c.n_sink = N, r, ns
     q0 = S.gen_tensor(seed, S.TID_Q, B, Hkv * GQ, 1, 128)[:, :, 0]
-    q = O.rope_query_f16(q0, N + r, theta) if theta > 0 else q0
+    q = O.rope_query_f16(q0, ns + N + r, theta) if theta > 0 else q0
     out = torch.full((B, Hkv * GQ, 128), float("nan"), device="cuda")
     wsb = K.kvq_workspace_bytes(c.c, Hkv * GQ, K.KVQ_OP_DECODE_ATTN)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
@@ -126,12 +138,30 @@ def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
     K.kvq_decode_attn(c.c, dev(q), Hkv * GQ, sm, theta, out, ws, wsb)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    kh = np.zeros((B, Hkv, N + r, 128))
-    vh = np.zeros((B, Hkv, N + r, 128))
+    T = ns + N + r
+    kh = np.zeros((B, Hkv, T, 128))
+    vh = np.zeros((B, Hkv, T, 128))
     for b in range(B):
         for h in range(Hkv):
-            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta)
+            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta, n_sink=ns)
             kh[b, h], vh[b, h] = ref["k_hat"], ref["v_hat"]
     want = O.decode_attention_f64(O.f16_to_f32(q), kh, vh, sm)
     assert np.isfinite(got).all()
-    assert_close(got, want, f"nuq decode B{B} Hkv{Hkv} GQ{GQ} N{N} r{r} bp{bp} theta{theta}")
+    assert_close(got, want,
+                 f"nuq decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} bp{bp} theta{theta}")
+
+
+@pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,theta", DECODE)
+def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
+    _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta)
+
+
+@pytest.mark.parametrize("B,Hkv,GQ,ns,S_len,N,r,R,bp,theta", [
+    (1, 2, 1, 4, 4, 2048, 0, 0, 100, 1e4),
+    (2, 2, 2, 40, 64, 1024, 37, 64, 100, 1e4),
+    (1, 1, 1, 30, 32, 0, 0, 0, 0, 1e4),
+    (1, 1, 8, 16, 16, 512, 3, 32, 100, 500000.0),
+])
+def test_nuq_decode_with_sink_matches_oracle(B, Hkv, GQ, ns, S_len, N, r, R, bp, theta):
+    """Sink keys sit at positions 0 .. ns-1 and shift the packed keys' positions by ns."""
+    _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns, S_len)

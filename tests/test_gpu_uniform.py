@@ -164,3 +164,62 @@ def test_decode_workspace_needs_no_initialization_and_repeats():
     K.kvq_decode_attn(cache.c, qd, Hkv * GQ, 0.09, 0.0, out2, ws, ws.numel())
     torch.cuda.synchronize()
     assert np.array_equal(out1, out2.cpu().numpy())   # same plan, same arithmetic order
+
+
+# ---- attention-sink window: the sequence's first tokens kept in fp16 for good
+# ("The KV cache has a geometry problem", section on where research goes)
+@pytest.mark.parametrize("S_len,R,n,kb,vb", [(4, 32, 3, 2, 2), (4, 32, 40, 2, 4),
+                                             (32, 128, 300, 4, 2), (7, 64, 200, 2, 2)])
+def test_streaming_append_with_sink_bit_exact(S_len, R, n, kb, vb):
+    B, H = 2, 2
+    k, v = _kv(70 + n, B, H, n)
+    cap = max(32, ((n + R) // R) * R)
+    cache = K.KVCache(B, H, cap, k_bits=kb, v_bits=vb, residual_len=R, sink_len=S_len)
+    ref = O.StreamingCache(B, H, 128, kb, vb, residual_len=R, sink_len=S_len)
+    kd, vd = dev(k), dev(v)
+    for t in range(n):
+        K.kvq_append_flush(cache.c, kd[:, :, t].contiguous(), vd[:, :, t].contiguous())
+        ref.append(k[:, :, t], v[:, :, t])
+    assert (cache.n_sink, cache.n_packed, cache.n_resid) == (ref.n_sink, ref.n_packed,
+                                                              ref.n_resid)
+    ns, N, r = ref.n_sink, ref.n_packed, ref.n_resid
+    ks = cache.buf("k_sink").cpu().numpy().view(np.uint16).reshape(B, H, S_len, 128)
+    vs = cache.buf("v_sink").cpu().numpy().view(np.uint16).reshape(B, H, S_len, 128)
+    assert np.array_equal(ks[:, :, :ns], ref.k_sink[:, :, :ns])
+    assert np.array_equal(vs[:, :, :ns], ref.v_sink[:, :, :ns])
+    nb = N // 32
+    kw = host_words(cache.buf("k_codes")).reshape(B, H, cap // 32, 32, 128 * kb // 32)
+    vw = host_words(cache.buf("v_codes")).reshape(B, H, cap // 32, 128 * vb)
+    vm = host_words(cache.buf("v_meta")).reshape(B, H, cap, 4)
+    assert np.array_equal(kw[:, :, :nb], O.pack_k_codes(ref.k_codes, kb))
+    assert np.array_equal(vw[:, :, :nb], O.pack_v_codes(ref.v_codes, vb))
+    assert np.array_equal(vm[:, :, :N], O.pack_meta(ref.v_scale, ref.v_min))
+    kr = cache.buf("k_resid").cpu().numpy().view(np.uint16).reshape(B, H, R, 128)
+    assert np.array_equal(kr[:, :, :r], ref.k_res[:, :, :r])
+
+
+SINK_CASES = [
+    # B, Hkv, GQ, n_sink, sink_len, n_packed, n_resid, kb, vb, R
+    (1, 2, 1, 4, 4, 512, 77, 2, 2, 128),        # vector kernel, split contexts
+    (2, 2, 1, 100, 128, 1024, 0, 4, 2, 128),    # ragged sink chunk, no window
+    (1, 2, 2, 32, 32, 3072, 5, 2, 2, 128),      # matrix-core kernel
+    (1, 1, 4, 7, 16, 40960, 100, 2, 2, 128),    # matrix-core kernel, many splits
+    (3, 1, 8, 20, 32, 96, 31, 2, 4, 64),        # 8 query heads per kv head
+    (1, 1, 1, 30, 32, 0, 0, 2, 2, 32),          # sink only
+    (2, 3, 1, 32, 32, 0, 17, 2, 2, 32),         # sink and window, nothing packed
+    (64, 5, 4, 3, 4, 96, 5, 2, 2, 128),         # one head per workgroup
+]
+
+
+@pytest.mark.parametrize("B,Hkv,GQ,ns,S_len,N,r,kb,vb,R", SINK_CASES)
+def test_decode_with_sink_matches_oracle(B, Hkv, GQ, ns, S_len, N, r, kb, vb, R):
+    seed = 3000 + B * 100 + Hkv * 10 + GQ + N + ns
+    k, v = _kv(seed, B, Hkv, ns + N + r)
+    q = S.gen_tensor(seed, S.TID_Q, B, Hkv * GQ, 1, 128)[:, :, 0]
+    cache = build_uniform_cache(K, k, v, N, r, kb, vb, R, cap=max(32, N + 32), n_sink=ns,
+                                sink_len=S_len)
+    sm = O.default_sm_scale(128)
+    out, _ = decode(K, cache, q, sm)
+    ref, _ = oracle_uniform_attention(k, v, q, N, r, kb, vb, sm, n_sink=ns)
+    assert np.isfinite(out).all()
+    assert_close(out, ref, f"sink decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} K{kb}V{vb}")

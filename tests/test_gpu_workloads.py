@@ -43,19 +43,25 @@ def _host_head(w, b, h, T):
 
 
 def _uniform_prefill(w, N, r, extra=0):
-    T = N + r
+    """Sink tokens [0, S) copied, the next N quantized, the r after them in the window."""
+    S0 = w.sink_len
+    T = S0 + N + r
     kd, vd = _device_kv(w, T, extra)
     Tt = T + extra
     cap = N + w.residual_len * (1 + extra // w.residual_len + 1)
     c = K.KVCache(w.batch, w.kv_heads, cap, k_bits=w.k_bits, v_bits=w.v_bits,
-                  residual_len=w.residual_len)
+                  residual_len=w.residual_len, sink_len=S0)
     D = w.head_dim
-    K.kvq_quantize_keys(c.c, kd, w.kv_heads * Tt * D, Tt * D, D, 0, N)
-    K.kvq_quantize_values(c.c, vd, w.kv_heads * Tt * D, Tt * D, D, 0, N)
+    K.kvq_quantize_keys(c.c, kd[:, :, S0:], w.kv_heads * Tt * D, Tt * D, D, 0, N)
+    K.kvq_quantize_values(c.c, vd[:, :, S0:], w.kv_heads * Tt * D, Tt * D, D, 0, N)
     R = w.residual_len
-    c.buf("k_resid").view(torch.int16).view(w.batch, w.kv_heads, R, D)[:, :, :r] = kd[:, :, N:T]
-    c.buf("v_resid").view(torch.int16).view(w.batch, w.kv_heads, R, D)[:, :, :r] = vd[:, :, N:T]
-    c.c.n_packed, c.c.n_resid = N, r
+    B, H = w.batch, w.kv_heads
+    c.buf("k_resid").view(torch.int16).view(B, H, R, D)[:, :, :r] = kd[:, :, S0 + N:T]
+    c.buf("v_resid").view(torch.int16).view(B, H, R, D)[:, :, :r] = vd[:, :, S0 + N:T]
+    if S0:
+        c.buf("k_sink").view(torch.int16).view(B, H, S0, D)[:] = kd[:, :, :S0]
+        c.buf("v_sink").view(torch.int16).view(B, H, S0, D)[:] = vd[:, :, :S0]
+    c.c.n_packed, c.c.n_resid, c.c.n_sink = N, r, S0
     torch.cuda.synchronize()
     return c, kd, vd
 
@@ -71,9 +77,9 @@ def _decode(c, w, q_bits):
 
 
 def _check_uniform_head(c, w, b, h, N, r, out, q):
-    T = N + r
+    T = w.sink_len + N + r
     k, v = _host_head(w, b, h, T)
-    ref = O.uniform_cache(k, v, w.k_bits, w.v_bits, N, r)
+    ref = O.uniform_cache(k, v, w.k_bits, w.v_bits, N, r, n_sink=w.sink_len)
     B, H, D = w.batch, w.kv_heads, w.head_dim
     cap = c.c.capacity_tokens
     kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 32, D * w.k_bits // 32)
@@ -95,6 +101,7 @@ def _check_uniform_head(c, w, b, h, N, r, out, q):
 @pytest.mark.parametrize("name,units", [
     ("tiny", [(0, 0)]),
     ("llama2_7b", [(0, 0), (3, 17), (7, 31)]),
+    ("llama2_7b_sink", [(0, 0), (5, 30)]),
     ("llama2_13b_k4v2", [(0, 5), (3, 39)]),
 ])
 def test_uniform_workload_full_size(name, units):
