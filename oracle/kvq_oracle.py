@@ -434,10 +434,27 @@ def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int)
     return codes, scale, mins, row_ptr, ent.astype(np.uint32), xhat
 
 
-def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray):
-    """Values of one head [N][D]: per token over all D channels, no outliers.
-    Returns codes [N][D], scale/min [N], x_hat float32 [N][D]."""
+def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int = 0):
+    """Values of one head [N][D]: per token over all D channels.
+
+    Without outliers returns codes [N][D], scale/min [N], x_hat float32 [N][D].  With
+    outlier_bp > 0 each token's vector is quantized dense-and-sparse like a key channel
+    ([KVQ] abstract (iv): outliers isolated for each vector): its ceil(D * bp / 10000)
+    largest magnitudes are kept exactly, and a fifth array [N][k] of entries (channel in
+    bits 0..15, fp16 value in bits 16..31, channels ascending) is returned after scale/min."""
     n, d = v_bits.shape
+    if outlier_bp > 0:
+        k = outlier_count(d, outlier_bp)
+        codes = np.zeros((n, d), np.uint8)
+        scale = np.zeros(n, np.uint16)
+        mins = np.zeros(n, np.uint16)
+        ent = np.zeros((n, k), np.uint32)
+        xhat = np.zeros((n, d), np.float32)
+        for t in range(n):
+            c, sc, mn, oi, xh = nuq_quantize_vector(v_bits[t], lut_bits, k)
+            codes[t], scale[t], mins[t], xhat[t] = c, sc, mn, xh
+            ent[t] = oi.astype(np.uint32) | (v_bits[t, oi].astype(np.uint32) << np.uint32(16))
+        return codes, scale, mins, ent, xhat
     codes = np.zeros((n, d), np.uint8)
     scale = np.zeros(n, np.uint16)
     mins = np.zeros(n, np.uint16)
@@ -546,7 +563,8 @@ def rope_query_f16(q_bits: np.ndarray, position: int, theta: float) -> np.ndarra
 
 
 def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: np.ndarray,
-             outlier_bp: int, n_packed: int, n_resid: int, theta: float, n_sink: int = 0):
+             outlier_bp: int, n_packed: int, n_resid: int, theta: float, n_sink: int = 0,
+             v_outlier_bp: int = 0):
     """One (batch, head) of a KVQuant-style cache: tokens [0, n_sink) kept in fp16 (the
     sink), tokens [n_sink, n_sink + n_packed) quantized (keys per channel with outliers over
     the quantized tokens only, values per token), the next n_resid tokens kept in fp16.
@@ -555,7 +573,11 @@ def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: n
     p0, p1 = n_sink, n_sink + n_packed
     kp, vp = k_bits[p0:p1], v_bits[p0:p1]
     kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp)
-    vc, vs, vm, vx = nuq_quantize_values(vp, lut_v)
+    if v_outlier_bp > 0:
+        vc, vs, vm, v_ent, vx = nuq_quantize_values(vp, lut_v, v_outlier_bp)
+    else:
+        vc, vs, vm, vx = nuq_quantize_values(vp, lut_v)
+        v_ent = np.zeros((n_packed, 0), np.uint32)
     kw = k_bits[p1:p1 + n_resid]
     vw = v_bits[p1:p1 + n_resid]
     k_hat = np.concatenate([f16_to_f32(k_bits[:p0]), kx, f16_to_f32(kw)],
@@ -569,5 +591,5 @@ def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: n
         "k_meta": pack_meta(ks, km),
         "v_codes": pack_nuq3(vc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
         "v_meta": pack_meta(vs, vm),
-        "rowptr": rp, "ent": ent, "k_hat": k_hat, "v_hat": v_hat,
+        "rowptr": rp, "ent": ent, "v_ent": v_ent, "k_hat": k_hat, "v_hat": v_hat,
     }

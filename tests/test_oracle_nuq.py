@@ -136,3 +136,59 @@ def test_rope_query_rounds_rotation():
     ref = O.rope_f64(O.f16_to_f32(q).astype(np.float64)[0][:, None, :], np.array([1000]), 1e4)
     assert np.array_equal(r[0], O.f32_to_f16_bits(ref[:, 0, :].astype(np.float32)))
     assert np.array_equal(O.rope_query_f16(q, 0, 1e4), q)
+
+
+# ---- dense-and-sparse values: outliers isolated for each token's vector (KVQuant review,
+# abstract item (iv)); the table's "-1%" rows keep 1 % of each vector exactly.
+@pytest.mark.parametrize("bp", [100, 250, 1000])
+def test_outlier_invariants_values(bp):
+    N, D = 96, 128
+    v = S.gen_tensor(14, S.TID_V, 1, 1, N, D)[0, 0].copy()
+    v[5, 17] = _f16(300.0)                        # a clear outlier channel in token 5
+    v[9, 3] = v[9, 100] = _f16(-64.0)             # a tie: both kept when k >= 2
+    lut = S.nuq3_lut()
+    codes, sc, mn, ent, xh = O.nuq_quantize_values(v, lut, bp)
+    kk = O.outlier_count(D, bp)
+    assert ent.shape == (N, kk)
+    cols = (ent & 0xFFFF).astype(np.int64)
+    assert np.all(np.diff(cols, axis=1) > 0)                     # ascending, distinct
+    assert np.array_equal((ent >> 16).astype(np.uint16), np.take_along_axis(v, cols, 1))
+    mag = (v & 0x7FFF).astype(np.int64)
+    x = O.f16_to_f32(v)
+    for t in range(N):
+        out = np.zeros(D, bool)
+        out[cols[t]] = True
+        assert mag[t, out].min() >= mag[t, ~out].max()
+        # ties at the threshold go to the lower channels
+        thr = mag[t, out].min()
+        tied = np.nonzero(mag[t] == thr)[0]
+        assert np.array_equal(out[tied], np.arange(len(tied)) < out[tied].sum())
+        assert O.f16_to_f32(mn[t]) == x[t, ~out].min() + np.float32(0)
+        assert np.array_equal(xh[t, out], x[t, out])
+    assert 17 in cols[5] and {3, 100} <= set(cols[9])
+    # without outliers the dense path is the per-token quantizer already pinned
+    c0, s0, m0, xh0 = O.nuq_quantize_values(v, lut)
+    assert O.f16_to_f32(m0[5]) <= O.f16_to_f32(mn[5])
+
+
+def test_value_outliers_by_hand():
+    """Token [1, 2, 9, 3] with one outlier: 9 is kept; the dense range is [1, 3], so the
+    scale is 2/7 and the min 1 (identity code book: levels 0..7)."""
+    v = _f16([[1.0, 2.0, 9.0, 3.0]])
+    codes, sc, mn, ent, xh = O.nuq_quantize_values(v, IDENT, 2500)
+    assert ent.shape == (1, 1) and ent[0, 0] == (2 | (int(_f16(9.0)) << 16))
+    assert O.f16_to_f32(mn[0]) == 1.0
+    assert sc[0] == _f16(2.0 / 7.0)
+    assert xh[0, 2] == 9.0
+    s = O.f16_to_f32(sc[0])
+    assert np.array_equal(codes[0, [0, 1, 3]], np.rint((np.float32([1, 2, 3]) - 1) / s))
+
+
+def test_nuq_head_value_outliers_change_only_the_outlier_values():
+    """Attention reads the exact value at every value outlier."""
+    rng = np.random.default_rng(4)
+    x = O.f32_to_f16_bits(rng.standard_normal((64, 128)).astype(np.float32))
+    h = O.nuq_head(x, x, S.nuq3_lut(), S.nuq3_lut(), 100, 64, 0, 0.0, v_outlier_bp=100)
+    cols = (h["v_ent"] & 0xFFFF).astype(np.int64)
+    rows = np.repeat(np.arange(64), cols.shape[1])
+    assert np.array_equal(h["v_hat"][rows, cols.ravel()], O.f16_to_f32(x)[rows, cols.ravel()])
