@@ -30,8 +30,8 @@ KVQ_AXIS_CHANNEL, KVQ_AXIS_TOKEN = 0, 1
 KVQ_UNIFORM, KVQ_NUQ = 0, 1
 (KVQ_BUF_K_CODES, KVQ_BUF_K_META, KVQ_BUF_V_CODES, KVQ_BUF_V_META, KVQ_BUF_K_RESID,
  KVQ_BUF_V_RESID, KVQ_BUF_K_CSR_ROWPTR, KVQ_BUF_K_CSR_ENT, KVQ_BUF_K_SINK,
- KVQ_BUF_V_SINK) = range(10)
-KVQ_NUM_BUFS = 10
+ KVQ_BUF_V_SINK, KVQ_BUF_V_OUT) = range(11)
+KVQ_NUM_BUFS = 11
 KVQ_OP_QUANTIZE_KEYS, KVQ_OP_DECODE_ATTN = 0, 1
 
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED",
@@ -51,7 +51,8 @@ class kvq_cache(C.Structure):
                 ("k_codes", C.c_void_p), ("k_meta", C.c_void_p), ("v_codes", C.c_void_p),
                 ("v_meta", C.c_void_p), ("k_resid", C.c_void_p), ("v_resid", C.c_void_p),
                 ("k_csr_rowptr", C.c_void_p), ("k_csr_ent", C.c_void_p),
-                ("csr_capacity", C.c_int64), ("n_packed", C.c_int64), ("n_resid", C.c_int32),
+                ("csr_capacity", C.c_int64), ("v_out", C.c_void_p),
+                ("n_packed", C.c_int64), ("n_resid", C.c_int32),
                 ("sink_len", C.c_int32), ("k_sink", C.c_void_p), ("v_sink", C.c_void_p),
                 ("n_sink", C.c_int32), ("reserved", C.c_int32)]
 
@@ -163,7 +164,8 @@ class KVCache:
     def __init__(self, batch: int, kv_heads: int, capacity_tokens: int, k_bits: int = 2,
                  v_bits: int = 2, residual_len: int = 128, head_dim: int = 128,
                  kind: int = KVQ_UNIFORM, lut=None, outlier_bp: int = 0,
-                 csr_capacity: int | None = None, sink_len: int = 0, device="cuda"):
+                 csr_capacity: int | None = None, sink_len: int = 0,
+                 v_outlier_bp: int = 0, device="cuda"):
         import torch
         self.lut = lut
         c = kvq_cache()
@@ -171,14 +173,14 @@ class KVCache:
         c.residual_len, c.capacity_tokens = residual_len, capacity_tokens
         c.sink_len = sink_len
         c.kq = make_qparams(kind, k_bits, KVQ_AXIS_CHANNEL, lut, outlier_bp)
-        c.vq = make_qparams(kind, v_bits, KVQ_AXIS_TOKEN, lut, 0)
+        c.vq = make_qparams(kind, v_bits, KVQ_AXIS_TOKEN, lut, v_outlier_bp)
         if csr_capacity is None:
             csr_capacity = max(0, kvq_csr_entries_needed(c))
         c.csr_capacity = csr_capacity
         sizes = kvq_layout_bytes(c)
         self.bufs = {}
         names = ["k_codes", "k_meta", "v_codes", "v_meta", "k_resid", "v_resid",
-                 "k_csr_rowptr", "k_csr_ent", "k_sink", "v_sink"]
+                 "k_csr_rowptr", "k_csr_ent", "k_sink", "v_sink", "v_out"]
         for i, n in enumerate(names):
             if sizes[i]:
                 t = torch.zeros(sizes[i], dtype=torch.uint8, device=device)

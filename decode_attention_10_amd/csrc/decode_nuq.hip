@@ -181,7 +181,7 @@ template <int GQ>
 struct NuqShared {
   float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
-  float lutk[8];
+  float lutk[8], lutv[8];
 };
 
 // Per-wave scratch (LDS).
@@ -192,6 +192,9 @@ struct NuqWaveScratch {
   uint32_t kc[kHeadDim][3];  // the block's key code words, per channel
   float corr[GQ][64];        // per CSR entry of the window: its score correction
   uint8_t tok[64];           // per CSR entry of the window: its token in the block
+  float pv[GQ][kGroup];      // p_t of the block's tokens (value outliers)
+  uint32_t vmeta[kGroup];    // value scale / min of the block's tokens
+  float vcorr[GQ][kHeadDim]; // value-outlier corrections of the block, per channel
 };
 
 struct NuqBlockRegs {
@@ -240,6 +243,11 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
       min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), a.csr_capacity);
   uint32_t ent_first = 0;
   if (e_begin + lane < e_end) ent_first = a.csr_ent[bh * a.csr_capacity + e_begin + lane];
+  // The block's value outliers: v_kv per token, 32 * v_kv entries from vbase.
+  const int v_ne = a.v_out != nullptr ? kGroup * a.v_kv : 0;
+  const int64_t vbase = (bh * (a.cap_blocks * kGroup) + (t0 - a.n_sink)) * a.v_kv;
+  uint32_t vent_first = 0;
+  if (lane < v_ne) vent_first = a.v_out[vbase + lane];
 
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
@@ -349,6 +357,44 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     st.o[j][0] = o0;
     st.o[j][1] = o1;
   }
+
+  // ---- value outliers: each token's entries replace the dequantized value by the exact
+  // one.  One lane per entry adds p_t * (x - v_hat) for its channel into LDS (the key
+  // code-word scratch now holds the value code words); each lane then takes its two
+  // channels' sums.
+  if (v_ne > 0) {
+    ws.kc[2 * lane][0] = vw0[0]; ws.kc[2 * lane][1] = vw0[1]; ws.kc[2 * lane][2] = vw0[2];
+    ws.kc[2 * lane + 1][0] = vw1[0]; ws.kc[2 * lane + 1][1] = vw1[1];
+    ws.kc[2 * lane + 1][2] = vw1[2];
+    if (!(lane & 1)) {
+      ws.vmeta[t] = r.vmeta;
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) ws.pv[j][t] = p[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int e0 = 0; e0 < v_ne; e0 += 64) {
+      const int e = e0 + lane;
+      if (e < v_ne) {
+        const uint32_t ent = e0 == 0 ? vent_first : a.v_out[vbase + e];
+        const int te = (e / a.v_kv) & (kGroup - 1);
+        const int d = (int)(ent & (kHeadDim - 1));
+        const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
+        const uint32_t vmw = ws.vmeta[te];
+        const float vhat = sh.lutv[code_at(ws.kc[d], te)] * lo_f16(vmw) + hi_f16(vmw);
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) atomicAdd(&ws.vcorr[j][d], ws.pv[j][te] * (x - vhat));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+      const float2 cv = *reinterpret_cast<const float2*>(&ws.vcorr[j][2 * lane]);
+      st.o[j][0] += cv.x;
+      st.o[j][1] += cv.y;
+      *reinterpret_cast<float2*>(&ws.vcorr[j][2 * lane]) = make_float2(0.f, 0.f);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
 }
 
 // Up to 32 fp16 window tokens (positions n_packed + 32 c + j), rotated like the keys.
@@ -446,6 +492,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
     sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
     if (lane < 8) sh.lutk[lane] = lut_value(a.lut_k, lane);
+    if (lane < 8) sh.lutv[lane] = lut_value(a.lut_v, lane);
   }
   __syncthreads();
 
@@ -456,6 +503,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     st.l[j] = 0.f;
     st.o[j][0] = st.o[j][1] = 0.f;
     st.mv[j] = 0.f;
+    *reinterpret_cast<float2*>(&wsc[wave].vcorr[j][2 * lane]) = make_float2(0.f, 0.f);
   }
 
   const int nchunks = fp16_chunks(a);

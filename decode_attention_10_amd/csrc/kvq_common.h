@@ -69,6 +69,8 @@ struct DecodeArgs {
   const int32_t* csr_rowptr;
   const uint32_t* csr_ent;
   int64_t csr_capacity;
+  const uint32_t* v_out;    // value outliers [bh][cap_tokens][v_kv] (NULL: none)
+  int32_t v_kv;
   float rope_theta;
   int32_t batch, kv_heads, q_heads;
   int32_t residual_len;
@@ -153,6 +155,8 @@ struct NuqValuesArgs {
   int64_t cap_tokens, cap_blocks;
   uint32_t* v_codes;
   uint32_t* v_meta;
+  uint32_t* v_out;          // outlier entries [bh][cap_tokens][kv] (NULL: none)
+  int32_t kv;               // outliers per token
 };
 
 // ---- launchers (defined in the .hip files) ------------------------------------

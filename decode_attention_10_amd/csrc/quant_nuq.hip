@@ -387,6 +387,54 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
   }
 }
 
+// Outliers of one token's vector ("KVQuant" review, abstract item (iv): the largest
+// magnitudes of each vector are kept exactly): the kv channels of largest fp16
+// magnitude, ties to the lower channel.  Eight threads (consecutive lanes) hold 16
+// channels each; a binary search finds the threshold T, the largest magnitude with at
+// least kv channels at or above it, then channels above T are outliers and the first
+// kv - count(> T) channels equal to T (in channel order) are too.  Returns this
+// thread's flags (bit j: channel 16 * part + j).
+__device__ __forceinline__ uint32_t count8(uint32_t x) {
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ uint32_t value_outliers(const uint16_t* row, int part, int kv) {
+  uint32_t mag[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) mag[j] = row[j] & 0x7FFFu;
+  uint32_t lo = 0, hi = 0x7FFF;
+  for (int it = 0; it < 15; ++it) {                // hi - lo + 1 halves from 2^15 to 1
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c += mag[j] >= mid ? 1u : 0u;
+    if (count8(c) >= (uint32_t)kv) lo = mid;
+    else hi = mid - 1;
+  }
+  uint32_t above = 0, ties = 0, tie_mask = 0, flags = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (mag[j] > lo) { above += 1; flags |= 1u << j; }
+    if (mag[j] == lo) { ties += 1; tie_mask |= 1u << j; }
+  }
+  const uint32_t need = (uint32_t)kv - count8(above);
+  uint32_t ties_before = ties;                      // ties in lower parts (exclusive scan)
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const uint32_t x = __shfl_up(ties_before, o, 8);
+    if (part >= o) ties_before += x;
+  }
+  ties_before -= ties;
+  uint32_t m = tie_mask;
+  for (uint32_t i = ties_before; m != 0u && i < need; ++i) {
+    flags |= m & (0u - m);                          // lowest remaining tie
+    m &= m - 1u;
+  }
+  return flags;
+}
+
 // ---- values: per token over all channels --------------------------------------------
 __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArgs a) {
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
@@ -409,19 +457,44 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   }
   __syncthreads();
   {
-    // 8 threads per token (same wave): min / max of 16 channels each, then combine
+    // 8 threads per token (same wave), 16 channels each
     const int t = tid >> 3, part = tid & 7;
-    float mn = f16_bits_to_f32(tile[t][part * 16]), mx = mn;
+    const uint16_t* row = &tile[t][part * 16];
+    const uint32_t outm = a.kv > 0 ? value_outliers(row, part, a.kv) : 0u;
+    // min / max of the dense channels, then combine
+    float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
-    for (int j = 1; j < 16; ++j) {
-      const float x = f16_bits_to_f32(tile[t][part * 16 + j]);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+    for (int j = 0; j < 16; ++j) {
+      if (!((outm >> j) & 1u)) {
+        const float x = f16_bits_to_f32(row[j]);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
     }
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) {
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    if (mn > mx) mn = mx = 0.0f;          // every channel an outlier
+    if (a.kv > 0) {
+      // this thread's outliers, channels ascending, after those of the lower parts
+      const uint32_t mine = (uint32_t)__builtin_popcount(outm);
+      uint32_t before = mine;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const uint32_t x = __shfl_up(before, o, 8);
+        if (part >= o) before += x;
+      }
+      before -= mine;
+      const int64_t tok = a.tok0 + (int64_t)blk * kGroup + t;
+      uint32_t* dst = a.v_out + (bh * a.cap_tokens + tok) * a.kv + before;
+      uint32_t m = outm;
+      for (int i = 0; m != 0u; ++i) {
+        const int j = __builtin_ctz(m);
+        m &= m - 1u;
+        dst[i] = (uint32_t)(part * 16 + j) | ((uint32_t)row[j] << 16);
+      }
     }
     if (part == 0) {
       uint32_t meta;

@@ -42,6 +42,10 @@
  *    n quantized tokens (ties: lower token first) are kept exactly in a CSR
  *    matrix and excluded from the channel's min/max.  A code is still stored
  *    for them; attention uses the exact value.
+ *  - Value outliers (nuq values, outlier_bp > 0): per (batch, head, token) the
+ *    kv = ceil(D * outlier_bp / 10000) channels of largest fp16 magnitude (ties:
+ *    lower channel first), handled like the key outliers (KVQuant review,
+ *    abstract item (iv): outliers isolated for each vector, keys and values).
  *  - Sequence order: the attention-sink tokens (positions 0..n_sink-1, fp16;
  *    "The KV cache has a geometry problem", section on where research goes:
  *    full-precision windows for the recent tokens and for the attention-sink
@@ -79,6 +83,8 @@
  *      offsets relative to the head's segment of k_csr_ent;
  *    k_csr_ent [batch][kv_heads][csr_capacity] uint32: channel in bits 0..15,
  *      fp16 value in bits 16..31, channels ascending within a row.
+ *  NUQ value outliers: v_out [batch][kv_heads][capacity_tokens][kv] uint32,
+ *      entries as for the keys, channels ascending (a CSR whose rows all hold kv).
  *  NUQ values (per token over all D channels):
  *    v_meta  [batch][kv_heads][capacity_tokens] words.
  *  Window: k_resid, v_resid [batch][kv_heads][residual_len][D] fp16.
@@ -123,7 +129,8 @@ enum { KVQ_UNIFORM = 0, KVQ_NUQ = 1 };
 enum {
   KVQ_BUF_K_CODES = 0, KVQ_BUF_K_META = 1, KVQ_BUF_V_CODES = 2, KVQ_BUF_V_META = 3,
   KVQ_BUF_K_RESID = 4, KVQ_BUF_V_RESID = 5, KVQ_BUF_K_CSR_ROWPTR = 6,
-  KVQ_BUF_K_CSR_ENT = 7, KVQ_BUF_K_SINK = 8, KVQ_BUF_V_SINK = 9, KVQ_NUM_BUFS = 10
+  KVQ_BUF_K_CSR_ENT = 7, KVQ_BUF_K_SINK = 8, KVQ_BUF_V_SINK = 9, KVQ_BUF_V_OUT = 10,
+  KVQ_NUM_BUFS = 11
 };
 
 /* Operations for kvq_workspace_bytes. */
@@ -137,8 +144,9 @@ typedef struct {
                           axes are valid for the method but KVQ_ERR_UNSUPPORTED */
   int32_t group_size;  /* UNIFORM: 32; NUQ: 0 (the whole vector) */
   const uint16_t* lut; /* NUQ: device fp16[8], ascending, level units; else NULL */
-  int32_t outlier_bp;  /* NUQ keys: outliers per channel in basis points of the
-                          quantized tokens (100 = 1 %), 0..10000; else 0 */
+  int32_t outlier_bp;  /* NUQ: outliers per vector in basis points (100 = 1 %),
+                          0..10000 - keys: of each channel's quantized tokens,
+                          values: of each token's D channels; UNIFORM: 0 */
   int32_t reserved;    /* 0 */
 } kvq_qparams;
 
@@ -160,6 +168,7 @@ typedef struct {
   int32_t* k_csr_rowptr;   /* NUQ keys with outlier_bp > 0, else NULL */
   uint32_t* k_csr_ent;
   int64_t csr_capacity;    /* entries per (batch, head) segment of k_csr_ent */
+  uint32_t* v_out;         /* NUQ values with vq.outlier_bp > 0, else NULL */
   int64_t n_packed;        /* tokens in the packed part (multiple of 32) */
   int32_t n_resid;         /* tokens in the window, 0..residual_len */
   int32_t sink_len;        /* attention-sink window: the sequence's first sink_len

@@ -169,6 +169,7 @@ class Workload:
     rope_theta: float = 0.0
     stream_steps: int = 0  # appends (each followed by attention) after the prefill
     sink_len: int = 0      # fp16 attention-sink tokens at the sequence start (kept full)
+    v_outlier_bp: int = 0  # dense-and-sparse values: outliers per token vector, basis points
 
     @property
     def ctx(self) -> int:
@@ -194,6 +195,9 @@ WORKLOADS = {
     "kvquant_1m": Workload("kvquant_1m", 1, 32, 32, 128, 1048576, 0, 3, 3, "nuq",
                            SEED_BASE + 5, 3, 100.0, residual_len=0, outlier_bp=100,
                            rope_theta=1.0e4),
+    "kvquant_256k_dense_sparse": Workload("kvquant_256k_dense_sparse", 1, 32, 32, 128, 262144, 0,
+                                          3, 3, "nuq", SEED_BASE + 7, 3, 100.0, residual_len=0,
+                                          outlier_bp=100, rope_theta=1.0e4, v_outlier_bp=100),
 }
 
 

@@ -23,10 +23,10 @@ def _kv(seed, B, H, T, D=128, n_out=3, gain=100.0):
             S.gen_tensor(seed, S.TID_V, B, H, T, D))
 
 
-def _nuq_cache(B, H, cap, R, bp, lut_k, lut_v):
+def _nuq_cache(B, H, cap, R, bp, lut_k, lut_v, v_bp=0):
     lk, lv = dev(lut_k), dev(lut_v)
     c = K.KVCache(B, H, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
-                  outlier_bp=bp)
+                  outlier_bp=bp, v_outlier_bp=v_bp)
     c.c.vq.lut = lv.data_ptr()
     c.luts = (lk, lv)
     return c
@@ -60,19 +60,29 @@ def _check_head(c, b, h, ref, n, bp):
         assert np.array_equal(rp[b, h, :n + 1], ref["rowptr"]), "CSR row pointers"
         nnz = int(ref["rowptr"][-1])
         assert np.array_equal(ent[b, h, :nnz], ref["ent"]), "CSR entries"
+    kv = ref["v_ent"].shape[1]
+    if kv:
+        vo = host_words(c.buf("v_out")).reshape(B, H, cap, kv)
+        assert np.array_equal(vo[b, h, :n], ref["v_ent"]), "value outlier entries"
 
 
-@pytest.mark.parametrize("B,H,n,bp,lut", [
-    (1, 1, 64, 0, "ident"), (2, 2, 96, 100, "nf"), (1, 3, 4160, 100, "nf"),
-    (1, 2, 2048 + 256, 250, "nf"), (1, 1, 64, 10000, "nf"), (2, 1, 320, 5000, "ident")])
-def test_nuq_quantize_bit_exact(B, H, n, bp, lut):
-    k, v = _kv(200 + n + bp, B, H, n)
+@pytest.mark.parametrize("B,H,n,bp,lut,v_bp", [
+    (1, 1, 64, 0, "ident", 0), (2, 2, 96, 100, "nf", 0), (1, 3, 4160, 100, "nf", 0),
+    (1, 2, 2048 + 256, 250, "nf", 0), (1, 1, 64, 10000, "nf", 0), (2, 1, 320, 5000, "ident", 0),
+    # dense-and-sparse values: 2, 4, 13 and all 128 channels of each token kept exactly
+    (2, 2, 96, 100, "nf", 100), (1, 1, 128, 0, "nf", 250), (1, 2, 64, 100, "ident", 1000),
+    (1, 1, 32, 0, "nf", 10000)])
+def test_nuq_quantize_bit_exact(B, H, n, bp, lut, v_bp):
+    k, v = _kv(200 + n + bp + v_bp, B, H, n)
+    if v_bp:
+        v = v.copy()
+        v[..., 7, 40] = v[..., 7, 41] = v[..., 7, 90]           # ties at a large magnitude
     L = IDENT if lut == "ident" else S.nuq3_lut()
-    c = _nuq_cache(B, H, n + 64, 0, bp, L, L)
+    c = _nuq_cache(B, H, n + 64, 0, bp, L, L, v_bp)
     _quantize(c, k, v, n)
     for b in range(B):
         for h in range(H):
-            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, n, 0, 0.0)
+            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, n, 0, 0.0, v_outlier_bp=v_bp)
             _check_head(c, b, h, ref, n, bp)
 
 
@@ -103,7 +113,7 @@ DECODE = [
 ]
 
 
-def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0):
+def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0):
     """Sink tokens [0, ns) in fp16, the next N quantized, the r after them in the window;
     the query sits at position ns + N + r."""
     seed = 300 + N + r + GQ + 7 * ns
@@ -112,7 +122,7 @@ def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0):
     cap = max(32, N)
     lk, lv = dev(L), dev(L)
     c = K.KVCache(B, Hkv, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
-                  outlier_bp=bp, sink_len=S_len)
+                  outlier_bp=bp, sink_len=S_len, v_outlier_bp=v_bp)
     c.c.vq.lut = lv.data_ptr()
     kd, vd = dev(k), dev(v)
     if N:
@@ -143,12 +153,14 @@ def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0):
     vh = np.zeros((B, Hkv, T, 128))
     for b in range(B):
         for h in range(Hkv):
-            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta, n_sink=ns)
+            ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta, n_sink=ns,
+                             v_outlier_bp=v_bp)
             kh[b, h], vh[b, h] = ref["k_hat"], ref["v_hat"]
     want = O.decode_attention_f64(O.f16_to_f32(q), kh, vh, sm)
     assert np.isfinite(got).all()
     assert_close(got, want,
-                 f"nuq decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} bp{bp} theta{theta}")
+                 f"nuq decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} bp{bp}/{v_bp} "
+                 f"theta{theta}")
 
 
 @pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,theta", DECODE)
@@ -165,3 +177,13 @@ def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
 def test_nuq_decode_with_sink_matches_oracle(B, Hkv, GQ, ns, S_len, N, r, R, bp, theta):
     """Sink keys sit at positions 0 .. ns-1 and shift the packed keys' positions by ns."""
     _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns, S_len)
+
+
+@pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,v_bp,theta", [
+    (1, 2, 1, 2048, 0, 0, 100, 100, 1e4),          # KVQuant's nuq3-1%: keys and values
+    (2, 2, 2, 1024, 37, 64, 100, 250, 1e4),
+    (1, 1, 8, 512, 3, 32, 0, 100, 500000.0),
+    (1, 3, 4, 256, 0, 0, 100, 10000, 0.0),         # every value exact
+])
+def test_nuq_decode_with_value_outliers_matches_oracle(B, Hkv, GQ, N, r, R, bp, v_bp, theta):
+    _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, v_bp=v_bp)

@@ -171,17 +171,19 @@ def test_gqa_long_context_streaming_1024_appends():
     assert np.array_equal(kw[0, 5, :N // 32], ref["k_codes"][0, 0])
 
 
-def test_kvquant_1m_context_full_size():
-    """1,048,576 tokens x 32 heads: nuq3 keys with 1 % outliers per channel and nuq3
-    values, RoPE theta 1e4 after dequantization.  Head 7 is checked end to end."""
-    w = S.WORKLOADS["kvquant_1m"]
+@pytest.mark.parametrize("name,h", [("kvquant_1m", 7), ("kvquant_256k_dense_sparse", 21)])
+def test_kvquant_context_full_size(name, h):
+    """kvquant_1m: 1,048,576 tokens x 32 heads, nuq3 keys with 1 % outliers per channel and
+    nuq3 values, RoPE theta 1e4 after dequantization.  kvquant_256k_dense_sparse: 262,144
+    tokens with 1 % outliers in every key channel and every value token.  One head is
+    checked end to end."""
+    w = S.WORKLOADS[name]
     N = w.n_packed
-    h = 7
     kd, vd = _device_kv(w, N)
     L = S.nuq3_lut()
     lut = dev(L)
     c = K.KVCache(1, w.kv_heads, N, k_bits=3, v_bits=3, residual_len=0, kind=K.KVQ_NUQ,
-                  lut=lut, outlier_bp=w.outlier_bp)
+                  lut=lut, outlier_bp=w.outlier_bp, v_outlier_bp=w.v_outlier_bp)
     wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     D = w.head_dim
@@ -195,7 +197,8 @@ def test_kvquant_1m_context_full_size():
     out = _decode(c, w, q)
     assert np.isfinite(out).all()
     k, v = _host_head(w, 0, h, N)
-    ref = O.nuq_head(k[0, 0], v[0, 0], L, L, w.outlier_bp, N, 0, w.rope_theta)
+    ref = O.nuq_head(k[0, 0], v[0, 0], L, L, w.outlier_bp, N, 0, w.rope_theta,
+                     v_outlier_bp=w.v_outlier_bp)
     kw = host_words(c.buf("k_codes")).reshape(w.kv_heads, N // 32, D, 3)
     assert np.array_equal(kw[h], ref["k_codes"])
     km = host_words(c.buf("k_meta")).reshape(w.kv_heads, D)
@@ -207,6 +210,9 @@ def test_kvquant_1m_context_full_size():
     assert int(rp[h, -1]) == D * O.outlier_count(N, w.outlier_bp)
     ent = host_words(c.buf("k_csr_ent")).reshape(w.kv_heads, -1)
     assert np.array_equal(ent[h, :rp[h, -1]], ref["ent"])
+    if w.v_outlier_bp:
+        vo = host_words(c.buf("v_out")).reshape(w.kv_heads, N, -1)
+        assert np.array_equal(vo[h], ref["v_ent"])
     want = O.decode_attention_f64(O.f16_to_f32(q[:, h:h + 1]), ref["k_hat"][None, None],
                                   ref["v_hat"][None, None], O.default_sm_scale(D))
-    assert_close(out[:, h:h + 1], want, "kvquant_1m head 7")
+    assert_close(out[:, h:h + 1], want, f"{name} head {h}")
