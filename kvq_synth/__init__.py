@@ -132,19 +132,27 @@ def gen_tensor(seed: int, tensor_id: int, batch: int, heads: int, tokens: int, h
     return x.astype(np.float16).view(np.uint16)
 
 
-def nuq3_lut() -> np.ndarray:
-    """fp16 bits [8]: an ascending non-uniform 3-bit code book in level units [0, 7].
+def nuq_lut(bits: int) -> np.ndarray:
+    """fp16 bits [2^bits]: an ascending non-uniform code book in level units [0, 2^bits - 1].
 
     The learned, sensitivity-weighted datatype of KVQuant is not printed on the
     pages, so a fixed normal-quantile code book stands in for it: level i sits
-    at the standard-normal quantile of (2i + 1) / 16, mapped affinely so that
-    level 0 is 0 and level 7 is 7.  It is an input of the method, not part of it.
+    at the standard-normal quantile of (2i + 1) / 2^(bits + 1), mapped affinely so that
+    the first level is 0 and the last 2^bits - 1.  It is an input of the method, not
+    part of it.
     """
     from statistics import NormalDist
     nd = NormalDist()
-    z = np.array([nd.inv_cdf((2 * i + 1) / 16.0) for i in range(8)], dtype=np.float64)
-    lv = 3.5 + 3.5 * z / z[-1]
+    n = 1 << bits
+    z = np.array([nd.inv_cdf((2 * i + 1) / (2.0 * n)) for i in range(n)], dtype=np.float64)
+    half = (n - 1) / 2.0
+    lv = half + half * z / z[-1]
     return np.sort(lv.astype(np.float16)).view(np.uint16)
+
+
+def nuq3_lut() -> np.ndarray:
+    """The 3-bit code book (nuq_lut(3))."""
+    return nuq_lut(3)
 
 
 @dataclasses.dataclass(frozen=True)

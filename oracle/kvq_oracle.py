@@ -234,32 +234,60 @@ def nuq3_bit_positions():
     return lo, hi
 
 
-def pack_nuq3(codes: np.ndarray) -> np.ndarray:
-    """3-bit codes [..., N, D] -> [..., N/32, D, 3 words] (per block, channel-major)."""
+def nuq_code_fields(bits: int):
+    """Where token j's code lives in a channel's ``bits`` words of a 32-token block: a list
+    per token of (word, bit position, field width, first code bit) pieces.
+
+    nuq2: words 0 and 1 as the low words of nuq3 (token j of its half at bit
+    8*(j % 4) + 2*(j // 4)).  nuq3: those two plus word 2 for the high bits.  nuq4: word i
+    holds tokens 8i..8i+7, token j of its octet at bit 8*(j % 4) + 4*(j // 4).  In every
+    width a shift and one mask bring four consecutive tokens' fields into the four bytes
+    of a word."""
+    fields = []
+    for j in range(GROUP):
+        if bits == 4:
+            jj = j % 8
+            fields.append([(j // 8, 8 * (jj % 4) + 4 * (jj // 4), 4, 0)])
+            continue
+        jj = j % 16
+        f = [(j // 16, 8 * (jj % 4) + 2 * (jj // 4), 2, 0)]
+        if bits == 3:
+            f.append((2, 8 * (j % 4) + j // 4, 1, 2))
+        fields.append(f)
+    return fields
+
+
+def pack_nuq(codes: np.ndarray, bits: int) -> np.ndarray:
+    """``bits``-bit codes [..., N, D] -> [..., N/32, D, bits words] (per block, channel-major)."""
     *lead, n, d = codes.shape
     blk = np.swapaxes(codes.reshape(*lead, n // GROUP, GROUP, d), -1, -2).astype(np.uint64)
-    lo, hi = nuq3_bit_positions()
-    words = np.zeros((*blk.shape[:-1], 3), dtype=np.uint64)
-    for j in range(GROUP):
-        w, b = lo[j]
-        words[..., w] |= (blk[..., j] & np.uint64(3)) << np.uint64(b)
-        w, b = hi[j]
-        words[..., w] |= (blk[..., j] >> np.uint64(2)) << np.uint64(b)
+    words = np.zeros((*blk.shape[:-1], bits), dtype=np.uint64)
+    for j, pieces in enumerate(nuq_code_fields(bits)):
+        for w, pos, width, first in pieces:
+            part = (blk[..., j] >> np.uint64(first)) & np.uint64((1 << width) - 1)
+            words[..., w] |= part << np.uint64(pos)
     return words.astype(np.uint32)
 
 
-def unpack_nuq3(words: np.ndarray) -> np.ndarray:
+def unpack_nuq(words: np.ndarray, bits: int) -> np.ndarray:
     *lead, nb, d, _ = words.shape
-    lo, hi = nuq3_bit_positions()
     w64 = words.astype(np.uint64)
     out = np.zeros((*lead, nb, d, GROUP), dtype=np.uint8)
-    for j in range(GROUP):
-        wl, bl = lo[j]
-        wh, bh = hi[j]
-        c = ((w64[..., wl] >> np.uint64(bl)) & np.uint64(3)) | \
-            (((w64[..., wh] >> np.uint64(bh)) & np.uint64(1)) << np.uint64(2))
+    for j, pieces in enumerate(nuq_code_fields(bits)):
+        c = np.zeros(w64.shape[:-1], dtype=np.uint64)
+        for w, pos, width, first in pieces:
+            c |= ((w64[..., w] >> np.uint64(pos)) & np.uint64((1 << width) - 1)) << np.uint64(first)
         out[..., j] = c.astype(np.uint8)
     return np.swapaxes(out, -1, -2).reshape(*lead, nb * GROUP, d)
+
+
+def pack_nuq3(codes: np.ndarray) -> np.ndarray:
+    """3-bit codes [..., N, D] -> [..., N/32, D, 3 words] (per block, channel-major)."""
+    return pack_nuq(codes, 3)
+
+
+def unpack_nuq3(words: np.ndarray) -> np.ndarray:
+    return unpack_nuq(words, 3)
 
 
 # --------------------------------------------------------------------------
@@ -571,6 +599,7 @@ def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: n
     Returns the packed buffers and the float64 keys (RoPE applied at positions 0.. in that
     order when theta > 0) and values attention reads."""
     p0, p1 = n_sink, n_sink + n_packed
+    bk, bv = int(round(math.log2(len(lut_k)))), int(round(math.log2(len(lut_v))))
     kp, vp = k_bits[p0:p1], v_bits[p0:p1]
     kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp)
     if v_outlier_bp > 0:
@@ -587,9 +616,9 @@ def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: n
     if theta > 0:
         k_hat = rope_f64(k_hat, np.arange(p1 + n_resid), theta)
     return {
-        "k_codes": pack_nuq3(kc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
+        "k_codes": pack_nuq(kc[None], bk)[0] if n_packed else np.zeros((0, k_bits.shape[1], bk), np.uint32),
         "k_meta": pack_meta(ks, km),
-        "v_codes": pack_nuq3(vc[None])[0] if n_packed else np.zeros((0, k_bits.shape[1], 3), np.uint32),
+        "v_codes": pack_nuq(vc[None], bv)[0] if n_packed else np.zeros((0, k_bits.shape[1], bv), np.uint32),
         "v_meta": pack_meta(vs, vm),
         "rowptr": rp, "ent": ent, "v_ent": v_ent, "k_hat": k_hat, "v_hat": v_hat,
     }

@@ -192,3 +192,30 @@ def test_nuq_head_value_outliers_change_only_the_outlier_values():
     cols = (h["v_ent"] & 0xFFFF).astype(np.int64)
     rows = np.repeat(np.arange(64), cols.shape[1])
     assert np.array_equal(h["v_hat"][rows, cols.ravel()], O.f16_to_f32(x)[rows, cols.ravel()])
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_identity_lut_equals_uniform_at_other_widths(bits):
+    """nuq2 / nuq4 with the identity code book {0 .. 2^B - 1} are the uniform B-bit
+    quantizer, per vector and per token, bit for bit."""
+    ident = np.arange(1 << bits).astype(np.float16).view(np.uint16)
+    rng = np.random.default_rng(bits)
+    x = _f16(rng.standard_normal(256) * 7.0)
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, ident, 0)
+    cu, su, mu = O.uniform_quantize_groups(x[None], bits)
+    assert np.array_equal(c, cu[0]) and s == su[0] and m == mu[0]
+    v = S.gen_tensor(6, S.TID_V, 1, 1, 32, 128)[0, 0]
+    c, s, m, xh = O.nuq_quantize_values(v, ident)
+    cu, su, mu = O.uniform_quantize_groups(v, bits)
+    assert np.array_equal(c, cu) and np.array_equal(s, su) and np.array_equal(m, mu)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_code_books_of_other_widths(bits):
+    """The stand-in code books: 2^B ascending levels from 0 to 2^B - 1, symmetric about the
+    middle (normal quantiles)."""
+    lut = O.f16_to_f32(S.nuq_lut(bits))
+    n = 1 << bits
+    assert lut.shape == (n,) and lut[0] == 0 and lut[-1] == n - 1
+    assert np.all(np.diff(lut) > 0)
+    np.testing.assert_allclose(lut + lut[::-1], n - 1, atol=0.01)

@@ -151,3 +151,50 @@ def test_kvquant_table_byte_accounting():
                                  row["outlier_frac"]) / 2 ** 30
             tol = 0.1 if row["outlier_frac"] else 0.05 + 1e-9
             assert abs(b - printed) <= tol, (name, mname, b, printed)
+
+
+# ---- nuq2 / nuq4 code layouts (KVQuant review: the results table covers nuq2, nuq3 and
+# nuq4).  nuq2 is nuq3 without its high-bit word; nuq4 keeps one octet of tokens per word.
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nuq_pack_round_trip_and_size(bits):
+    rng = np.random.default_rng(10 + bits)
+    c = rng.integers(0, 1 << bits, (2, 1, 96, 128)).astype(np.uint8)
+    w = O.pack_nuq(c, bits)
+    assert w.shape == (2, 1, 3, 128, bits)
+    assert np.array_equal(O.unpack_nuq(w, bits), c)
+    assert w.nbytes == c.size * bits // 8
+
+
+def test_nuq2_layout_bit_positions_by_hand():
+    c = np.zeros((32, 128), np.uint8)
+    c[0, 6] = 3          # token 0: word 0 bits 0-1
+    c[6, 6] = 1          # token 6: byte 2, slot 1 -> bits 16 + 2 = 18..19 of word 0
+    c[17, 6] = 2         # token 17 (16 + 1): word 1, byte 1 -> bits 8..9
+    c[31, 7] = 3         # token 31 (16 + 15): word 1, byte 3, slot 3 -> bits 30..31
+    w = O.pack_nuq(c, 2)[0]
+    assert int(w[6, 0]) == 3 | (1 << 18) and int(w[6, 1]) == 2 << 8
+    assert int(w[7, 1]) == 3 << 30 and int(w[7, 0]) == 0
+
+
+def test_nuq4_layout_bit_positions_by_hand():
+    c = np.zeros((32, 128), np.uint8)
+    c[0, 2] = 0xF        # token 0: word 0 bits 0-3
+    c[5, 2] = 0xA        # token 5: byte 1, upper nibble -> bits 12..15 of word 0
+    c[8, 2] = 0x3        # token 8: word 1 bits 0-3
+    c[31, 2] = 0x9       # token 31 (octet 3, 7): byte 3, upper nibble -> bits 28..31 of word 3
+    w = O.pack_nuq(c, 4)[0]
+    assert int(w[2, 0]) == 0xF | (0xA << 12) and int(w[2, 1]) == 0x3
+    assert int(w[2, 3]) == 0x9 << 28 and int(w[2, 2]) == 0
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_nuq_one_mask_gives_four_tokens(bits):
+    rng = np.random.default_rng(20 + bits)
+    cc = rng.integers(0, 1 << bits, (32, 128)).astype(np.uint8)
+    ww = O.pack_nuq(cc, bits)[0]
+    for m in range(8):
+        if bits == 2:
+            codes = (int(ww[11, m // 4]) >> (2 * (m % 4))) & 0x03030303
+        else:
+            codes = (int(ww[11, m // 2]) >> (4 * (m % 2))) & 0x0F0F0F0F
+        assert [(codes >> (8 * k)) & 0xFF for k in range(4)] == list(cc[4 * m:4 * m + 4, 11])
