@@ -103,14 +103,14 @@ def decode_bytes(w, n_packed: int, n_resid: int) -> int:
 
 
 def nuq_decode_bytes(w, n_packed: int) -> int:
-    """Algorithmic bytes of one decode over a nuq3 cache: 3-bit codes of K and V, per-channel
+    """Algorithmic bytes of one decode over a nuq cache: B-bit codes of K and V, per-channel
     key metadata, per-token value metadata, the CSR of key outliers (row pointers and one
     4-byte entry per outlier), the value outliers (4 bytes each), q and out."""
     bh = w.batch * w.kv_heads
     D = w.head_dim
     k_out = (n_packed * w.outlier_bp + 9999) // 10000
     v_out = (D * w.v_outlier_bp + 9999) // 10000
-    codes = 2 * bh * n_packed * D * 3 // 8
+    codes = bh * n_packed * D * (w.k_bits + w.v_bits) // 8
     meta = bh * D * 4 + bh * n_packed * 4
     csr = (bh * (n_packed + 1) * 4 + bh * D * k_out * 4) if w.outlier_bp else 0
     return codes + meta + csr + bh * n_packed * v_out * 4 + w.batch * w.q_heads * D * (2 + 4)
@@ -122,7 +122,7 @@ def nuq_quantize_bytes(w, n_tokens: int) -> int:
     D = w.head_dim
     k_out = (n_tokens * w.outlier_bp + 9999) // 10000
     read = 2 * bh * n_tokens * D * 2
-    written = 2 * bh * n_tokens * D * 3 // 8 + bh * D * 4 + bh * n_tokens * 4
+    written = bh * n_tokens * D * (w.k_bits + w.v_bits) // 8 + bh * D * 4 + bh * n_tokens * 4
     if w.outlier_bp:
         written += bh * (n_tokens + 1) * 4 + bh * D * k_out * 4
     written += bh * n_tokens * ((D * w.v_outlier_bp + 9999) // 10000) * 4
@@ -213,8 +213,9 @@ def bench_nuq(w, args) -> dict:
     v_src = torch.empty_like(k_src)
     S.fill_device(k_src, w.seed, S.TID_K, B, Hkv, N, D, gains=gains)
     S.fill_device(v_src, w.seed, S.TID_V, B, Hkv, N, D)
-    lut = torch.from_numpy(S.nuq3_lut().view(np.int16)).to(dev)
-    c = K.KVCache(B, Hkv, N, k_bits=3, v_bits=3, residual_len=0, kind=K.KVQ_NUQ, lut=lut,
+    lut = torch.from_numpy(S.nuq_lut(w.k_bits).view(np.int16)).to(dev)
+    c = K.KVCache(B, Hkv, N, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=0, kind=K.KVQ_NUQ,
+                  lut=lut,
                   outlier_bp=w.outlier_bp, v_outlier_bp=w.v_outlier_bp)
     wsq = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
     ws_q = torch.empty(wsq, dtype=torch.uint8, device=dev)
@@ -282,8 +283,9 @@ def bench_nuq(w, args) -> dict:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {B}, {Hq} heads, head_dim {D}, {N} tokens, "
-                               f"nuq3 keys per channel pre-RoPE with {w.outlier_bp / 100:g}% "
-                               f"CSR outliers, nuq3 values per token"
+                               f"nuq{w.k_bits} keys per channel pre-RoPE with "
+                               f"{w.outlier_bp / 100:g}% CSR outliers, nuq{w.v_bits} values per "
+                               f"token"
                                + (f" with {w.v_outlier_bp / 100:g}% outliers"
                                   if w.v_outlier_bp else "")
                                + f", RoPE theta {w.rope_theta:g}"},

@@ -27,42 +27,80 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kWindowUnits = 4;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
+// Code book in registers: the low and the high bytes of the fp16 entries, four entries
+// per register (entries 4i..4i+3 in lo[i] / hi[i]).
+template <int B>
 struct Lut {
-  uint32_t lo_a, lo_b, hi_a, hi_b;   // low / high bytes of entries 0-3 and 4-7
+  uint32_t lo[B == 4 ? 4 : 2], hi[B == 4 ? 4 : 2];
 };
 
-__device__ __forceinline__ Lut load_lut(const uint16_t* lut) {
-  uint32_t e[8];
+template <int B>
+__device__ __forceinline__ Lut<B> load_lut(const uint16_t* lut) {
+  constexpr int NR = B == 4 ? 4 : 2;
+  Lut<B> r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = lut[i];
-  Lut r;
-  r.lo_a = (e[0] & 255) | (e[1] & 255) << 8 | (e[2] & 255) << 16 | (e[3] & 255) << 24;
-  r.lo_b = (e[4] & 255) | (e[5] & 255) << 8 | (e[6] & 255) << 16 | (e[7] & 255) << 24;
-  r.hi_a = (e[0] >> 8) | (e[1] >> 8) << 8 | (e[2] >> 8) << 16 | (e[3] >> 8) << 24;
-  r.hi_b = (e[4] >> 8) | (e[5] >> 8) << 8 | (e[6] >> 8) << 16 | (e[7] >> 8) << 24;
+  for (int i = 0; i < NR; ++i) {
+    r.lo[i] = r.hi[i] = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t e = 4 * i + k < (1 << B) ? lut[4 * i + k] : 0u;
+      r.lo[i] |= (e & 255u) << (8 * k);
+      r.hi[i] |= (e >> 8) << (8 * k);
+    }
+  }
   return r;
 }
 
-// Four codes (one per byte, 0..7) -> their fp16 entries as two packed pairs.
-__device__ __forceinline__ void lut4(const Lut& L, uint32_t codes, uint32_t& p01, uint32_t& p23) {
-  const uint32_t lo = __builtin_amdgcn_perm(L.lo_b, L.lo_a, codes);
-  const uint32_t hi = __builtin_amdgcn_perm(L.hi_b, L.hi_a, codes);
+// Four codes (one per byte) -> their fp16 entries as two packed pairs.  Eight entries
+// fit one v_perm_b32 source pair; with 16 (nuq4) both halves are looked up and the
+// code's high bit picks the byte.
+template <int B>
+__device__ __forceinline__ void lut4(const Lut<B>& L, uint32_t codes, uint32_t& p01,
+                                     uint32_t& p23) {
+  uint32_t lo, hi;
+  if constexpr (B == 4) {
+    const uint32_t c7 = codes & 0x07070707u;
+    const uint32_t t = (codes >> 3) & 0x01010101u;
+    const uint32_t sel = (t << 8) - t;            // 0xFF in the bytes of codes 8..15
+    const uint32_t lo0 = __builtin_amdgcn_perm(L.lo[1], L.lo[0], c7);
+    const uint32_t lo1 = __builtin_amdgcn_perm(L.lo[3], L.lo[2], c7);
+    const uint32_t hi0 = __builtin_amdgcn_perm(L.hi[1], L.hi[0], c7);
+    const uint32_t hi1 = __builtin_amdgcn_perm(L.hi[3], L.hi[2], c7);
+    lo = (lo1 & sel) | (lo0 & ~sel);
+    hi = (hi1 & sel) | (hi0 & ~sel);
+  } else {
+    lo = __builtin_amdgcn_perm(L.lo[1], L.lo[0], codes);
+    hi = __builtin_amdgcn_perm(L.hi[1], L.hi[0], codes);
+  }
   p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
   p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
-// Codes of tokens 4m..4m+3 of one channel's three nuq3 words, one per byte.
+// Codes of tokens 4m..4m+3 of one channel's B code words, one per byte.
+template <int B>
 __device__ __forceinline__ uint32_t codes4(const uint32_t* w, int m) {
-  const uint32_t lo = (w[m >> 2] >> (2 * (m & 3))) & 0x03030303u;
-  const uint32_t hi = (w[2] >> m) & 0x01010101u;
-  return lo | (hi << 2);
+  if constexpr (B == 4) {
+    return (w[m >> 1] >> (4 * (m & 1))) & 0x0F0F0F0Fu;
+  } else {
+    const uint32_t lo = (w[m >> 2] >> (2 * (m & 3))) & 0x03030303u;
+    if constexpr (B == 2) return lo;
+    const uint32_t hi = (w[2] >> m) & 0x01010101u;
+    return lo | (hi << 2);
+  }
 }
 
+template <int B>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
-  const int jj = j & 15;
-  const uint32_t lo = (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
-  const uint32_t hi = (w[2] >> (8 * (j & 3) + (j >> 2))) & 1u;
-  return lo | (hi << 2);
+  if constexpr (B == 4) {
+    const int jj = j & 7;
+    return (w[j >> 3] >> (8 * (jj & 3) + 4 * (jj >> 2))) & 15u;
+  } else {
+    const int jj = j & 15;
+    const uint32_t lo = (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
+    if constexpr (B == 2) return lo;
+    const uint32_t hi = (w[2] >> (8 * (j & 3) + (j >> 2))) & 1u;
+    return lo | (hi << 2);
+  }
 }
 
 __device__ __forceinline__ float lut_value(const uint16_t* lut, uint32_t c) {
@@ -181,15 +219,15 @@ template <int GQ>
 struct NuqShared {
   float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
-  float lutk[8], lutv[8];
+  float lutk[16], lutv[16];
 };
 
 // Per-wave scratch (LDS).
-template <int GQ>
+template <int GQ, int B>
 struct NuqWaveScratch {
   float ps[GQ][kGroup];      // p_t * scale_t of the block's tokens
   float2 qb[GQ][64];         // q e^(-i t0 theta_i) per head and pair: the block's first token
-  uint32_t kc[kHeadDim][3];  // the block's key code words, per channel
+  uint32_t kc[kHeadDim][B];  // the block's key (later value) code words, per channel
   float corr[GQ][64];        // per CSR entry of the window: its score correction
   uint8_t tok[64];           // per CSR entry of the window: its token in the block
   float pv[GQ][kGroup];      // p_t of the block's tokens (value outliers)
@@ -197,25 +235,37 @@ struct NuqWaveScratch {
   float vcorr[GQ][kHeadDim]; // value-outlier corrections of the block, per channel
 };
 
+template <int B>
 struct NuqBlockRegs {
-  uint32_t kw[6], vw[6];     // key / value code words of channels 2l, 2l+1
+  uint32_t kw[2 * B], vw[2 * B];   // key / value code words of channels 2l, 2l+1
   uint32_t vmeta;            // value scale / min of token lane >> 1
   int32_t r0, r1;            // CSR row of token lane >> 1
 };
 
-__device__ __forceinline__ void load_nuq_block(NuqBlockRegs& r, const DecodeArgs& a, int64_t bh,
-                                               int64_t blk, int lane) {
+// 2B consecutive code words of a lane's channel pair.
+template <int B>
+__device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
+  if constexpr (B == 3) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    const uint4 y = *reinterpret_cast<const uint4*>(p + 2);
+    dst[0] = x.x; dst[1] = x.y; dst[2] = y.x; dst[3] = y.y; dst[4] = y.z; dst[5] = y.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < B / 2; ++i) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + 4 * i);
+      dst[4 * i] = x.x; dst[4 * i + 1] = x.y; dst[4 * i + 2] = x.z; dst[4 * i + 3] = x.w;
+    }
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const DecodeArgs& a,
+                                               int64_t bh, int64_t blk, int lane) {
   const int t = lane >> 1;
   const int64_t gblk = bh * a.cap_blocks + blk;
   const int64_t t0 = blk * kGroup;
-  const uint32_t* kp = a.k_codes + (gblk * kHeadDim + 2 * lane) * 3;
-  const uint32_t* vp = a.v_codes + (gblk * kHeadDim + 2 * lane) * 3;
-  const uint2 k01 = *reinterpret_cast<const uint2*>(kp);
-  const uint4 k25 = *reinterpret_cast<const uint4*>(kp + 2);
-  const uint2 v01 = *reinterpret_cast<const uint2*>(vp);
-  const uint4 v25 = *reinterpret_cast<const uint4*>(vp + 2);
-  r.kw[0] = k01.x; r.kw[1] = k01.y; r.kw[2] = k25.x; r.kw[3] = k25.y; r.kw[4] = k25.z; r.kw[5] = k25.w;
-  r.vw[0] = v01.x; r.vw[1] = v01.y; r.vw[2] = v25.x; r.vw[3] = v25.y; r.vw[4] = v25.z; r.vw[5] = v25.w;
+  load_words<B>(r.kw, a.k_codes + (gblk * kHeadDim + 2 * lane) * B);
+  load_words<B>(r.vw, a.v_codes + (gblk * kHeadDim + 2 * lane) * B);
   r.vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
   r.r0 = r.r1 = 0;
   if (a.csr_rowptr) {
@@ -225,16 +275,16 @@ __device__ __forceinline__ void load_nuq_block(NuqBlockRegs& r, const DecodeArgs
   }
 }
 
-template <int GQ>
+template <int GQ, int B>
 __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
-                                  const NuqBlockRegs& r, const PairConsts& pc, const Lut& lk,
-                                  const Lut& lv, NuqState<GQ>& st, const NuqShared<GQ>& sh,
-                                  NuqWaveScratch<GQ>& ws, int lane) {
+                                  const NuqBlockRegs<B>& r, const PairConsts& pc,
+                                  const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
+                                  const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
   const uint32_t* kw0 = r.kw;
-  const uint32_t* kw1 = r.kw + 3;
+  const uint32_t* kw1 = r.kw + B;
   const uint32_t* vw0 = r.vw;
-  const uint32_t* vw1 = r.vw + 3;
+  const uint32_t* vw1 = r.vw + B;
 
   // The block's CSR entries [e_begin, e_end): the first 64 are loaded now, one per
   // lane, so that the dense work below covers the load.
@@ -255,8 +305,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
 #pragma unroll
   for (int m4 = 0; m4 < 8; ++m4) {
     uint32_t a01, a23, b01, b23;
-    lut4(lk, codes4(kw0, m4), a01, a23);
-    lut4(lk, codes4(kw1, m4), b01, b23);
+    lut4<B>(lk, codes4<B>(kw0, m4), a01, a23);
+    lut4<B>(lk, codes4<B>(kw1, m4), b01, b23);
     kd0[4 * m4 + 0] = fmaf(lo_f16(a01), pc.ks0, pc.km0);
     kd0[4 * m4 + 1] = fmaf(hi_f16(a01), pc.ks0, pc.km0);
     kd0[4 * m4 + 2] = fmaf(lo_f16(a23), pc.ks0, pc.km0);
@@ -291,8 +341,11 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   if (e_begin < e_end) {
 #pragma unroll
     for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
-    ws.kc[2 * lane][0] = kw0[0]; ws.kc[2 * lane][1] = kw0[1]; ws.kc[2 * lane][2] = kw0[2];
-    ws.kc[2 * lane + 1][0] = kw1[0]; ws.kc[2 * lane + 1][1] = kw1[1]; ws.kc[2 * lane + 1][2] = kw1[2];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      ws.kc[2 * lane][i] = kw0[i];
+      ws.kc[2 * lane + 1][i] = kw1[i];
+    }
     for (int64_t w0 = e_begin; w0 < e_end; w0 += 64) {
       const bool has = w0 + lane < e_end;
       uint32_t ent = ent_first;
@@ -306,7 +359,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
-        const float khat = fmaf(sh.lutk[code_at(ws.kc[col], te)], sh.ks[col], sh.km[col]);
+        const float khat = fmaf(sh.lutk[code_at<B>(ws.kc[col], te)], sh.ks[col], sh.km[col]);
         const float d = x - khat;
         const float2 e = sh.rot[te][pr];
         const bool odd = col & 1;
@@ -347,8 +400,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     for (int m4 = 0; m4 < 8; ++m4) {
       const float4 w4 = pp[m4];
       uint32_t a01, a23, b01, b23;
-      lut4(lv, codes4(vw0, m4), a01, a23);
-      lut4(lv, codes4(vw1, m4), b01, b23);
+      lut4<B>(lv, codes4<B>(vw0, m4), a01, a23);
+      lut4<B>(lv, codes4<B>(vw1, m4), b01, b23);
       o0 = fmaf(w4.x, lo_f16(a01), o0); o0 = fmaf(w4.y, hi_f16(a01), o0);
       o0 = fmaf(w4.z, lo_f16(a23), o0); o0 = fmaf(w4.w, hi_f16(a23), o0);
       o1 = fmaf(w4.x, lo_f16(b01), o1); o1 = fmaf(w4.y, hi_f16(b01), o1);
@@ -363,9 +416,11 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   // code-word scratch now holds the value code words); each lane then takes its two
   // channels' sums.
   if (v_ne > 0) {
-    ws.kc[2 * lane][0] = vw0[0]; ws.kc[2 * lane][1] = vw0[1]; ws.kc[2 * lane][2] = vw0[2];
-    ws.kc[2 * lane + 1][0] = vw1[0]; ws.kc[2 * lane + 1][1] = vw1[1];
-    ws.kc[2 * lane + 1][2] = vw1[2];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      ws.kc[2 * lane][i] = vw0[i];
+      ws.kc[2 * lane + 1][i] = vw1[i];
+    }
     if (!(lane & 1)) {
       ws.vmeta[t] = r.vmeta;
 #pragma unroll
@@ -380,7 +435,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
         const int d = (int)(ent & (kHeadDim - 1));
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
         const uint32_t vmw = ws.vmeta[te];
-        const float vhat = sh.lutv[code_at(ws.kc[d], te)] * lo_f16(vmw) + hi_f16(vmw);
+        const float vhat = sh.lutv[code_at<B>(ws.kc[d], te)] * lo_f16(vmw) + hi_f16(vmw);
 #pragma unroll
         for (int j = 0; j < GQ; ++j) atomicAdd(&ws.vcorr[j][d], ws.pv[j][te] * (x - vhat));
       }
@@ -450,11 +505,11 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
   }
 }
 
-template <int GQ, int NW>
+template <int GQ, int NW, int B>
 __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ NuqShared<GQ> sh;
-  __shared__ __align__(16) NuqWaveScratch<GQ> wsc[NW];
+  __shared__ __align__(16) NuqWaveScratch<GQ, B> wsc[NW];
   __shared__ float wm[NW][GQ], wl[NW][GQ];
   __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
 
@@ -485,14 +540,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   } else {
     pc.ks0 = pc.km0 = pc.ks1 = pc.km1 = 0.f;
   }
-  const Lut lk = load_lut(a.lut_k);
-  const Lut lv = load_lut(a.lut_v);
+  const Lut<B> lk = load_lut<B>(a.lut_k);
+  const Lut<B> lv = load_lut<B>(a.lut_v);
   for (int j = wave; j < kGroup; j += NW) sh.rot[j][lane] = rot_at(j, pc.theta);
   if (wave == 0) {
     sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
     sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
-    if (lane < 8) sh.lutk[lane] = lut_value(a.lut_k, lane);
-    if (lane < 8) sh.lutv[lane] = lut_value(a.lut_v, lane);
+    if (lane < (1 << B)) sh.lutk[lane] = lut_value(a.lut_k, lane);
+    if (lane < (1 << B)) sh.lutv[lane] = lut_value(a.lut_v, lane);
   }
   __syncthreads();
 
@@ -521,15 +576,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     // One block in flight ahead of the one being processed (clamped index, unrolled by
     // two so no register copy waits on the loads just issued).
     const int last = b1 - 1;
-    NuqBlockRegs r0, r1;
-    load_nuq_block(r0, a, bh, b0, lane);
+    NuqBlockRegs<B> r0, r1;
+    load_nuq_block<B>(r0, a, bh, b0, lane);
     for (int i = b0; i < b1; i += 2) {
-      load_nuq_block(r1, a, bh, min(i + 1, last), lane);
-      process_nuq_block<GQ>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave],
+      load_nuq_block<B>(r1, a, bh, min(i + 1, last), lane);
+      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave],
                             lane);
       if (i + 1 >= b1) break;
-      load_nuq_block(r0, a, bh, min(i + 2, last), lane);
-      process_nuq_block<GQ>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh,
+      load_nuq_block<B>(r0, a, bh, min(i + 2, last), lane);
+      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh,
                             wsc[wave], lane);
     }
   }
@@ -578,28 +633,32 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, hipStream_t s) {
+hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, int bits, hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
   const int nw = a.waves_per_group;
   dim3 grid((unsigned)wgs), block((unsigned)(nw * kWave));
-#define KVQ_DN(G_, NW_)                                                   \
-  if (gq == G_ && nw == NW_) {                                            \
-    decode_nuq_kernel<G_, NW_><<<grid, block, 0, s>>>(a);                 \
+#define KVQ_DN(G_, NW_, B_)                                               \
+  if (gq == G_ && nw == NW_ && bits == B_) {                              \
+    decode_nuq_kernel<G_, NW_, B_><<<grid, block, 0, s>>>(a);             \
     hipError_t e_ = hipGetLastError();                                    \
     if (e_ != hipSuccess || a.splits == 1) return e_;                     \
     return launch_merge_splits(a, s);                                     \
   }
-  KVQ_DN(1, 4) KVQ_DN(2, 4) KVQ_DN(4, 4) KVQ_DN(8, 4)
+#define KVQ_DNB(B_) KVQ_DN(1, 4, B_) KVQ_DN(2, 4, B_) KVQ_DN(4, 4, B_) KVQ_DN(8, 4, B_)
+  KVQ_DNB(2) KVQ_DNB(3) KVQ_DNB(4)
+#undef KVQ_DNB
 #undef KVQ_DN
   return hipErrorInvalidValue;
 }
 
-const void* decode_nuq_fn(int gq, int nw) {
-  if (nw != 4) return nullptr;
-  if (gq == 1) return reinterpret_cast<const void*>(&decode_nuq_kernel<1, 4>);
-  if (gq == 2) return reinterpret_cast<const void*>(&decode_nuq_kernel<2, 4>);
-  if (gq == 4) return reinterpret_cast<const void*>(&decode_nuq_kernel<4, 4>);
-  if (gq == 8) return reinterpret_cast<const void*>(&decode_nuq_kernel<8, 4>);
+const void* decode_nuq_fn(int gq, int nw, int bits) {
+#define KVQ_DF(G_, B_)                                                    \
+  if (nw == 4 && gq == G_ && bits == B_)                                  \
+    return reinterpret_cast<const void*>(&decode_nuq_kernel<G_, 4, B_>);
+#define KVQ_DFB(B_) KVQ_DF(1, B_) KVQ_DF(2, B_) KVQ_DF(4, B_) KVQ_DF(8, B_)
+  KVQ_DFB(2) KVQ_DFB(3) KVQ_DFB(4)
+#undef KVQ_DFB
+#undef KVQ_DF
   return nullptr;
 }
 

@@ -122,7 +122,8 @@ constexpr int kNuqChunk = 2048;                // tokens per chunk in the nuq ke
 struct NuqKeysArgs {
   const uint16_t* k;        // keys of token 0: element (b, h, t, d) at b*sb + h*sh + t*st + d
   int64_t sb, sh, st;
-  const uint16_t* lut;      // fp16[8]
+  const uint16_t* lut;      // fp16[2^bits]
+  int32_t bits;             // 2, 3 or 4
   int32_t kv_heads;
   int32_t bh_count;         // batch * kv_heads
   int64_t n_tokens;         // tokens quantized (multiple of 32)
@@ -149,6 +150,7 @@ struct NuqValuesArgs {
   const uint16_t* v;        // values of token tok0
   int64_t sb, sh, st;
   const uint16_t* lut;
+  int32_t bits;             // 2, 3 or 4
   int32_t kv_heads, bh_count;
   int32_t n_blocks;
   int64_t tok0;
@@ -170,10 +172,10 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, int k_bits, int v_bits, int gq
 hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s);
 hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s);
-hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, hipStream_t s);
+hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, int bits, hipStream_t s);
 // The kernel a launcher above would run (for occupancy queries); NULL if none.
 const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw);
 const void* decode_gqa_fn(int k_bits, int v_bits, int gq);
-const void* decode_nuq_fn(int gq, int nw);
+const void* decode_nuq_fn(int gq, int nw, int bits);
 
 }  // namespace kvq

@@ -1,11 +1,11 @@
-// Non-uniform 3-bit quantizers with per-vector dense-and-sparse outliers.
+// Non-uniform 2-, 3- and 4-bit quantizers with per-vector dense-and-sparse outliers.
 //
 // KVQuant review ("KVQuant: Towards 10 Million Context Length LLM Inference with KV
 // Cache Quantization"), abstract items (i)-(iv): keys are quantized per channel and
 // before RoPE, with a non-uniform datatype, and in each vector the largest-magnitude
 // entries are kept in full precision in a sparse matrix; values are quantized per
 // token.  Readings (shared with the oracle): (min, scale) over the dense entries
-// exactly as the uniform quantizer with B = 3; the normalized value (x - min) * inv
+// exactly as the uniform quantizer with B bits; the normalized value (x - min) * inv
 // goes to the nearest code-book level (ties to the even index); a key channel's
 // outliers are its ceil(n * bp / 1e4) largest fp16 magnitudes, ties to lower tokens.
 //
@@ -27,15 +27,21 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Midpoints between consecutive code-book levels (2^B - 1 of them, B <= 4).
 struct Mids {
-  float m[7];
+  float m[15];
+  int n;
 };
 
-__device__ __forceinline__ Mids load_mids(const uint16_t* lut) {
+__device__ __forceinline__ Mids load_mids(const uint16_t* lut, int bits) {
   Mids r;
+  r.n = (1 << bits) - 1;
 #pragma unroll
-  for (int i = 0; i < 7; ++i)
-    r.m[i] = (f16_bits_to_f32(lut[i]) + f16_bits_to_f32(lut[i + 1])) * 0.5f;
+  for (int i = 0; i < 15; ++i) {
+    r.m[i] = __builtin_inff();
+    if (i < r.n)                                       // reads lut[0 .. 2^bits - 1] only
+      r.m[i] = (f16_bits_to_f32(lut[i]) + f16_bits_to_f32(lut[i + 1])) * 0.5f;
+  }
   return r;
 }
 
@@ -43,20 +49,21 @@ __device__ __forceinline__ Mids load_mids(const uint16_t* lut) {
 __device__ __forceinline__ uint32_t nuq_code(float xn, const Mids& md) {
   uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < 7; ++i) c += xn > md.m[i] ? 1u : 0u;
+  for (int i = 0; i < 15; ++i) c += xn > md.m[i] ? 1u : 0u;      // unused midpoints: +inf
   float mid_c = md.m[0];
 #pragma unroll
-  for (int i = 1; i < 7; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
-  if (c < 7 && (c & 1u) && xn == mid_c) c += 1;
+  for (int i = 1; i < 15; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
+  if (c < (uint32_t)md.n && (c & 1u) && xn == mid_c) c += 1;
   return c;
 }
 
-__device__ __forceinline__ void params3(float mn, float mx, uint32_t* meta, float* mn_o,
-                                        float* inv_o) {
+// (scale, min) of a dense range for B-bit codes: scale = (max - min) / (2^B - 1).
+__device__ __forceinline__ void params_nuq(float mn, float mx, int bits, uint32_t* meta,
+                                           float* mn_o, float* inv_o) {
   mn = mn + 0.0f;
   mx = mx + 0.0f;
   const uint16_t min_h = f32_to_f16_bits(mn);
-  const uint16_t scale_h = f32_to_f16_bits((mx - mn) / 7.0f);
+  const uint16_t scale_h = f32_to_f16_bits((mx - mn) / (float)((1 << bits) - 1));
   const float s = f16_bits_to_f32(scale_h);
   *mn_o = mn;
   *inv_o = (s == 0.0f) ? 0.0f : 1.0f / s;
@@ -232,16 +239,24 @@ __global__ void nuq_finalize_kernel(NuqKeysArgs a) {
   if (!(dmin <= dmax)) { dmin = 0.0f; dmax = 0.0f; }     // no dense entry
   uint32_t meta;
   float mn, inv;
-  params3(dmin, dmax, &meta, &mn, &inv);
+  params_nuq(dmin, dmax, a.bits, &meta, &mn, &inv);
   a.k_meta[bh * kHeadDim + d] = meta;
   a.norm[i * 2] = mn;
   a.norm[i * 2 + 1] = inv;
 }
 
-// Pack one channel's 32 codes (LDS tile [token][channel] of bytes) into word w.
-__device__ __forceinline__ uint32_t pack_nuq3_word(const uint8_t (*ct)[kHeadDim], int d, int w) {
+// Pack one channel's 32 codes (LDS tile [token][channel] of bytes) into word w of the
+// channel's B words (B = 2: words 0/1 hold tokens 0..15 / 16..31 at 8*(j%4) + 2*(j/4);
+// B = 3: the same for the low two bits, word 2 the high bits at 8*(j%4) + j/4; B = 4:
+// word w holds tokens 8w..8w+7 at 8*(j%4) + 4*(j/4)).
+__device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim], int d, int w,
+                                                  int bits_per_code) {
   uint32_t bits = 0;
-  if (w < 2) {
+  if (bits_per_code == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bits |= (uint32_t)(ct[8 * w + j][d] & 15u) << (8 * (j & 3) + 4 * (j >> 2));
+  } else if (w < 2) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       bits |= (uint32_t)(ct[16 * w + j][d] & 3u) << (8 * (j & 3) + 2 * (j >> 2));
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
-  const Mids md = load_mids(a.lut);
+  const Mids md = load_mids(a.lut, a.bits);
   int T = 0x8000, need = 0;
   uint32_t rank = 0;
   float mn = 0.f, inv = 0.f;
@@ -295,8 +310,9 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
     }
     __syncthreads();
     const int64_t blk = bh * a.cap_blocks + tb / kGroup;
-    for (int wi = tid; wi < kHeadDim * 3; wi += kThreads)
-      a.k_codes[blk * (kHeadDim * 3) + wi] = pack_nuq3_word(ct, wi / 3, wi % 3);
+    for (int wi = tid; wi < kHeadDim * a.bits; wi += kThreads)
+      a.k_codes[blk * (kHeadDim * a.bits) + wi] =
+          pack_nuq_word(ct, wi / a.bits, wi % a.bits, a.bits);
     if (tid < kGroup * 4)
       a.outmask[(bh * a.cap_tokens + tb + (tid >> 2)) * 4 + (tid & 3)] = om[tid >> 2][tid & 3];
     __syncthreads();
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   const int64_t bh = job / a.n_blocks;
   const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
   const int tid = threadIdx.x;
-  const Mids md = load_mids(a.lut);
+  const Mids md = load_mids(a.lut, a.bits);
   {
     const int t = tid >> 3, c = (tid & 7) * 16;
     const uint4* p = reinterpret_cast<const uint4*>(a.v + b * a.sb + h * a.sh +
@@ -499,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
     if (part == 0) {
       uint32_t meta;
       float m0, inv;
-      params3(mn, mx, &meta, &m0, &inv);
+      params_nuq(mn, mx, a.bits, &meta, &m0, &inv);
       a.v_meta[bh * a.cap_tokens + a.tok0 + (int64_t)blk * kGroup + t] = meta;
       st[t] = make_float2(m0, inv);
     }
@@ -516,8 +532,8 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   }
   __syncthreads();
   const int64_t dst = bh * a.cap_blocks + a.tok0 / kGroup + blk;
-  for (int wi = tid; wi < kHeadDim * 3; wi += kThreads)
-    a.v_codes[dst * (kHeadDim * 3) + wi] = pack_nuq3_word(ct, wi / 3, wi % 3);
+  for (int wi = tid; wi < kHeadDim * a.bits; wi += kThreads)
+    a.v_codes[dst * (kHeadDim * a.bits) + wi] = pack_nuq_word(ct, wi / a.bits, wi % a.bits, a.bits);
 }
 
 inline unsigned grid1(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }

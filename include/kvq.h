@@ -31,12 +31,12 @@
  *    (s == 0 ? 0 : clamp(rint((x - mn) * inv), 0, 2^B - 1)), every operation an
  *    IEEE fp32 operation with round-to-nearest-even and no fused multiply-add.
  *    Dequantized value: code * s + min.
- *  - nuq (KVQ_NUQ): the same (mn, scale, inv) with B = 3 over the vector's
- *    dense entries; xn = (x - mn) * inv; the code is the index of the nearest
- *    level of the caller's 8-entry fp16 code book (levels in "level units",
- *    0..7, strictly ascending; ties go to the even index).  Dequantized value:
- *    lut[code] * s + mn.  The identity code book {0,...,7} reproduces the
- *    uniform 3-bit quantizer exactly.
+ *  - nuq (KVQ_NUQ, B = 2, 3 or 4): the same (mn, scale, inv) over the
+ *    vector's dense entries; xn = (x - mn) * inv; the code is the index of the
+ *    nearest level of the caller's 2^B-entry fp16 code book (levels in "level
+ *    units", 0..2^B - 1, strictly ascending; ties go to the even index).
+ *    Dequantized value: lut[code] * s + mn.  The identity code book
+ *    {0, ..., 2^B - 1} reproduces the uniform B-bit quantizer exactly.
  *  - Outliers (nuq keys, outlier_bp > 0): per (batch, head, channel) the
  *    ceil(n * outlier_bp / 10000) entries of largest fp16 magnitude over the
  *    n quantized tokens (ties: lower token first) are kept exactly in a CSR
@@ -72,11 +72,13 @@
  *      octet, then 4..7); the even token fills bits 0..15 and the odd token bits
  *      16..31, the channels Bv bits apart from bit 0 of each half.
  *    v_meta  [batch][kv_heads][nb*32 tokens][D/32] words.
- *  NUQ codes (3 bits), keys and values alike:
- *    [batch][kv_heads][nb][D][3 words]: per block and channel, word 0 holds the
- *      low two bits of tokens 0..15 and word 1 those of tokens 16..31 (token j
- *      of its half at bit 8*(j%4) + 2*(j/4)); word 2 holds the high bits of all
- *      32 tokens (token j at bit 8*(j%4) + j/4).
+ *  NUQ codes (B = 2, 3 or 4 bits), keys and values alike:
+ *    [batch][kv_heads][nb][D][B words] per block and channel.  B = 3: word 0
+ *      holds the low two bits of tokens 0..15 and word 1 those of tokens 16..31
+ *      (token j of its half at bit 8*(j%4) + 2*(j/4)); word 2 holds the high bits
+ *      of all 32 tokens (token j at bit 8*(j%4) + j/4).  B = 2: words 0 and 1 as
+ *      for B = 3.  B = 4: word i holds tokens 8i..8i+7, token j of its octet at
+ *      bit 8*(j%4) + 4*(j/4).
  *  NUQ keys (per channel over all quantized tokens):
  *    k_meta  [batch][kv_heads][D] words (one scale/min per channel).
  *    k_csr_rowptr [batch][kv_heads][capacity_tokens + 1] int32, rows = tokens,
@@ -139,11 +141,12 @@ enum { KVQ_OP_QUANTIZE_KEYS = 0, KVQ_OP_DECODE_ATTN = 1 };
 /* Quantization settings of one tensor (K or V). */
 typedef struct {
   int32_t kind;        /* KVQ_UNIFORM or KVQ_NUQ (K and V must agree) */
-  int32_t bits;        /* UNIFORM: 2 or 4; NUQ: 3 */
+  int32_t bits;        /* UNIFORM: 2 or 4; NUQ: 2, 3 or 4 (K and V alike) */
   int32_t axis;        /* K: KVQ_AXIS_CHANNEL, V: KVQ_AXIS_TOKEN; the swapped
                           axes are valid for the method but KVQ_ERR_UNSUPPORTED */
   int32_t group_size;  /* UNIFORM: 32; NUQ: 0 (the whole vector) */
-  const uint16_t* lut; /* NUQ: device fp16[8], ascending, level units; else NULL */
+  const uint16_t* lut; /* NUQ: device fp16[2^bits], ascending, level units
+                          [0, 2^bits - 1]; else NULL */
   int32_t outlier_bp;  /* NUQ: outliers per vector in basis points (100 = 1 %),
                           0..10000 - keys: of each channel's quantized tokens,
                           values: of each token's D channels; UNIFORM: 0 */

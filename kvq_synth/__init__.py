@@ -203,6 +203,12 @@ WORKLOADS = {
     "kvquant_1m": Workload("kvquant_1m", 1, 32, 32, 128, 1048576, 0, 3, 3, "nuq",
                            SEED_BASE + 5, 3, 100.0, residual_len=0, outlier_bp=100,
                            rope_theta=1.0e4),
+    "kvquant_256k_nuq2": Workload("kvquant_256k_nuq2", 1, 32, 32, 128, 262144, 0, 2, 2, "nuq",
+                                  SEED_BASE + 8, 3, 100.0, residual_len=0, outlier_bp=100,
+                                  rope_theta=1.0e4),
+    "kvquant_256k_nuq4": Workload("kvquant_256k_nuq4", 1, 32, 32, 128, 262144, 0, 4, 4, "nuq",
+                                  SEED_BASE + 9, 3, 100.0, residual_len=0, outlier_bp=100,
+                                  rope_theta=1.0e4),
     "kvquant_256k_dense_sparse": Workload("kvquant_256k_dense_sparse", 1, 32, 32, 128, 262144, 0,
                                           3, 3, "nuq", SEED_BASE + 7, 3, 100.0, residual_len=0,
                                           outlier_bp=100, rope_theta=1.0e4, v_outlier_bp=100),

@@ -106,6 +106,14 @@ def test_layout_bytes_nuq_and_csr_capacity():
     (lambda c: setattr(c, "batch", 0), K.KVQ_ERR_INVALID_ARG),
     (lambda c: setattr(c.vq, "kind", K.KVQ_NUQ), K.KVQ_ERR_UNSUPPORTED),
     (lambda c: setattr(c, "sink_len", -1), K.KVQ_ERR_INVALID_ARG),
+    (lambda c: (setattr(c.kq, "kind", K.KVQ_NUQ), setattr(c.vq, "kind", K.KVQ_NUQ),
+                setattr(c.kq, "group_size", 0), setattr(c.vq, "group_size", 0),
+                setattr(c.kq, "lut", 0x1000), setattr(c.vq, "lut", 0x1000),
+                setattr(c.kq, "bits", 5), setattr(c.vq, "bits", 5)), K.KVQ_ERR_UNSUPPORTED),
+    (lambda c: (setattr(c.kq, "kind", K.KVQ_NUQ), setattr(c.vq, "kind", K.KVQ_NUQ),
+                setattr(c.kq, "group_size", 0), setattr(c.vq, "group_size", 0),
+                setattr(c.kq, "lut", 0x1000), setattr(c.vq, "lut", 0x1000),
+                setattr(c.kq, "bits", 4), setattr(c.vq, "bits", 2)), K.KVQ_ERR_UNSUPPORTED),
     (lambda c: setattr(c, "sink_len", 1025), K.KVQ_ERR_INVALID_ARG),
 ])
 def test_descriptor_errors(mutate, status):
@@ -232,3 +240,12 @@ def test_sink_errors_leave_state_unchanged():
         K.kvq_decode_attn(c, FAKE, 3, 0.1, 0.0, FAKE, FAKE, 1 << 20, stream=0)
     assert e.value.status == K.KVQ_ERR_INVALID_ARG
     assert "sink" in K.kvq_last_error()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_layout_bytes_nuq_widths_and_value_outliers(bits):
+    c = _desc(kind=K.KVQ_NUQ, kb=bits, vb=bits, B=1, H=2, cap=1024, R=0)
+    c.vq.outlier_bp = 100
+    s = K.kvq_layout_bytes(c)
+    assert s[K.KVQ_BUF_K_CODES] == s[K.KVQ_BUF_V_CODES] == 2 * 1024 * 128 * bits // 8
+    assert s[K.KVQ_BUF_V_OUT] == 2 * 1024 * 2 * 4          # 2 outliers per 128-channel token

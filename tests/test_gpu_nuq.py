@@ -25,7 +25,8 @@ def _kv(seed, B, H, T, D=128, n_out=3, gain=100.0):
 
 def _nuq_cache(B, H, cap, R, bp, lut_k, lut_v, v_bp=0):
     lk, lv = dev(lut_k), dev(lut_v)
-    c = K.KVCache(B, H, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
+    bits = int(np.log2(len(lut_k)))
+    c = K.KVCache(B, H, cap, k_bits=bits, v_bits=bits, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
                   outlier_bp=bp, v_outlier_bp=v_bp)
     c.c.vq.lut = lv.data_ptr()
     c.luts = (lk, lv)
@@ -46,8 +47,9 @@ def _quantize(c, k, v, n):
 def _check_head(c, b, h, ref, n, bp):
     B, H = c.c.batch, c.c.kv_heads
     cap = c.c.capacity_tokens
-    kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 128, 3)
-    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, 128, 3)
+    nb = c.c.kq.bits
+    kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 128, nb)
+    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, 128, nb)
     km = host_words(c.buf("k_meta")).reshape(B, H, 128)
     vm = host_words(c.buf("v_meta")).reshape(B, H, cap)
     assert np.array_equal(kw[b, h, :n // 32], ref["k_codes"]), "key codes"
@@ -71,13 +73,18 @@ def _check_head(c, b, h, ref, n, bp):
     (1, 2, 2048 + 256, 250, "nf", 0), (1, 1, 64, 10000, "nf", 0), (2, 1, 320, 5000, "ident", 0),
     # dense-and-sparse values: 2, 4, 13 and all 128 channels of each token kept exactly
     (2, 2, 96, 100, "nf", 100), (1, 1, 128, 0, "nf", 250), (1, 2, 64, 100, "ident", 1000),
-    (1, 1, 32, 0, "nf", 10000)])
+    (1, 1, 32, 0, "nf", 10000),
+    # nuq2 and nuq4
+    (2, 2, 96, 100, "nf2", 100), (1, 3, 4160, 100, "nf2", 0), (1, 1, 64, 0, "ident2", 0),
+    (2, 2, 96, 100, "nf4", 100), (1, 3, 4160, 250, "nf4", 0), (1, 1, 64, 0, "ident4", 250)])
 def test_nuq_quantize_bit_exact(B, H, n, bp, lut, v_bp):
     k, v = _kv(200 + n + bp + v_bp, B, H, n)
     if v_bp:
         v = v.copy()
         v[..., 7, 40] = v[..., 7, 41] = v[..., 7, 90]           # ties at a large magnitude
-    L = IDENT if lut == "ident" else S.nuq3_lut()
+    width = int(lut[-1]) if lut[-1].isdigit() else 3
+    ident = np.arange(1 << width).astype(np.float16).view(np.uint16)
+    L = ident if lut.startswith("ident") else S.nuq_lut(width)
     c = _nuq_cache(B, H, n + 64, 0, bp, L, L, v_bp)
     _quantize(c, k, v, n)
     for b in range(B):
@@ -113,16 +120,16 @@ DECODE = [
 ]
 
 
-def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0):
+def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0, bits=3):
     """Sink tokens [0, ns) in fp16, the next N quantized, the r after them in the window;
     the query sits at position ns + N + r."""
     seed = 300 + N + r + GQ + 7 * ns
     k, v = _kv(seed, B, Hkv, ns + N + r)
-    L = S.nuq3_lut()
+    L = S.nuq_lut(bits)
     cap = max(32, N)
     lk, lv = dev(L), dev(L)
-    c = K.KVCache(B, Hkv, cap, k_bits=3, v_bits=3, residual_len=R, kind=K.KVQ_NUQ, lut=lk,
-                  outlier_bp=bp, sink_len=S_len, v_outlier_bp=v_bp)
+    c = K.KVCache(B, Hkv, cap, k_bits=bits, v_bits=bits, residual_len=R, kind=K.KVQ_NUQ,
+                  lut=lk, outlier_bp=bp, sink_len=S_len, v_outlier_bp=v_bp)
     c.c.vq.lut = lv.data_ptr()
     kd, vd = dev(k), dev(v)
     if N:
@@ -159,7 +166,7 @@ def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0):
     want = O.decode_attention_f64(O.f16_to_f32(q), kh, vh, sm)
     assert np.isfinite(got).all()
     assert_close(got, want,
-                 f"nuq decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} bp{bp}/{v_bp} "
+                 f"nuq{bits} decode B{B} Hkv{Hkv} GQ{GQ} sink{ns} N{N} r{r} bp{bp}/{v_bp} "
                  f"theta{theta}")
 
 
@@ -187,3 +194,17 @@ def test_nuq_decode_with_sink_matches_oracle(B, Hkv, GQ, ns, S_len, N, r, R, bp,
 ])
 def test_nuq_decode_with_value_outliers_matches_oracle(B, Hkv, GQ, N, r, R, bp, v_bp, theta):
     _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, v_bp=v_bp)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("B,Hkv,GQ,N,r,R,bp,v_bp,theta,ns", [
+    (1, 2, 1, 2048, 0, 0, 100, 0, 1e4, 0),
+    (2, 2, 2, 1024, 37, 64, 100, 100, 1e4, 0),
+    (1, 1, 8, 512, 3, 32, 0, 250, 500000.0, 0),
+    (1, 2, 4, 4096, 0, 0, 250, 0, 1e4, 16),
+    (1, 3, 1, 96, 5, 32, 100, 100, 0.0, 0),
+])
+def test_nuq_other_widths_decode_matches_oracle(bits, B, Hkv, GQ, N, r, R, bp, v_bp, theta, ns):
+    """nuq2 and nuq4 (the KVQuant table's other widths): code books of 4 and 16 levels."""
+    _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=ns, S_len=max(ns, 0), v_bp=v_bp,
+                     bits=bits)

@@ -171,19 +171,21 @@ def test_gqa_long_context_streaming_1024_appends():
     assert np.array_equal(kw[0, 5, :N // 32], ref["k_codes"][0, 0])
 
 
-@pytest.mark.parametrize("name,h", [("kvquant_1m", 7), ("kvquant_256k_dense_sparse", 21)])
+@pytest.mark.parametrize("name,h", [("kvquant_1m", 7), ("kvquant_256k_dense_sparse", 21),
+                                    ("kvquant_256k_nuq2", 3), ("kvquant_256k_nuq4", 30)])
 def test_kvquant_context_full_size(name, h):
     """kvquant_1m: 1,048,576 tokens x 32 heads, nuq3 keys with 1 % outliers per channel and
     nuq3 values, RoPE theta 1e4 after dequantization.  kvquant_256k_dense_sparse: 262,144
-    tokens with 1 % outliers in every key channel and every value token.  One head is
-    checked end to end."""
+    tokens with 1 % outliers in every key channel and every value token.
+    kvquant_256k_nuq2 / _nuq4: the 2- and 4-bit widths.  One head is checked end to end."""
     w = S.WORKLOADS[name]
     N = w.n_packed
     kd, vd = _device_kv(w, N)
-    L = S.nuq3_lut()
+    L = S.nuq_lut(w.k_bits)
     lut = dev(L)
-    c = K.KVCache(1, w.kv_heads, N, k_bits=3, v_bits=3, residual_len=0, kind=K.KVQ_NUQ,
-                  lut=lut, outlier_bp=w.outlier_bp, v_outlier_bp=w.v_outlier_bp)
+    c = K.KVCache(1, w.kv_heads, N, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=0,
+                  kind=K.KVQ_NUQ, lut=lut, outlier_bp=w.outlier_bp,
+                  v_outlier_bp=w.v_outlier_bp)
     wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     D = w.head_dim
@@ -199,7 +201,7 @@ def test_kvquant_context_full_size(name, h):
     k, v = _host_head(w, 0, h, N)
     ref = O.nuq_head(k[0, 0], v[0, 0], L, L, w.outlier_bp, N, 0, w.rope_theta,
                      v_outlier_bp=w.v_outlier_bp)
-    kw = host_words(c.buf("k_codes")).reshape(w.kv_heads, N // 32, D, 3)
+    kw = host_words(c.buf("k_codes")).reshape(w.kv_heads, N // 32, D, w.k_bits)
     assert np.array_equal(kw[h], ref["k_codes"])
     km = host_words(c.buf("k_meta")).reshape(w.kv_heads, D)
     assert np.array_equal(km[h], ref["k_meta"])
