@@ -410,8 +410,46 @@ def nuq_code(xn: np.ndarray, lut_f32: np.ndarray) -> np.ndarray:
     return (c + tie).astype(np.uint8)
 
 
-def nuq_quantize_vector(x_bits: np.ndarray, lut_bits: np.ndarray, n_outliers: int = 0):
-    """One vector (fp16 bits, 1-D).  Returns (codes, scale_h, min_h, outlier_idx, x_hat)."""
+def qnorm_params(x_dense: np.ndarray, codes_dense: np.ndarray, lut: np.ndarray,
+                 scale_h, min_h):
+    """Q-Norm ([KVQ] "Proposed method" and findings: the dequantized distribution is made to
+    match the statistics taken before quantization).  Reading: per vector, over its dense
+    entries, the affine map x_hat -> a * x_hat + b that gives the dequantized values the
+    mean and standard deviation of the original ones; it folds into the metadata as
+    scale' = a * scale, min' = a * min + b (codes unchanged).
+
+    Moments in float64: the original's from the values (E[x], E[x^2] - E[x]^2), the
+    dequantized ones from the code histogram (level by level, ascending), each level's
+    value lut[c] * scale + min in float32.  a = sqrt(var / var_hat) (1 when var_hat is 0),
+    b = mean - a * mean_hat; the new metadata are a * scale and a * min + b rounded to
+    float32, then to fp16.  Returns (scale_h', min_h')."""
+    n = x_dense.shape[0]
+    if n == 0:
+        return scale_h, min_h
+    x = np.asarray(x_dense, dtype=np.float64)
+    mean = x.sum() / n
+    var = max((x * x).sum() / n - mean * mean, 0.0)
+    s, m = f16_to_f32(scale_h), f16_to_f32(min_h)
+    levels = (lut * s + m).astype(np.float32).astype(np.float64)
+    cnt = np.bincount(np.asarray(codes_dense, dtype=np.int64), minlength=len(lut))
+    m1 = 0.0
+    m2 = 0.0
+    for c in range(len(lut)):
+        m1 += float(cnt[c]) * levels[c]
+        m2 += float(cnt[c]) * levels[c] * levels[c]
+    mean_hat = m1 / n
+    var_hat = max(m2 / n - mean_hat * mean_hat, 0.0)
+    a = math.sqrt(var / var_hat) if var_hat > 0.0 else 1.0
+    b = mean - a * mean_hat
+    new_s = f32_to_f16_bits(np.float32(a * float(s)))
+    new_m = f32_to_f16_bits(np.float32(a * float(m) + b))
+    return new_s, new_m
+
+
+def nuq_quantize_vector(x_bits: np.ndarray, lut_bits: np.ndarray, n_outliers: int = 0,
+                        qnorm: bool = False):
+    """One vector (fp16 bits, 1-D).  Returns (codes, scale_h, min_h, outlier_idx, x_hat).
+    With qnorm the returned metadata (and x_hat) are the Q-Norm-corrected ones."""
     lut = f16_to_f32(lut_bits)
     bits = int(round(math.log2(len(lut))))
     x = f16_to_f32(x_bits)
@@ -432,12 +470,16 @@ def nuq_quantize_vector(x_bits: np.ndarray, lut_bits: np.ndarray, n_outliers: in
         inv = np.float32(1.0) / s
         xn = (x - mn) * inv
         codes = nuq_code(xn, lut)
+    if qnorm:
+        scale_h, min_h = qnorm_params(x[dense], codes[dense], lut, scale_h, min_h)
+        s, mn = f16_to_f32(scale_h), f16_to_f32(min_h)
     xhat = lut[codes] * s + mn
     xhat[out_idx] = x[out_idx]
     return codes, scale_h, min_h, out_idx, xhat
 
 
-def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int):
+def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int,
+                      qnorm: bool = False):
     """Keys of one head [N][D]: per channel over the whole context, with outliers.
 
     Returns codes [N][D], scale/min [D], CSR (row_ptr int32 [N+1], entries uint32: column in
@@ -451,7 +493,7 @@ def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int)
     xhat = np.zeros((n, d), np.float32)
     is_out = np.zeros((n, d), bool)
     for ch in range(d):
-        c, s, m, oi, xh = nuq_quantize_vector(k_bits[:, ch], lut_bits, k)
+        c, s, m, oi, xh = nuq_quantize_vector(k_bits[:, ch], lut_bits, k, qnorm)
         codes[:, ch], scale[ch], mins[ch], xhat[:, ch] = c, s, m, xh
         is_out[oi, ch] = True
     counts = is_out.sum(axis=1)
@@ -462,7 +504,8 @@ def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int)
     return codes, scale, mins, row_ptr, ent.astype(np.uint32), xhat
 
 
-def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int = 0):
+def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int = 0,
+                        qnorm: bool = False):
     """Values of one head [N][D]: per token over all D channels.
 
     Without outliers returns codes [N][D], scale/min [N], x_hat float32 [N][D].  With
@@ -471,7 +514,7 @@ def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: in
     largest magnitudes are kept exactly, and a fifth array [N][k] of entries (channel in
     bits 0..15, fp16 value in bits 16..31, channels ascending) is returned after scale/min."""
     n, d = v_bits.shape
-    if outlier_bp > 0:
+    if outlier_bp > 0 or qnorm:
         k = outlier_count(d, outlier_bp)
         codes = np.zeros((n, d), np.uint8)
         scale = np.zeros(n, np.uint16)
@@ -479,9 +522,11 @@ def nuq_quantize_values(v_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: in
         ent = np.zeros((n, k), np.uint32)
         xhat = np.zeros((n, d), np.float32)
         for t in range(n):
-            c, sc, mn, oi, xh = nuq_quantize_vector(v_bits[t], lut_bits, k)
+            c, sc, mn, oi, xh = nuq_quantize_vector(v_bits[t], lut_bits, k, qnorm)
             codes[t], scale[t], mins[t], xhat[t] = c, sc, mn, xh
             ent[t] = oi.astype(np.uint32) | (v_bits[t, oi].astype(np.uint32) << np.uint32(16))
+        if outlier_bp == 0:
+            return codes, scale, mins, xhat
         return codes, scale, mins, ent, xhat
     codes = np.zeros((n, d), np.uint8)
     scale = np.zeros(n, np.uint16)
@@ -592,7 +637,7 @@ def rope_query_f16(q_bits: np.ndarray, position: int, theta: float) -> np.ndarra
 
 def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: np.ndarray,
              outlier_bp: int, n_packed: int, n_resid: int, theta: float, n_sink: int = 0,
-             v_outlier_bp: int = 0):
+             v_outlier_bp: int = 0, qnorm: bool = False):
     """One (batch, head) of a KVQuant-style cache: tokens [0, n_sink) kept in fp16 (the
     sink), tokens [n_sink, n_sink + n_packed) quantized (keys per channel with outliers over
     the quantized tokens only, values per token), the next n_resid tokens kept in fp16.
@@ -601,11 +646,11 @@ def nuq_head(k_bits: np.ndarray, v_bits: np.ndarray, lut_k: np.ndarray, lut_v: n
     p0, p1 = n_sink, n_sink + n_packed
     bk, bv = int(round(math.log2(len(lut_k)))), int(round(math.log2(len(lut_v))))
     kp, vp = k_bits[p0:p1], v_bits[p0:p1]
-    kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp)
+    kc, ks, km, rp, ent, kx = nuq_quantize_keys(kp, lut_k, outlier_bp, qnorm)
     if v_outlier_bp > 0:
-        vc, vs, vm, v_ent, vx = nuq_quantize_values(vp, lut_v, v_outlier_bp)
+        vc, vs, vm, v_ent, vx = nuq_quantize_values(vp, lut_v, v_outlier_bp, qnorm)
     else:
-        vc, vs, vm, vx = nuq_quantize_values(vp, lut_v)
+        vc, vs, vm, vx = nuq_quantize_values(vp, lut_v, 0, qnorm)
         v_ent = np.zeros((n_packed, 0), np.uint32)
     kw = k_bits[p1:p1 + n_resid]
     vw = v_bits[p1:p1 + n_resid]

@@ -219,3 +219,57 @@ def test_code_books_of_other_widths(bits):
     assert lut.shape == (n,) and lut[0] == 0 and lut[-1] == n - 1
     assert np.all(np.diff(lut) > 0)
     np.testing.assert_allclose(lut + lut[::-1], n - 1, atol=0.01)
+
+
+# ---- Q-Norm (KVQuant review, "Proposed method" and findings: the dequantized distribution
+# is matched to the statistics before quantization; it helps most at 2 bits).
+@pytest.mark.parametrize("bits,bp", [(2, 0), (2, 100), (3, 100), (4, 0)])
+def test_qnorm_matches_mean_and_std(bits, bp):
+    rng = np.random.default_rng(30 + bits)
+    x = _f16(rng.standard_normal(4096) * 3.0 + 1.5)
+    lut = S.nuq_lut(bits)
+    k = O.outlier_count(4096, bp)
+    c0, s0, m0, oi0, xh0 = O.nuq_quantize_vector(x, lut, k)
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, lut, k, qnorm=True)
+    assert np.array_equal(c, c0) and np.array_equal(oi, oi0)     # codes and outliers unchanged
+    dense = np.ones(4096, bool)
+    dense[oi] = False
+    xf = O.f16_to_f32(x)[dense].astype(np.float64)
+    got = xh[dense].astype(np.float64)
+    # the fp16 metadata round a and b: the moments match to within that rounding
+    assert abs(got.mean() - xf.mean()) <= 2e-3 * xf.std()
+    assert abs(got.std() / xf.std() - 1.0) <= 2e-3
+    # and plain dequantization does not match them as closely at 2 bits
+    if bits == 2:
+        assert abs(xh0[dense].std() / xf.std() - 1.0) > 5e-3
+    assert np.array_equal(xh[oi], O.f16_to_f32(x)[oi])
+
+
+def test_qnorm_by_hand():
+    """x = [0, 0, 3, 3] with the identity 2-bit code book: codes [0, 0, 3, 3], x_hat = x,
+    so a = 1, b = 0 and the metadata stay.  x = [0, 1, 1, 3]: scale 1, codes [0, 1, 1, 3],
+    again exact.  A constant vector has var_hat = 0: a = 1 and b = 0."""
+    ident = np.arange(4).astype(np.float16).view(np.uint16)
+    for vals in ([0.0, 0.0, 3.0, 3.0], [0.0, 1.0, 1.0, 3.0]):
+        x = _f16(vals)
+        a = O.nuq_quantize_vector(x, ident, 0)
+        b = O.nuq_quantize_vector(x, ident, 0, qnorm=True)
+        assert a[1] == b[1] and a[2] == b[2] and np.array_equal(b[4], O.f16_to_f32(x))
+    x = _f16([2.0, 2.0, 2.0])
+    c, s, m, oi, xh = O.nuq_quantize_vector(x, ident, 0, qnorm=True)
+    assert s == 0 and O.f16_to_f32(m) == 2.0 and np.array_equal(xh, [2.0, 2.0, 2.0])
+
+
+def test_qnorm_on_keys_and_values_of_a_head():
+    k = S.gen_tensor(8, S.TID_K, 1, 1, 256, 128)[0, 0]
+    lut = S.nuq_lut(2)
+    h0 = O.nuq_head(k, k, lut, lut, 100, 256, 0, 0.0)
+    h1 = O.nuq_head(k, k, lut, lut, 100, 256, 0, 0.0, qnorm=True)
+    assert np.array_equal(h0["k_codes"], h1["k_codes"])
+    assert np.array_equal(h0["v_codes"], h1["v_codes"])
+    assert not np.array_equal(h0["k_meta"], h1["k_meta"])
+    # per key channel: dequantized std within 0.5 % of the original's after Q-Norm
+    x = O.f16_to_f32(k).astype(np.float64)
+    r0 = np.abs(h0["k_hat"].std(0) / x.std(0) - 1).mean()
+    r1 = np.abs(h1["k_hat"].std(0) / x.std(0) - 1).mean()
+    assert r1 < r0 and r1 < 5e-3
