@@ -216,7 +216,7 @@ def bench_nuq(w, args) -> dict:
     lut = torch.from_numpy(S.nuq_lut(w.k_bits).view(np.int16)).to(dev)
     c = K.KVCache(B, Hkv, N, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=0, kind=K.KVQ_NUQ,
                   lut=lut,
-                  outlier_bp=w.outlier_bp, v_outlier_bp=w.v_outlier_bp)
+                  outlier_bp=w.outlier_bp, v_outlier_bp=w.v_outlier_bp, qnorm=w.qnorm)
     wsq = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
     ws_q = torch.empty(wsq, dtype=torch.uint8, device=dev)
     sT = (Hkv * N * D, N * D, D)
@@ -288,6 +288,7 @@ def bench_nuq(w, args) -> dict:
                                f"token"
                                + (f" with {w.v_outlier_bp / 100:g}% outliers"
                                   if w.v_outlier_bp else "")
+                               + (", Q-Norm" if w.qnorm else "")
                                + f", RoPE theta {w.rope_theta:g}"},
         "decode_us": round(mean_dec_s * 1e6, 3),
         "decode_bytes": nbytes,

@@ -41,7 +41,7 @@ STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED",
 class kvq_qparams(C.Structure):
     _fields_ = [("kind", C.c_int32), ("bits", C.c_int32), ("axis", C.c_int32),
                 ("group_size", C.c_int32), ("lut", C.c_void_p), ("outlier_bp", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("qnorm", C.c_int32)]
 
 
 class kvq_cache(C.Structure):
@@ -152,10 +152,11 @@ def kvq_decode_attn(c: kvq_cache, q, q_heads: int, sm_scale: float, rope_theta: 
 
 
 # ---- device-memory plumbing --------------------------------------------------------
-def make_qparams(kind: int, bits: int, axis: int, lut=None, outlier_bp: int = 0) -> kvq_qparams:
+def make_qparams(kind: int, bits: int, axis: int, lut=None, outlier_bp: int = 0,
+                 qnorm: int = 0) -> kvq_qparams:
     return kvq_qparams(kind=kind, bits=bits, axis=axis,
                        group_size=32 if kind == KVQ_UNIFORM else 0,
-                       lut=_ptr(lut), outlier_bp=outlier_bp, reserved=0)
+                       lut=_ptr(lut), outlier_bp=outlier_bp, qnorm=qnorm)
 
 
 class KVCache:
@@ -165,15 +166,15 @@ class KVCache:
                  v_bits: int = 2, residual_len: int = 128, head_dim: int = 128,
                  kind: int = KVQ_UNIFORM, lut=None, outlier_bp: int = 0,
                  csr_capacity: int | None = None, sink_len: int = 0,
-                 v_outlier_bp: int = 0, device="cuda"):
+                 v_outlier_bp: int = 0, qnorm: int = 0, device="cuda"):
         import torch
         self.lut = lut
         c = kvq_cache()
         c.batch, c.kv_heads, c.head_dim = batch, kv_heads, head_dim
         c.residual_len, c.capacity_tokens = residual_len, capacity_tokens
         c.sink_len = sink_len
-        c.kq = make_qparams(kind, k_bits, KVQ_AXIS_CHANNEL, lut, outlier_bp)
-        c.vq = make_qparams(kind, v_bits, KVQ_AXIS_TOKEN, lut, v_outlier_bp)
+        c.kq = make_qparams(kind, k_bits, KVQ_AXIS_CHANNEL, lut, outlier_bp, qnorm)
+        c.vq = make_qparams(kind, v_bits, KVQ_AXIS_TOKEN, lut, v_outlier_bp, qnorm)
         if csr_capacity is None:
             csr_capacity = max(0, kvq_csr_entries_needed(c))
         c.csr_capacity = csr_capacity

@@ -124,6 +124,7 @@ struct NuqKeysArgs {
   int64_t sb, sh, st;
   const uint16_t* lut;      // fp16[2^bits]
   int32_t bits;             // 2, 3 or 4
+  int32_t qnorm;            // 1: Q-Norm the per-channel metadata
   int32_t kv_heads;
   int32_t bh_count;         // batch * kv_heads
   int64_t n_tokens;         // tokens quantized (multiple of 32)
@@ -144,6 +145,8 @@ struct NuqKeysArgs {
   uint32_t* outmask;        // [bh][cap_tokens][4]
   uint32_t* chunk_cnt;      // [bh][nchunks]
   uint32_t* chunk_off;      // [bh][nchunks]
+  double* qn_sum;           // [bh][nchunks][D][2]: sum x, sum x^2 of dense entries (Q-Norm)
+  uint32_t* qn_hist;        // [bh][nchunks][D][16]: dense code counts (Q-Norm)
 };
 
 struct NuqValuesArgs {
@@ -151,6 +154,7 @@ struct NuqValuesArgs {
   int64_t sb, sh, st;
   const uint16_t* lut;
   int32_t bits;             // 2, 3 or 4
+  int32_t qnorm;            // 1: Q-Norm the per-token metadata
   int32_t kv_heads, bh_count;
   int32_t n_blocks;
   int64_t tok0;

@@ -70,6 +70,39 @@ __device__ __forceinline__ void params_nuq(float mn, float mx, int bits, uint32_
   *meta = (uint32_t)scale_h | ((uint32_t)min_h << 16);
 }
 
+// Q-Norm of one vector ("KVQuant" review, "Proposed method": the dequantized
+// distribution matched to the statistics before quantization): from the dense
+// entries' sum and sum of squares (fp64) and their code histogram, the metadata
+// (a * scale, a * min + b) that give the dequantized entries the original mean and
+// variance; a = sqrt(var / var_hat) (1 if var_hat = 0), b = mean - a * mean_hat, the
+// moments of the dequantized entries taken level by level (ascending) in fp64 from
+// the fp32 level values lut[c] * scale + min.  The old metadata stand if n = 0.
+__device__ uint32_t qnorm_meta(uint32_t meta, double sx, double sxx, const uint32_t* hist,
+                               uint32_t n, const uint16_t* lut, int bits) {
+  if (n == 0) return meta;
+  const double dn = (double)n;
+  const double mean = sx / dn;
+  double var = sxx / dn - mean * mean;
+  if (var < 0.0) var = 0.0;
+  const float s = f16_bits_to_f32((uint16_t)(meta & 0xFFFFu));
+  const float m = f16_bits_to_f32((uint16_t)(meta >> 16));
+  double m1 = 0.0, m2 = 0.0;
+  for (int c = 0; c < (1 << bits); ++c) {
+    const double lev = (double)(f16_bits_to_f32(lut[c]) * s + m);
+    const double cnt = (double)hist[c];
+    m1 += cnt * lev;
+    m2 += cnt * lev * lev;
+  }
+  const double mean_hat = m1 / dn;
+  double var_hat = m2 / dn - mean_hat * mean_hat;
+  if (var_hat < 0.0) var_hat = 0.0;
+  const double a = var_hat > 0.0 ? sqrt(var / var_hat) : 1.0;
+  const double b = mean - a * mean_hat;
+  const uint16_t s_h = f32_to_f16_bits((float)(a * (double)s));
+  const uint16_t m_h = f32_to_f16_bits((float)(a * (double)m + b));
+  return (uint32_t)s_h | ((uint32_t)m_h << 16);
+}
+
 __device__ __forceinline__ const uint16_t* key_row(const NuqKeysArgs& a, int64_t bh,
                                                    int64_t t) {
   const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
@@ -273,10 +306,14 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
   __shared__ uint32_t om[kGroup][4];
+  __shared__ uint32_t qh[kHeadDim][16];     // Q-Norm: dense code counts per channel
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
   const Mids md = load_mids(a.lut, a.bits);
+  double qsx = 0.0, qsxx = 0.0;
+  if (a.qnorm)
+    for (int i = tid; i < kHeadDim * 16; i += kThreads) (&qh[0][0])[i] = 0u;
   int T = 0x8000, need = 0;
   uint32_t rank = 0;
   float mn = 0.f, inv = 0.f;
@@ -306,6 +343,12 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         const uint32_t c = inv == 0.0f ? 0u : nuq_code((f16_bits_to_f32(x) - mn) * inv, md);
         ct[j][tid] = (uint8_t)c;
         if (out) atomicOr(&om[j][tid >> 5], 1u << (tid & 31));
+        if (a.qnorm && !out) {
+          const double xf = (double)f16_bits_to_f32(x);
+          qsx += xf;
+          qsxx += xf * xf;
+          qh[tid][c] += 1u;                  // the channel's own row: no other writer
+        }
       }
     }
     __syncthreads();
@@ -317,6 +360,37 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
       a.outmask[(bh * a.cap_tokens + tb + (tid >> 2)) * 4 + (tid & 3)] = om[tid >> 2][tid & 3];
     __syncthreads();
   }
+  if (a.qnorm && tid < kHeadDim) {
+    const int64_t q = (bh * a.nchunks + chunk) * kHeadDim + tid;
+    a.qn_sum[q * 2] = qsx;
+    a.qn_sum[q * 2 + 1] = qsxx;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) a.qn_hist[q * 16 + c] = qh[tid][c];
+  }
+}
+
+// Q-Norm of the key channels: the chunks' sums and counts combined in chunk order.
+__global__ void nuq_qnorm_keys_kernel(NuqKeysArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.bh_count * kHeadDim) return;
+  const int64_t bh = i / kHeadDim;
+  const int d = (int)(i % kHeadDim);
+  double sx = 0.0, sxx = 0.0;
+  uint32_t hist[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) hist[c] = 0u;
+  for (int ch = 0; ch < a.nchunks; ++ch) {
+    const int64_t q = (bh * a.nchunks + ch) * kHeadDim + d;
+    sx += a.qn_sum[q * 2];
+    sxx += a.qn_sum[q * 2 + 1];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) hist[c] += a.qn_hist[q * 16 + c];
+  }
+  uint32_t n = 0;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) n += hist[c];
+  uint32_t* meta = a.k_meta + bh * kHeadDim + d;
+  *meta = qnorm_meta(*meta, sx, sxx, hist, n, a.lut, a.bits);
 }
 
 // ---- 7: CSR -------------------------------------------------------------------------
@@ -456,6 +530,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
   __shared__ float2 st[kGroup];
+  __shared__ uint32_t qh[kGroup][16];       // Q-Norm: dense code counts per token
   const int64_t job = blockIdx.x;
   const int blk = (int)(job % a.n_blocks);
   const int64_t bh = job / a.n_blocks;
@@ -471,12 +546,15 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
     dd[0] = u0;
     dd[1] = u1;
   }
+  uint32_t outm = 0;                        // this thread's outlier channels (bits)
+  if (a.qnorm)
+    for (int i = tid; i < kGroup * 16; i += kThreads) (&qh[0][0])[i] = 0u;
   __syncthreads();
   {
     // 8 threads per token (same wave), 16 channels each
     const int t = tid >> 3, part = tid & 7;
     const uint16_t* row = &tile[t][part * 16];
-    const uint32_t outm = a.kv > 0 ? value_outliers(row, part, a.kv) : 0u;
+    outm = a.kv > 0 ? value_outliers(row, part, a.kv) : 0u;
     // min / max of the dense channels, then combine
     float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
@@ -531,6 +609,33 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
     }
   }
   __syncthreads();
+  if (a.qnorm) {
+    // Q-Norm: the token's dense sums and code counts, then its metadata again
+    const int t = tid >> 3, c0 = (tid & 7) * 16;
+    double sx = 0.0, sxx = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (!((outm >> j) & 1u)) {
+        const double xf = (double)f16_bits_to_f32(tile[t][c0 + j]);
+        sx += xf;
+        sxx += xf * xf;
+        atomicAdd(&qh[t][ct[t][c0 + j]], 1u);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sx += __shfl_xor(sx, o);
+      sxx += __shfl_xor(sxx, o);
+    }
+    __syncthreads();
+    if ((tid & 7) == 0) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) n += qh[t][c];
+      uint32_t* meta = a.v_meta + bh * a.cap_tokens + a.tok0 + (int64_t)blk * kGroup + t;
+      *meta = qnorm_meta(*meta, sx, sxx, qh[t], n, a.lut, a.bits);
+    }
+  }
   const int64_t dst = bh * a.cap_blocks + a.tok0 / kGroup + blk;
   for (int wi = tid; wi < kHeadDim * a.bits; wi += kThreads)
     a.v_codes[dst * (kHeadDim * a.bits) + wi] = pack_nuq_word(ct, wi / a.bits, wi % a.bits, a.bits);
@@ -552,6 +657,7 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
   nuq_chunk_stats_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   nuq_finalize_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
   nuq_quant_keys_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  if (a.qnorm) nuq_qnorm_keys_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
   if (a.rowptr != nullptr) {
     csr_count_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
     csr_scan_kernel<<<dim3((unsigned)a.bh_count), dim3(kThreads), 0, s>>>(a);

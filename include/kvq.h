@@ -42,6 +42,15 @@
  *    n quantized tokens (ties: lower token first) are kept exactly in a CSR
  *    matrix and excluded from the channel's min/max.  A code is still stored
  *    for them; attention uses the exact value.
+ *  - Q-Norm (nuq, qnorm = 1; KVQuant review, "Proposed method": the dequantized
+ *    distribution is matched to the statistics taken before quantization): per
+ *    vector, after its codes, (scale, min) become (a * scale, a * min + b) with
+ *    a = sqrt(var / var_hat) (1 if var_hat = 0) and b = mean - a * mean_hat, so
+ *    that the dequantized dense entries get the mean and variance of the original
+ *    ones; each result rounded to fp32, then fp16.  mean and var of the original
+ *    dense entries in fp64 (E[x^2] - E[x]^2); mean_hat and var_hat from the code
+ *    histogram, level values lut[c] * scale + min in fp32, summed in fp64 over c
+ *    ascending.  Codes are unchanged.
  *  - Value outliers (nuq values, outlier_bp > 0): per (batch, head, token) the
  *    kv = ceil(D * outlier_bp / 10000) channels of largest fp16 magnitude (ties:
  *    lower channel first), handled like the key outliers (KVQuant review,
@@ -150,7 +159,8 @@ typedef struct {
   int32_t outlier_bp;  /* NUQ: outliers per vector in basis points (100 = 1 %),
                           0..10000 - keys: of each channel's quantized tokens,
                           values: of each token's D channels; UNIFORM: 0 */
-  int32_t reserved;    /* 0 */
+  int32_t qnorm;       /* NUQ: 1 = Q-Norm the metadata (see above), 0 = off;
+                          UNIFORM: 0 */
 } kvq_qparams;
 
 /* The cache descriptor.  Caller-owned; the library reads it and only

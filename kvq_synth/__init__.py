@@ -178,6 +178,7 @@ class Workload:
     stream_steps: int = 0  # appends (each followed by attention) after the prefill
     sink_len: int = 0      # fp16 attention-sink tokens at the sequence start (kept full)
     v_outlier_bp: int = 0  # dense-and-sparse values: outliers per token vector, basis points
+    qnorm: int = 0         # 1: Q-Norm the nuq metadata
 
     @property
     def ctx(self) -> int:
@@ -209,6 +210,9 @@ WORKLOADS = {
     "kvquant_256k_nuq4": Workload("kvquant_256k_nuq4", 1, 32, 32, 128, 262144, 0, 4, 4, "nuq",
                                   SEED_BASE + 9, 3, 100.0, residual_len=0, outlier_bp=100,
                                   rope_theta=1.0e4),
+    "kvquant_256k_nuq2_qnorm": Workload("kvquant_256k_nuq2_qnorm", 1, 32, 32, 128, 262144, 0,
+                                        2, 2, "nuq", SEED_BASE + 10, 3, 100.0, residual_len=0,
+                                        outlier_bp=100, rope_theta=1.0e4, qnorm=1),
     "kvquant_256k_dense_sparse": Workload("kvquant_256k_dense_sparse", 1, 32, 32, 128, 262144, 0,
                                           3, 3, "nuq", SEED_BASE + 7, 3, 100.0, residual_len=0,
                                           outlier_bp=100, rope_theta=1.0e4, v_outlier_bp=100),

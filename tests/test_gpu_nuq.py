@@ -120,7 +120,7 @@ DECODE = [
 ]
 
 
-def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0, bits=3):
+def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0, bits=3, qnorm=0):
     """Sink tokens [0, ns) in fp16, the next N quantized, the r after them in the window;
     the query sits at position ns + N + r."""
     seed = 300 + N + r + GQ + 7 * ns
@@ -129,7 +129,7 @@ def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0, bits
     cap = max(32, N)
     lk, lv = dev(L), dev(L)
     c = K.KVCache(B, Hkv, cap, k_bits=bits, v_bits=bits, residual_len=R, kind=K.KVQ_NUQ,
-                  lut=lk, outlier_bp=bp, sink_len=S_len, v_outlier_bp=v_bp)
+                  lut=lk, outlier_bp=bp, sink_len=S_len, v_outlier_bp=v_bp, qnorm=qnorm)
     c.c.vq.lut = lv.data_ptr()
     kd, vd = dev(k), dev(v)
     if N:
@@ -161,7 +161,7 @@ def _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=0, S_len=0, v_bp=0, bits
     for b in range(B):
         for h in range(Hkv):
             ref = O.nuq_head(k[b, h], v[b, h], L, L, bp, N, r, theta, n_sink=ns,
-                             v_outlier_bp=v_bp)
+                             v_outlier_bp=v_bp, qnorm=bool(qnorm))
             kh[b, h], vh[b, h] = ref["k_hat"], ref["v_hat"]
     want = O.decode_attention_f64(O.f16_to_f32(q), kh, vh, sm)
     assert np.isfinite(got).all()
@@ -208,3 +208,45 @@ def test_nuq_other_widths_decode_matches_oracle(bits, B, Hkv, GQ, N, r, R, bp, v
     """nuq2 and nuq4 (the KVQuant table's other widths): code books of 4 and 16 levels."""
     _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta, ns=ns, S_len=max(ns, 0), v_bp=v_bp,
                      bits=bits)
+
+
+def _f16_ulps(a, b):
+    """Distance in fp16 units in the last place between arrays of fp16 bit patterns."""
+    def key(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(key(a) - key(b))
+
+
+@pytest.mark.parametrize("bits,bp,v_bp", [(2, 100, 0), (2, 100, 100), (3, 0, 0), (4, 250, 100)])
+def test_nuq_qnorm_quantize_matches_oracle(bits, bp, v_bp):
+    """Q-Norm (KVQuant review, "Proposed method"): codes, outliers and CSR bit-exact; the
+    rewritten fp16 metadata come from fp64 sums whose order differs from the oracle's, so
+    they may differ by one unit in the last place."""
+    B, H, n = 1, 2, 4160
+    k, v = _kv(500 + bits + bp + v_bp, B, H, n)
+    L = S.nuq_lut(bits)
+    lk = dev(L)
+    c = K.KVCache(B, H, n + 64, k_bits=bits, v_bits=bits, residual_len=0, kind=K.KVQ_NUQ,
+                  lut=lk, outlier_bp=bp, v_outlier_bp=v_bp, qnorm=1)
+    _quantize(c, k, v, n)
+    cap = c.c.capacity_tokens
+    kw = host_words(c.buf("k_codes")).reshape(B, H, cap // 32, 128, bits)
+    vw = host_words(c.buf("v_codes")).reshape(B, H, cap // 32, 128, bits)
+    km = host_words(c.buf("k_meta")).reshape(B, H, 128)
+    vm = host_words(c.buf("v_meta")).reshape(B, H, cap)
+    for h in range(H):
+        ref = O.nuq_head(k[0, h], v[0, h], L, L, bp, n, 0, 0.0, v_outlier_bp=v_bp, qnorm=True)
+        plain = O.nuq_head(k[0, h], v[0, h], L, L, bp, n, 0, 0.0, v_outlier_bp=v_bp)
+        assert np.array_equal(kw[0, h, :n // 32], ref["k_codes"])
+        assert np.array_equal(vw[0, h, :n // 32], ref["v_codes"])
+        for got, want in ((km[0, h], ref["k_meta"]), (vm[0, h, :n], ref["v_meta"])):
+            g16 = np.stack([got & 0xFFFF, got >> 16]).astype(np.uint16)
+            w16 = np.stack([want & 0xFFFF, want >> 16]).astype(np.uint16)
+            assert _f16_ulps(g16, w16).max() <= 1
+        assert not np.array_equal(km[0, h], plain["k_meta"])        # the metadata did move
+
+
+@pytest.mark.parametrize("bits,GQ,bp,v_bp", [(2, 1, 100, 0), (2, 4, 100, 100), (3, 2, 0, 0)])
+def test_nuq_qnorm_decode_matches_oracle(bits, GQ, bp, v_bp):
+    _nuq_decode_case(1, 2, GQ, 2048, 17, 32, bp, 1e4, v_bp=v_bp, bits=bits, qnorm=1)

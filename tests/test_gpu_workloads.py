@@ -172,12 +172,14 @@ def test_gqa_long_context_streaming_1024_appends():
 
 
 @pytest.mark.parametrize("name,h", [("kvquant_1m", 7), ("kvquant_256k_dense_sparse", 21),
-                                    ("kvquant_256k_nuq2", 3), ("kvquant_256k_nuq4", 30)])
+                                    ("kvquant_256k_nuq2", 3), ("kvquant_256k_nuq4", 30),
+                                    ("kvquant_256k_nuq2_qnorm", 11)])
 def test_kvquant_context_full_size(name, h):
     """kvquant_1m: 1,048,576 tokens x 32 heads, nuq3 keys with 1 % outliers per channel and
     nuq3 values, RoPE theta 1e4 after dequantization.  kvquant_256k_dense_sparse: 262,144
     tokens with 1 % outliers in every key channel and every value token.
-    kvquant_256k_nuq2 / _nuq4: the 2- and 4-bit widths.  One head is checked end to end."""
+    kvquant_256k_nuq2 / _nuq4: the 2- and 4-bit widths; _nuq2_qnorm with Q-Norm.  One head
+    is checked end to end."""
     w = S.WORKLOADS[name]
     N = w.n_packed
     kd, vd = _device_kv(w, N)
@@ -185,7 +187,7 @@ def test_kvquant_context_full_size(name, h):
     lut = dev(L)
     c = K.KVCache(1, w.kv_heads, N, k_bits=w.k_bits, v_bits=w.v_bits, residual_len=0,
                   kind=K.KVQ_NUQ, lut=lut, outlier_bp=w.outlier_bp,
-                  v_outlier_bp=w.v_outlier_bp)
+                  v_outlier_bp=w.v_outlier_bp, qnorm=w.qnorm)
     wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     D = w.head_dim
@@ -200,13 +202,20 @@ def test_kvquant_context_full_size(name, h):
     assert np.isfinite(out).all()
     k, v = _host_head(w, 0, h, N)
     ref = O.nuq_head(k[0, 0], v[0, 0], L, L, w.outlier_bp, N, 0, w.rope_theta,
-                     v_outlier_bp=w.v_outlier_bp)
+                     v_outlier_bp=w.v_outlier_bp, qnorm=bool(w.qnorm))
     kw = host_words(c.buf("k_codes")).reshape(w.kv_heads, N // 32, D, w.k_bits)
     assert np.array_equal(kw[h], ref["k_codes"])
     km = host_words(c.buf("k_meta")).reshape(w.kv_heads, D)
-    assert np.array_equal(km[h], ref["k_meta"])
     vm = host_words(c.buf("v_meta")).reshape(w.kv_heads, N)
-    assert np.array_equal(vm[h], ref["v_meta"])
+    if w.qnorm:          # fp64 sums in another order: one unit in the last place at most
+        for got, want in ((km[h], ref["k_meta"]), (vm[h], ref["v_meta"])):
+            g = np.stack([got & 0xFFFF, got >> 16]).astype(np.int64)
+            e = np.stack([want & 0xFFFF, want >> 16]).astype(np.int64)
+            key = lambda x: np.where(x & 0x8000, -(x & 0x7FFF), x)   # noqa: E731
+            assert np.abs(key(g) - key(e)).max() <= 1
+    else:
+        assert np.array_equal(km[h], ref["k_meta"])
+        assert np.array_equal(vm[h], ref["v_meta"])
     rp = c.buf("k_csr_rowptr").cpu().numpy().view(np.int32).reshape(w.kv_heads, N + 1)
     assert np.array_equal(rp[h], ref["rowptr"])
     assert int(rp[h, -1]) == D * O.outlier_count(N, w.outlier_bp)
