@@ -332,7 +332,8 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
   }
 #define KVQ_DLB(G_, NW_) KVQ_DL(2, 2, G_, NW_) KVQ_DL(2, 4, G_, NW_) KVQ_DL(4, 2, G_, NW_) \
   KVQ_DL(4, 4, G_, NW_)
-  KVQ_DLB(1, 4) KVQ_DLB(2, 4) KVQ_DLB(4, 4) KVQ_DLB(8, 4)
+  // 2 and 4 query heads per kv head run on the matrix cores (decode_gqa.hip)
+  KVQ_DLB(1, 4) KVQ_DLB(8, 4)
   KVQ_DLB(1, 8) KVQ_DLB(1, 16)
 #undef KVQ_DLB
 #undef KVQ_DL
@@ -345,7 +346,7 @@ const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw) {
     return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_>);
 #define KVQ_DFB(G_, NW_) KVQ_DF(2, 2, G_, NW_) KVQ_DF(2, 4, G_, NW_) KVQ_DF(4, 2, G_, NW_) \
   KVQ_DF(4, 4, G_, NW_)
-  KVQ_DFB(1, 4) KVQ_DFB(2, 4) KVQ_DFB(4, 4) KVQ_DFB(8, 4)
+  KVQ_DFB(1, 4) KVQ_DFB(8, 4)
   KVQ_DFB(1, 8) KVQ_DFB(1, 16)
 #undef KVQ_DFB
 #undef KVQ_DF
