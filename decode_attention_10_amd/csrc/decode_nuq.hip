@@ -25,7 +25,6 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kWindowUnits = 4;
-constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 // Code book in registers: the low and the high bytes of the fp16 entries, four entries
 // per register (entries 4i..4i+3 in lo[i] / hi[i]).
@@ -89,6 +88,14 @@ __device__ __forceinline__ uint32_t codes4(const uint32_t* w, int m) {
   }
 }
 
+// codes4 for nuq3 with the high bits moved straight to bit 2 of each byte by one shift
+// (right by m - 2, or left by 2 - m: m is a constant of the unrolled loop) and merged by
+// one AND-OR.
+__device__ __forceinline__ uint32_t codes4_3(const uint32_t* w, int m) {
+  const uint32_t hs = m >= 2 ? (w[2] >> (m - 2)) : (w[2] << (2 - m));
+  return ((w[m >> 2] >> (2 * (m & 3))) & 0x03030303u) | (hs & 0x04040404u);
+}
+
 template <int B>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
   if constexpr (B == 4) {
@@ -107,9 +114,17 @@ __device__ __forceinline__ float lut_value(const uint16_t* lut, uint32_t c) {
   return f16_bits_to_f32(lut[c]);
 }
 
-// e^(-i phi) for phi = t * theta reduced modulo 2 pi in fp64.
+// e^(-i phi) for phi = t * theta reduced modulo 2 pi in fp64 (Cody-Waite: 2 pi as a
+// 24-bit head, so that k * head is exact for the k < 2^29 of any position below 2^31,
+// plus a tail; the reduced angle lies in [-pi, pi]).
+constexpr double kTwoPiHi = 0x1.921fb4p+2;
+constexpr double kTwoPiLo = 0x1.4442d18469899p-22;
+constexpr double kInvTwoPi = 0x1.45f306dc9c883p-3;
+
 __device__ __forceinline__ float2 rot_at(int64_t t, double theta) {
-  double ph = fmod((double)t * theta, kTwoPi);
+  const double x = (double)t * theta;
+  const double k = rint(x * kInvTwoPi);
+  const double ph = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x));
   float s, c;
   sincosf((float)ph, &s, &c);
   return make_float2(c, -s);
@@ -305,8 +320,13 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
 #pragma unroll
   for (int m4 = 0; m4 < 8; ++m4) {
     uint32_t a01, a23, b01, b23;
-    lut4<B>(lk, codes4<B>(kw0, m4), a01, a23);
-    lut4<B>(lk, codes4<B>(kw1, m4), b01, b23);
+    if constexpr (B == 3) {
+      lut4<B>(lk, codes4_3(kw0, m4), a01, a23);
+      lut4<B>(lk, codes4_3(kw1, m4), b01, b23);
+    } else {
+      lut4<B>(lk, codes4<B>(kw0, m4), a01, a23);
+      lut4<B>(lk, codes4<B>(kw1, m4), b01, b23);
+    }
     kd0[4 * m4 + 0] = fmaf(lo_f16(a01), pc.ks0, pc.km0);
     kd0[4 * m4 + 1] = fmaf(hi_f16(a01), pc.ks0, pc.km0);
     kd0[4 * m4 + 2] = fmaf(lo_f16(a23), pc.ks0, pc.km0);
@@ -400,8 +420,13 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     for (int m4 = 0; m4 < 8; ++m4) {
       const float4 w4 = pp[m4];
       uint32_t a01, a23, b01, b23;
-      lut4<B>(lv, codes4<B>(vw0, m4), a01, a23);
-      lut4<B>(lv, codes4<B>(vw1, m4), b01, b23);
+      if constexpr (B == 3) {
+        lut4<B>(lv, codes4_3(vw0, m4), a01, a23);
+        lut4<B>(lv, codes4_3(vw1, m4), b01, b23);
+      } else {
+        lut4<B>(lv, codes4<B>(vw0, m4), a01, a23);
+        lut4<B>(lv, codes4<B>(vw1, m4), b01, b23);
+      }
       o0 = fmaf(w4.x, lo_f16(a01), o0); o0 = fmaf(w4.y, hi_f16(a01), o0);
       o0 = fmaf(w4.z, lo_f16(a23), o0); o0 = fmaf(w4.w, hi_f16(a23), o0);
       o1 = fmaf(w4.x, lo_f16(b01), o1); o1 = fmaf(w4.y, hi_f16(b01), o1);
