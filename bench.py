@@ -17,8 +17,11 @@ launch overhead.
 Printed: one JSON line.  value = decode-attention GB/s: algorithmic bytes of codes,
 metadata, fp16 window, q and out per decode / mean decode time, from HIP events on
 the launch stream around replays of a decode-only graph (kernel plus the small gap
-between launches).  Also tokens*ctx/s, prefill quantize GB/s, the roofline of the
-decode kernel and the oracle timed on a bounded host sample.
+between launches); p10 / p50 / p90 of the per-replay means beside it.  Also
+tokens*ctx/s, prefill quantize GB/s, the roofline of the decode kernel, the rate of a
+plain 1 GiB device copy on the same box (and value as a fraction of it) and the oracle
+timed on a bounded host sample.  KVQuant-style workloads (--workload kvquant_...) time
+one decode per step over a one-shot quantized context.
 """
 from __future__ import annotations
 
@@ -89,6 +92,44 @@ def copy_calibration(mib: int) -> dict:
         dst.copy_(src)
     torch.cuda.synchronize()
     return {"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}
+
+
+def time_replays(graph, rounds: int, per_replay: int, stream):
+    """Replays ``graph`` ``rounds`` times with HIP events on ``stream`` around each replay.
+    Returns (mean seconds per step over the whole run, [p10, p50, p90] of the per-replay
+    mean step time)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(rounds + 1)]
+    ev[0].record(stream)
+    for i in range(rounds):
+        graph.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 / per_replay for i in range(rounds)])
+    mean = ev[0].elapsed_time(ev[rounds]) * 1e-3 / (rounds * per_replay)
+    return mean, [float(np.percentile(per, q)) for q in (10, 50, 90)]
+
+
+def copy_bandwidth(mib: int = 1024) -> float:
+    """GB/s of a plain device-to-device copy (bytes read + bytes written): the streaming
+    rate this machine reaches outside the library, reported next to the 8 TB/s peak."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / 10
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / t / 1e9
 
 
 def decode_bytes(w, n_packed: int, n_resid: int) -> int:
@@ -266,15 +307,10 @@ def bench_nuq(w, args) -> dict:
     g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(rounds):
-        g.replay()
-    d1.record(stream)
-    torch.cuda.synchronize()
+    mean_dec_s, pct = time_replays(g, rounds, round_len, stream)
     wall = time.perf_counter() - t0
-    mean_dec_s = d0.elapsed_time(d1) * 1e-3 / steps
     nbytes = nuq_decode_bytes(w, N)
+    copy_gbs = copy_bandwidth()
     gbs = nbytes / mean_dec_s / 1e9
     return {
         "metric": "decode-attn HBM GB/s on packed KV (% of peak); tokens*ctx/s; quantize GB/s",
@@ -291,7 +327,10 @@ def bench_nuq(w, args) -> dict:
                                + (", Q-Norm" if w.qnorm else "")
                                + f", RoPE theta {w.rope_theta:g}"},
         "decode_us": round(mean_dec_s * 1e6, 3),
+        "decode_us_p10_p50_p90": [round(x * 1e6, 3) for x in pct],
         "decode_bytes": nbytes,
+        "copy_gbs": round(copy_gbs, 1),
+        "frac_of_copy": round(gbs / copy_gbs, 4),
         "tokens_ctx_per_s": round(B * N / mean_dec_s, 1),
         "quantize_gbs": round(quant_gbs, 1),
         "quantize_ms_prefill": round(quant_ms, 3),
@@ -440,13 +479,8 @@ def main() -> int:
     wall = time.perf_counter() - t0
 
     # decode kernel time: events around replays of the decode-only graph
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(rounds):
-        dec_graph.replay()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    mean_dec_s = d0.elapsed_time(d1) * 1e-3 / (rounds * round_len)
+    mean_dec_s, pct = time_replays(dec_graph, rounds, round_len, stream)
+    copy_gbs = copy_bandwidth()
     dec_bytes = decode_bytes(w, N, w.n_resid)
     gbs = dec_bytes / mean_dec_s / 1e9
     tok_ctx = B * T / mean_dec_s
@@ -470,6 +504,9 @@ def main() -> int:
                                f"per-channel / V int{w.v_bits} per-token, group 32",
                    "layers_rotated": layers, "flush_every": R},
         "decode_us": round(mean_dec_s * 1e6, 3),
+        "decode_us_p10_p50_p90": [round(x * 1e6, 3) for x in pct],
+        "copy_gbs": round(copy_gbs, 1),
+        "frac_of_copy": round(gbs / copy_gbs, 4),
         "step_bytes_mean": int(np.mean(nbytes)),
         "tokens_ctx_per_s": round(tok_ctx, 1),
         "quantize_gbs": round(quant_gbs, 1),
