@@ -15,9 +15,11 @@
 // corrections in row order.
 //
 // Values: one lane per channel pair as well; o_d += (p_t * s_t) * lut[c_td] plus the
-// per-token minimum term sum_t p_t m_t, identical for every channel.
-// Code-book lookups: four codes in the four bytes of a word select bytes of the
-// eight-entry fp16 table with v_perm_b32.
+// per-token minimum term sum_t p_t m_t, identical for every channel; each token's
+// value outliers (if any) add p_t * (x - dequant(code)) to their channels.
+// Code-book lookups: four codes in the four bytes of a word select bytes of the fp16
+// table with v_perm_b32 (4 or 8 entries in one source pair; 16 entries in two).
+// Code widths B = 2, 3, 4 (kernel template); sink and window tokens are fp16 chunks.
 #include "kvq_common.h"
 
 namespace kvq {
