@@ -27,33 +27,32 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Midpoints between consecutive code-book levels (2^B - 1 of them, B <= 4).
+// Midpoints between consecutive code-book levels (2^B - 1 of them).
+template <int B>
 struct Mids {
-  float m[15];
-  int n;
+  float m[(1 << B) - 1];
 };
 
-__device__ __forceinline__ Mids load_mids(const uint16_t* lut, int bits) {
-  Mids r;
-  r.n = (1 << bits) - 1;
+template <int B>
+__device__ __forceinline__ Mids<B> load_mids(const uint16_t* lut) {
+  Mids<B> r;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) {
-    r.m[i] = __builtin_inff();
-    if (i < r.n)                                       // reads lut[0 .. 2^bits - 1] only
-      r.m[i] = (f16_bits_to_f32(lut[i]) + f16_bits_to_f32(lut[i + 1])) * 0.5f;
-  }
+  for (int i = 0; i < (1 << B) - 1; ++i)
+    r.m[i] = (f16_bits_to_f32(lut[i]) + f16_bits_to_f32(lut[i + 1])) * 0.5f;
   return r;
 }
 
 // Index of the nearest code-book level (ties to the even index).
-__device__ __forceinline__ uint32_t nuq_code(float xn, const Mids& md) {
+template <int B>
+__device__ __forceinline__ uint32_t nuq_code(float xn, const Mids<B>& md) {
+  constexpr int NM = (1 << B) - 1;
   uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < 15; ++i) c += xn > md.m[i] ? 1u : 0u;      // unused midpoints: +inf
+  for (int i = 0; i < NM; ++i) c += xn > md.m[i] ? 1u : 0u;
   float mid_c = md.m[0];
 #pragma unroll
-  for (int i = 1; i < 15; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
-  if (c < (uint32_t)md.n && (c & 1u) && xn == mid_c) c += 1;
+  for (int i = 1; i < NM; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
+  if (c < (uint32_t)NM && (c & 1u) && xn == mid_c) c += 1;
   return c;
 }
 
@@ -302,6 +301,7 @@ __device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim],
 }
 
 // ---- 6: codes and outlier bitmask ---------------------------------------------------
+template <int B>
 __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a) {
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
-  const Mids md = load_mids(a.lut, a.bits);
+  const Mids<B> md = load_mids<B>(a.lut);
   double qsx = 0.0, qsxx = 0.0;
   if (a.qnorm)
     for (int i = tid; i < kHeadDim * 16; i += kThreads) (&qh[0][0])[i] = 0u;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
           out = rank < (uint32_t)need;
           ++rank;
         }
-        const uint32_t c = inv == 0.0f ? 0u : nuq_code((f16_bits_to_f32(x) - mn) * inv, md);
+        const uint32_t c = inv == 0.0f ? 0u : nuq_code<B>((f16_bits_to_f32(x) - mn) * inv, md);
         ct[j][tid] = (uint8_t)c;
         if (out) atomicOr(&om[j][tid >> 5], 1u << (tid & 31));
         if (a.qnorm && !out) {
@@ -526,6 +526,7 @@ __device__ uint32_t value_outliers(const uint16_t* row, int part, int kv) {
 }
 
 // ---- values: per token over all channels --------------------------------------------
+template <int B>
 __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArgs a) {
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   const int64_t bh = job / a.n_blocks;
   const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
   const int tid = threadIdx.x;
-  const Mids md = load_mids(a.lut, a.bits);
+  const Mids<B> md = load_mids<B>(a.lut);
   {
     const int t = tid >> 3, c = (tid & 7) * 16;
     const uint4* p = reinterpret_cast<const uint4*>(a.v + b * a.sb + h * a.sh +
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float x = f16_bits_to_f32(tile[t][c0 + j]);
-      ct[t][c0 + j] = (uint8_t)(g.y == 0.0f ? 0u : nuq_code((x - g.x) * g.y, md));
+      ct[t][c0 + j] = (uint8_t)(g.y == 0.0f ? 0u : nuq_code<B>((x - g.x) * g.y, md));
     }
   }
   __syncthreads();
@@ -656,7 +657,9 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
   nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 1);
   nuq_chunk_stats_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   nuq_finalize_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
-  nuq_quant_keys_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  if (a.bits == 2) nuq_quant_keys_kernel<2><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  else if (a.bits == 3) nuq_quant_keys_kernel<3><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  else nuq_quant_keys_kernel<4><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   if (a.qnorm) nuq_qnorm_keys_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
   if (a.rowptr != nullptr) {
     csr_count_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
@@ -669,7 +672,10 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
 hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s) {
   const int64_t jobs = (int64_t)a.bh_count * a.n_blocks;
   if (jobs == 0) return hipSuccess;
-  nuq_quant_values_kernel<<<dim3((unsigned)jobs), dim3(kThreads), 0, s>>>(a);
+  const dim3 grid((unsigned)jobs), block(kThreads);
+  if (a.bits == 2) nuq_quant_values_kernel<2><<<grid, block, 0, s>>>(a);
+  else if (a.bits == 3) nuq_quant_values_kernel<3><<<grid, block, 0, s>>>(a);
+  else nuq_quant_values_kernel<4><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
