@@ -113,6 +113,10 @@
  *    status of the calling thread.
  *  - Calls that share a cache or a workspace on one stream are ordered; calls
  *    on different streams that touch the same buffers race.
+ *  - Calls enqueue kernel launches only (no memsets, copies or allocations), so
+ *    they can be captured into a HIP graph.  A captured call keeps the pointers
+ *    and the counters (n_packed, n_resid, n_sink) it saw at capture: each replay
+ *    repeats that step on the buffers' current contents.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -247,7 +251,9 @@ kvq_status kvq_append_flush(kvq_cache* c, const uint16_t* k_new, const uint16_t*
  * cache: q fp16 [batch][q_heads][D], out fp32 [batch][q_heads][D], both contiguous.
  * q_heads is a multiple of kv_heads (at most 8 query heads per kv head).
  * rope_theta: 0 = no rotation; > 0 (NUQ caches only) rotates key t at position t.
- * workspace: kvq_workspace_bytes(c, q_heads, KVQ_OP_DECODE_ATTN) bytes. */
+ * workspace: kvq_workspace_bytes(c, q_heads, KVQ_OP_DECODE_ATTN) bytes; its
+ * contents need no initialization.  A cache with no tokens (no sink, packed or
+ * window tokens) gives out = 0. */
 kvq_status kvq_decode_attn(const kvq_cache* c, const uint16_t* q, int32_t q_heads,
                            float sm_scale, float rope_theta, float* out, void* workspace,
                            size_t ws_bytes, void* stream);
