@@ -92,19 +92,35 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
       st[tid] = make_float2(g.mn, g.inv);
     }
     __syncthreads();
+    // Word wi = t * WK + col holds channels col*CPW .. col*CPW + CPW - 1 of token t.  A
+    // thread keeps one column for all its words, so it reads its channels' (min, 1/scale)
+    // once, and reads each token's CPW fp16 values as 16-byte vectors: the lanes of one
+    // token read a contiguous row (scalar 2-byte reads of the same values conflicted
+    // heavily in the LDS banks).
+    const int col = tid % WK;
+    const int c0 = col * CPW;
+    float gmn[CPW], ginv[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; j += 2) {
+      const float4 g = *reinterpret_cast<const float4*>(&st[c0 + j]);
+      gmn[j] = g.x; ginv[j] = g.y; gmn[j + 1] = g.z; ginv[j + 1] = g.w;
+    }
 #pragma unroll
     for (int i = 0; i < (kGroup * WK) / kThreads; ++i) {
-      const int wi = tid + i * kThreads;
-      const int t = wi / WK;
-      const int c0 = (wi % WK) * CPW;
+      const int t = tid / WK + i * (kThreads / WK);
+      uint32_t x[CPW / 2];                      // CPW fp16 values, two per word
+#pragma unroll
+      for (int k = 0; k < CPW / 8; ++k) {
+        const uint4 u = *reinterpret_cast<const uint4*>(&tile[t][c0 + 8 * k]);
+        x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+      }
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
-        const float2 g = st[c0 + j];
-        const uint32_t q = code_of(f16_bits_to_f32(tile[t][c0 + j]), g.x, g.y, L);
-        word |= q << (KB * j);
+        const float v = (j & 1) ? hi_f16(x[j >> 1]) : lo_f16(x[j >> 1]);
+        word |= code_of(v, gmn[j], ginv[j], L) << (KB * j);
       }
-      a.k_codes[dst * (kGroup * WK) + wi] = word;
+      a.k_codes[dst * (kGroup * WK) + t * WK + col] = word;
     }
     __syncthreads();
    }
