@@ -42,17 +42,46 @@ __device__ __forceinline__ Mids<B> load_mids(const uint16_t* lut) {
   return r;
 }
 
-// Index of the nearest code-book level (ties to the even index).
+// Index of the nearest code-book level (ties to the even index).  The code is the
+// number of midpoints below xn, found by a binary search over the ascending midpoints:
+// bit by bit from the top, each step comparing with the midpoint its higher bits pick.
+// The picks are select trees on those comparison results (constant indices, so the
+// midpoints stay in registers).  A value exactly on the midpoint above an odd level goes
+// to the even level above it.
 template <int B>
 __device__ __forceinline__ uint32_t nuq_code(float xn, const Mids<B>& md) {
-  constexpr int NM = (1 << B) - 1;
-  uint32_t c = 0;
+  // the midpoints as values: a conditional between two array elements would otherwise be
+  // a select of their addresses, which keeps the array out of registers
+  float m[(1 << B) - 1];
 #pragma unroll
-  for (int i = 0; i < NM; ++i) c += xn > md.m[i] ? 1u : 0u;
-  float mid_c = md.m[0];
-#pragma unroll
-  for (int i = 1; i < NM; ++i) mid_c = (c == (uint32_t)i) ? md.m[i] : mid_c;
-  if (c < (uint32_t)NM && (c & 1u) && xn == mid_c) c += 1;
+  for (int i = 0; i < (1 << B) - 1; ++i) m[i] = md.m[i];
+  const auto v = [&](int i) -> float { return m[i]; };
+  uint32_t c;
+  float mo;                                        // midpoint above level c when c is odd
+  if constexpr (B == 2) {
+    const bool b1 = xn > v(1);
+    const bool b2 = xn > (b1 ? v(2) : v(0));
+    c = 2u * b1 + b2;
+    mo = v(1);
+  } else if constexpr (B == 3) {
+    const bool b1 = xn > v(3);
+    const bool b2 = xn > (b1 ? v(5) : v(1));
+    const bool b3 = xn > (b1 ? (b2 ? v(6) : v(4)) : (b2 ? v(2) : v(0)));
+    c = 4u * b1 + 2u * b2 + b3;
+    mo = b1 ? v(5) : (b2 ? v(3) : v(1));
+  } else {
+    const bool b1 = xn > v(7);
+    const bool b2 = xn > (b1 ? v(11) : v(3));
+    const bool b3 = xn > (b1 ? (b2 ? v(13) : v(9)) : (b2 ? v(5) : v(1)));
+    const float q0 = b2 ? (b3 ? v(6) : v(4)) : (b3 ? v(2) : v(0));
+    const float q1 = b2 ? (b3 ? v(14) : v(12)) : (b3 ? v(10) : v(8));
+    const bool b4 = xn > (b1 ? q1 : q0);
+    c = 8u * b1 + 4u * b2 + 2u * b3 + b4;
+    const float o0 = b2 ? (b3 ? v(7) : v(5)) : (b3 ? v(3) : v(1));
+    const float o1 = b2 ? (b3 ? v(14) : v(13)) : (b3 ? v(11) : v(9));
+    mo = b1 ? o1 : o0;
+  }
+  if ((c & 1u) && c < (uint32_t)((1 << B) - 1) && xn == mo) c += 1;
   return c;
 }
 
@@ -115,14 +144,20 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 }
 
 // ---- 1/3: magnitude histograms (LDS counts are u16 pairs packed in u32) ------------
+// A lane owns channels 2l, 2l+1 (one 4-byte load per token); the four waves take every
+// fourth token.  Each channel's row of counters is padded by one word so that the rows
+// of different channels start on different LDS banks: key magnitudes crowd into a few
+// bins, and unpadded rows put a wave's 128 atomics on the same few banks.  Sixteen
+// tokens' loads are issued before their atomics.
 template <bool LOW>
 __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
-  __shared__ uint32_t h[kHeadDim][64 + (LOW ? 0 : 64)];   // 256 or 128 bins per channel
   constexpr int NB = LOW ? 128 : 256;
+  constexpr int RW = NB / 2 + 1;                          // words per channel row
+  __shared__ uint32_t h[kHeadDim][RW];
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kHeadDim * NB / 2; i += kThreads) (&h[0][0])[i] = 0;
+  for (int i = tid; i < kHeadDim * RW; i += kThreads) (&h[0][0])[i] = 0;
   int sel0 = -1, sel1 = -1;
   const int cp = tid & 63;
   if (LOW) {
@@ -132,8 +167,7 @@ __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
   __syncthreads();
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
   const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
-  for (int64_t t = t0 + (tid >> 6); t < t1; t += kThreads / 64) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + 2 * cp);
+  auto count = [&](uint32_t w) {
     const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
     if (!LOW) {
       atomicAdd(&h[2 * cp][(m0 >> 7) >> 1], (m0 >> 7) & 1u ? 0x10000u : 1u);
@@ -142,13 +176,25 @@ __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
       if ((int)(m0 >> 7) == sel0) atomicAdd(&h[2 * cp][(m0 & 127u) >> 1], m0 & 1u ? 0x10000u : 1u);
       if ((int)(m1 >> 7) == sel1) atomicAdd(&h[2 * cp + 1][(m1 & 127u) >> 1], m1 & 1u ? 0x10000u : 1u);
     }
+  };
+  constexpr int U = 16;                                   // tokens in flight per lane
+  constexpr int STEP = kThreads / 64;                     // tokens per pass of the block
+  int64_t t = t0 + (tid >> 6);
+  for (; t + (int64_t)(U - 1) * STEP < t1; t += (int64_t)U * STEP) {
+    uint32_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * STEP) + 2 * cp);
+#pragma unroll
+    for (int u = 0; u < U; ++u) count(w[u]);
   }
+  for (; t < t1; t += STEP) count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + 2 * cp));
   __syncthreads();
   uint32_t* g = LOW ? a.hist_lo : a.hist_hi;
   for (int i = tid; i < kHeadDim * NB / 2; i += kThreads) {
-    const uint32_t v = (&h[0][0])[i];
-    if (v == 0) continue;
     const int d = i / (NB / 2), b2 = i % (NB / 2);
+    const uint32_t v = h[d][b2];
+    if (v == 0) continue;
     uint32_t* row = g + (bh * kHeadDim + d) * NB;
     if (v & 0xFFFFu) atomicAdd(&row[2 * b2], v & 0xFFFFu);
     if (v >> 16) atomicAdd(&row[2 * b2 + 1], v >> 16);
@@ -304,7 +350,6 @@ __device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim],
 template <int B>
 __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a) {
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
-  __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
   __shared__ uint32_t om[kGroup][4];
   __shared__ uint32_t qh[kHeadDim][16];     // Q-Norm: dense code counts per channel
   const int64_t bh = blockIdx.x / a.nchunks;
@@ -314,16 +359,18 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   double qsx = 0.0, qsxx = 0.0;
   if (a.qnorm)
     for (int i = tid; i < kHeadDim * 16; i += kThreads) (&qh[0][0])[i] = 0u;
-  int T = 0x8000, need = 0;
-  uint32_t rank = 0;
-  float mn = 0.f, inv = 0.f;
-  if (tid < kHeadDim) {
-    const int64_t i = bh * kHeadDim + tid;
-    T = a.thr[i * 4];
-    need = a.thr[i * 4 + 1];
-    rank = a.tie_prefix[(bh * a.nchunks + chunk) * kHeadDim + tid];
-    mn = a.norm[i * 2];
-    inv = a.norm[i * 2 + 1];
+  // per-channel state of this lane's channel (two lanes per channel)
+  int cT, cneed;
+  uint32_t crank;
+  float cmn, cinv;
+  {
+    const int ch = tid >> 1;
+    const int64_t i = bh * kHeadDim + ch;
+    cT = a.thr[i * 4];
+    cneed = a.thr[i * 4 + 1];
+    crank = a.tie_prefix[(bh * a.nchunks + chunk) * kHeadDim + ch];
+    cmn = a.norm[i * 2];
+    cinv = a.norm[i * 2 + 1];
   }
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
   const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
@@ -331,41 +378,81 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
     load_key_tile(tile, a, bh, tb);
     if (tid < kGroup * 4) om[tid >> 2][tid & 3] = 0;
     __syncthreads();
-    if (tid < kHeadDim) {
-      for (int j = 0; j < kGroup; ++j) {
-        const uint16_t x = tile[j][tid];
-        const int mag = x & 0x7FFF;
-        bool out = mag > T;
-        if (mag == T) {
-          out = rank < (uint32_t)need;
-          ++rank;
+    {
+      // Two lanes of one wave per channel, tokens 0..15 and 16..31.  The outlier rank of
+      // ties at the threshold runs in token order: the second half's continues from the
+      // first half's count.  Codes go straight into the channel's B code words.
+      const int ch = tid >> 1, half = tid & 1;
+      uint32_t xs[16];
+      uint32_t my_ties = 0;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        xs[jj] = tile[16 * half + jj][ch];
+        my_ties += (int)(xs[jj] & 0x7FFFu) == cT ? 1u : 0u;
+      }
+      const uint32_t other_ties = __shfl_xor(my_ties, 1);
+      uint32_t r = crank + (half ? other_ties : 0u);
+      uint32_t lo = 0u, hi = 0u, w4[2] = {0u, 0u};
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const uint32_t x = xs[jj];
+        const int mag = (int)(x & 0x7FFFu);
+        bool out = mag > cT;
+        if (mag == cT) {
+          out = r < (uint32_t)cneed;
+          ++r;
         }
-        const uint32_t c = inv == 0.0f ? 0u : nuq_code<B>((f16_bits_to_f32(x) - mn) * inv, md);
-        ct[j][tid] = (uint8_t)c;
-        if (out) atomicOr(&om[j][tid >> 5], 1u << (tid & 31));
+        const uint32_t c =
+            cinv == 0.0f ? 0u : nuq_code<B>((f16_bits_to_f32((uint16_t)x) - cmn) * cinv, md);
+        // the bit positions of pack_nuq_word for token j = 16 * half + jj
+        if constexpr (B == 4) {
+          w4[jj >> 3] |= (c & 15u) << (8 * (jj & 3) + 4 * ((jj & 7) >> 2));
+        } else {
+          lo |= (c & 3u) << (8 * (jj & 3) + 2 * (jj >> 2));
+          if constexpr (B == 3) hi |= (c >> 2) << (8 * (jj & 3) + (jj >> 2));
+        }
+        const int j = 16 * half + jj;
+        if (out) atomicOr(&om[j][ch >> 5], 1u << (ch & 31));
         if (a.qnorm && !out) {
-          const double xf = (double)f16_bits_to_f32(x);
+          const double xf = (double)f16_bits_to_f32((uint16_t)x);
           qsx += xf;
           qsxx += xf * xf;
-          qh[tid][c] += 1u;                  // the channel's own row: no other writer
+          atomicAdd(&qh[ch][c], 1u);
+        }
+      }
+      crank += my_ties + other_ties;
+      uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
+      if constexpr (B == 4) {
+        kw[2 * half] = w4[0];
+        kw[2 * half + 1] = w4[1];
+      } else {
+        kw[half] = lo;
+        if constexpr (B == 3) {
+          // high bits of token 16 * half + jj sit at 8 * (jj & 3) + 4 * half + (jj >> 2)
+          const uint32_t h = hi << (4 * half);
+          const uint32_t both = h | __shfl_xor(h, 1);
+          if (half == 0) kw[2] = both;
         }
       }
     }
     __syncthreads();
-    const int64_t blk = bh * a.cap_blocks + tb / kGroup;
-    for (int wi = tid; wi < kHeadDim * a.bits; wi += kThreads)
-      a.k_codes[blk * (kHeadDim * a.bits) + wi] =
-          pack_nuq_word(ct, wi / a.bits, wi % a.bits, a.bits);
     if (tid < kGroup * 4)
       a.outmask[(bh * a.cap_tokens + tb + (tid >> 2)) * 4 + (tid & 3)] = om[tid >> 2][tid & 3];
     __syncthreads();
   }
-  if (a.qnorm && tid < kHeadDim) {
-    const int64_t q = (bh * a.nchunks + chunk) * kHeadDim + tid;
-    a.qn_sum[q * 2] = qsx;
-    a.qn_sum[q * 2 + 1] = qsxx;
+  if (a.qnorm) {
+    // the two lanes of a channel combine their sums; the block's atomics on qh are done
+    qsx += __shfl_xor(qsx, 1);
+    qsxx += __shfl_xor(qsxx, 1);
+    __syncthreads();
+    if ((tid & 1) == 0) {
+      const int ch = tid >> 1;
+      const int64_t q = (bh * a.nchunks + chunk) * kHeadDim + ch;
+      a.qn_sum[q * 2] = qsx;
+      a.qn_sum[q * 2 + 1] = qsxx;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) a.qn_hist[q * 16 + c] = qh[tid][c];
+      for (int c = 0; c < 16; ++c) a.qn_hist[q * 16 + c] = qh[ch][c];
+    }
   }
 }
 
@@ -480,20 +567,39 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
 // Outliers of one token's vector ("KVQuant" review, abstract item (iv): the largest
 // magnitudes of each vector are kept exactly): the kv channels of largest fp16
 // magnitude, ties to the lower channel.  Eight threads (consecutive lanes) hold 16
-// channels each; a binary search finds the threshold T, the largest magnitude with at
-// least kv channels at or above it, then channels above T are outliers and the first
-// kv - count(> T) channels equal to T (in channel order) are too.  Returns this
-// thread's flags (bit j: channel 16 * part + j).
+// channels each.  Up to six outliers are taken one at a time, largest magnitude first
+// (lower channel first among equals).  Otherwise a binary search finds the threshold T,
+// the largest magnitude with at least kv channels at or above it; channels above T are
+// outliers, and so are the first kv - count(> T) channels equal to T (in channel
+// order).  Returns this thread's flags (bit j: channel 16 * part + j).
 __device__ __forceinline__ uint32_t count8(uint32_t x) {
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
 
-__device__ uint32_t value_outliers(const uint16_t* row, int part, int kv) {
+__device__ uint32_t value_outliers(const uint32_t (&xw)[8], int part, int kv) {
   uint32_t mag[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) mag[j] = row[j] & 0x7FFFu;
+  for (int j = 0; j < 16; ++j) mag[j] = (xw[j >> 1] >> (16 * (j & 1))) & 0x7FFFu;
+  if (kv <= 6) {
+    // Few outliers: take the largest remaining (magnitude, lower channel first) kv times.
+    // The key (magnitude << 8 | 255 - channel) is unique per channel and at least 128.
+    uint32_t flags = 0;
+    for (int r = 0; r < kv; ++r) {
+      uint32_t best = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t key = (mag[j] << 8) | (uint32_t)(255 - (part * 16 + j));
+        if (!((flags >> j) & 1u)) best = max(best, key);
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) best = max(best, (uint32_t)__shfl_xor(best, o));
+      const int ch = 255 - (int)(best & 255u);
+      if ((ch >> 4) == part) flags |= 1u << (ch & 15);
+    }
+    return flags;
+  }
   uint32_t lo = 0, hi = 0x7FFF;
   for (int it = 0; it < 15; ++it) {                // hi - lo + 1 halves from 2^15 to 1
     const uint32_t mid = (lo + hi + 1) >> 1;
@@ -526,7 +632,9 @@ __device__ uint32_t value_outliers(const uint16_t* row, int part, int kv) {
 }
 
 // ---- values: per token over all channels --------------------------------------------
-template <int B>
+// VOUT: the cache keeps per-token value outliers (an instance of its own, so that the
+// search's registers do not lower the occupancy of the plain case).
+template <int B, bool VOUT>
 __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArgs a) {
   __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
@@ -551,17 +659,26 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   if (a.qnorm)
     for (int i = tid; i < kGroup * 16; i += kThreads) (&qh[0][0])[i] = 0u;
   __syncthreads();
+  // 8 threads per token (same wave), 16 channels each; the thread's 16 fp16 values are
+  // read from LDS once, as two 16-byte vectors (two values per word)
+  const int t = tid >> 3, part = tid & 7, c0 = part * 16;
+  uint32_t xw[8];
   {
-    // 8 threads per token (same wave), 16 channels each
-    const int t = tid >> 3, part = tid & 7;
-    const uint16_t* row = &tile[t][part * 16];
-    outm = a.kv > 0 ? value_outliers(row, part, a.kv) : 0u;
+    const uint4* rp = reinterpret_cast<const uint4*>(&tile[t][c0]);
+    const uint4 r0 = rp[0], r1 = rp[1];
+    xw[0] = r0.x; xw[1] = r0.y; xw[2] = r0.z; xw[3] = r0.w;
+    xw[4] = r1.x; xw[5] = r1.y; xw[6] = r1.z; xw[7] = r1.w;
+  }
+  const auto xv = [&](int j) -> float { return (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]); };
+  {
+    const uint16_t* row = &tile[t][c0];
+    outm = VOUT ? value_outliers(xw, part, a.kv) : 0u;
     // min / max of the dense channels, then combine
     float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (!((outm >> j) & 1u)) {
-        const float x = f16_bits_to_f32(row[j]);
+        const float x = xv(j);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
       }
@@ -572,7 +689,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
     if (mn > mx) mn = mx = 0.0f;          // every channel an outlier
-    if (a.kv > 0) {
+    if (VOUT) {
       // this thread's outliers, channels ascending, after those of the lower parts
       const uint32_t mine = (uint32_t)__builtin_popcount(outm);
       uint32_t before = mine;
@@ -600,27 +717,28 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
     }
   }
   __syncthreads();
+  uint32_t code[16];
   {
-    const int t = tid >> 3, c0 = (tid & 7) * 16;
     const float2 g = st[t];
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float x = f16_bits_to_f32(tile[t][c0 + j]);
-      ct[t][c0 + j] = (uint8_t)(g.y == 0.0f ? 0u : nuq_code<B>((x - g.x) * g.y, md));
+      code[j] = g.y == 0.0f ? 0u : nuq_code<B>((xv(j) - g.x) * g.y, md);
+      cw[j >> 2] |= code[j] << (8 * (j & 3));
     }
+    *reinterpret_cast<uint4*>(&ct[t][c0]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
   }
   __syncthreads();
   if (a.qnorm) {
     // Q-Norm: the token's dense sums and code counts, then its metadata again
-    const int t = tid >> 3, c0 = (tid & 7) * 16;
     double sx = 0.0, sxx = 0.0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (!((outm >> j) & 1u)) {
-        const double xf = (double)f16_bits_to_f32(tile[t][c0 + j]);
+        const double xf = (double)xv(j);
         sx += xf;
         sxx += xf * xf;
-        atomicAdd(&qh[t][ct[t][c0 + j]], 1u);
+        atomicAdd(&qh[t][code[j]], 1u);
       }
     }
 #pragma unroll
@@ -673,9 +791,13 @@ hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s) {
   const int64_t jobs = (int64_t)a.bh_count * a.n_blocks;
   if (jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)jobs), block(kThreads);
-  if (a.bits == 2) nuq_quant_values_kernel<2><<<grid, block, 0, s>>>(a);
-  else if (a.bits == 3) nuq_quant_values_kernel<3><<<grid, block, 0, s>>>(a);
-  else nuq_quant_values_kernel<4><<<grid, block, 0, s>>>(a);
+  const bool vout = a.kv > 0;
+  if (a.bits == 2 && vout) nuq_quant_values_kernel<2, true><<<grid, block, 0, s>>>(a);
+  else if (a.bits == 2) nuq_quant_values_kernel<2, false><<<grid, block, 0, s>>>(a);
+  else if (a.bits == 3 && vout) nuq_quant_values_kernel<3, true><<<grid, block, 0, s>>>(a);
+  else if (a.bits == 3) nuq_quant_values_kernel<3, false><<<grid, block, 0, s>>>(a);
+  else if (vout) nuq_quant_values_kernel<4, true><<<grid, block, 0, s>>>(a);
+  else nuq_quant_values_kernel<4, false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
