@@ -92,11 +92,13 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
       st[tid] = make_float2(g.mn, g.inv);
     }
     __syncthreads();
-    // Word wi = t * WK + col holds channels col*CPW .. col*CPW + CPW - 1 of token t.  A
-    // thread keeps one column for all its words, so it reads its channels' (min, 1/scale)
-    // once, and reads each token's CPW fp16 values as 16-byte vectors: the lanes of one
-    // token read a contiguous row (scalar 2-byte reads of the same values conflicted
-    // heavily in the LDS banks).
+    // Word wi = t * WK + col holds channels col*CPW .. col*CPW + CPW - 1 of token t.
+    // 4-bit codes: a thread keeps one column for all its words, so it reads its
+    // channels' (min, 1/scale) once, and reads each token's 8 fp16 values as one 16-byte
+    // vector; the lanes of one token read a contiguous row (per-code 2-byte reads of the
+    // same values conflicted heavily in the LDS banks and took twice as long).  2-bit
+    // codes: one word per thread, per-code reads (measured faster for that layout).
+   if constexpr (KB == 4) {
     const int col = tid % WK;
     const int c0 = col * CPW;
     float gmn[CPW], ginv[CPW];
@@ -122,6 +124,22 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
       }
       a.k_codes[dst * (kGroup * WK) + t * WK + col] = word;
     }
+   } else {
+#pragma unroll
+    for (int i = 0; i < (kGroup * WK) / kThreads; ++i) {
+      const int wi = tid + i * kThreads;
+      const int t = wi / WK;
+      const int c0 = (wi % WK) * CPW;
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const float2 g = st[c0 + j];
+        const uint32_t q = code_of(f16_bits_to_f32(tile[t][c0 + j]), g.x, g.y, L);
+        word |= q << (KB * j);
+      }
+      a.k_codes[dst * (kGroup * WK) + wi] = word;
+    }
+   }
     __syncthreads();
    }
   }
