@@ -2,8 +2,8 @@
 
 Every step of the quantize/append/attention path runs in the library's HIP
 kernels; PyTorch is used for device memory and streams.  Importing this module
-fails loudly if the library has not been built (python -m
-decode_attention_10_amd.build) - there is no fallback.
+fails loudly if the library has not been built (python
+decode_attention_10_amd/build.py) - there is no fallback.
 """
 from __future__ import annotations
 
@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_attention_10_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python decode_attention_10_amd/build.py`")
 
 # torch first: its HIP runtime then satisfies libkvq.so's libamdhip64 dependency (same
 # soname), so the library and torch share one runtime, one device context and the same

@@ -1,6 +1,6 @@
 """Builds the HIP sources into in-tree shared libraries for gfx950.
 
-    python -m decode_attention_10_amd.build        (or build_all() from Python)
+    python decode_attention_10_amd/build.py        (or build_all() from Python)
 
 libkvq.so       <- decode_attention_10_amd/csrc/*.hip   (the C ABI of include/kvq.h)
 libkvq_synth.so <- kvq_synth/synth.hip                 (seeded input generator)

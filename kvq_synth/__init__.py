@@ -235,7 +235,7 @@ def _load_synth():
         import os
         path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq_synth.so")
         if not os.path.exists(path):
-            raise ImportError(f"{path} is missing: run python -m decode_attention_10_amd.build")
+            raise ImportError(f"{path} is missing: run python decode_attention_10_amd/build.py")
         import torch  # noqa: F401  (share torch's HIP runtime, see the binding)
         lib = C.CDLL(path)
         lib.kvq_synth_fill.restype = C.c_int
