@@ -263,13 +263,13 @@ struct NuqBlockRegs {
 template <int B>
 __device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
   if constexpr (B == 3) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    const uint4 y = *reinterpret_cast<const uint4*>(p + 2);
+    const uint2 x = ld_stream2(p);
+    const uint4 y = ld_stream4(p + 2);
     dst[0] = x.x; dst[1] = x.y; dst[2] = y.x; dst[3] = y.y; dst[4] = y.z; dst[5] = y.w;
   } else {
 #pragma unroll
     for (int i = 0; i < B / 2; ++i) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p + 4 * i);
+      const uint4 x = ld_stream4(p + 4 * i);
       dst[4 * i] = x.x; dst[4 * i + 1] = x.y; dst[4 * i + 2] = x.z; dst[4 * i + 3] = x.w;
     }
   }

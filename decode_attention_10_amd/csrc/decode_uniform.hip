@@ -57,7 +57,7 @@ struct HeadPtrs {
 
 // Loads of block `blk` (wave-uniform) of a segment: the block's base address is scalar
 // arithmetic, each lane adds a fixed 32-bit offset.
-template <int KB, int VB>
+template <int KB, int VB, bool NT>
 __device__ __forceinline__ void load_block(BlockRegs<KB, VB>& r, const HeadPtrs& hp, int blk,
                                            int lane) {
   constexpr int WK = kHeadDim * KB / 32;            // words per token row
@@ -65,28 +65,26 @@ __device__ __forceinline__ void load_block(BlockRegs<KB, VB>& r, const HeadPtrs&
   const uint32_t* kp = hp.kc + (uint32_t)blk * (kGroup * WK);
   const uint32_t ka_off = (uint32_t)(tp * WK + q * KB), kb_off = ka_off + 16 * WK;
   if constexpr (KB == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(kp + ka_off);
-    const uint2 y = *reinterpret_cast<const uint2*>(kp + kb_off);
+    const uint2 x = ld_cache2<NT>(kp + ka_off);
+    const uint2 y = ld_cache2<NT>(kp + kb_off);
     r.ka[0] = x.x; r.ka[1] = x.y; r.kb[0] = y.x; r.kb[1] = y.y;
   } else {
-    const uint4 x = *reinterpret_cast<const uint4*>(kp + ka_off);
-    const uint4 y = *reinterpret_cast<const uint4*>(kp + kb_off);
+    const uint4 x = ld_cache4<NT>(kp + ka_off);
+    const uint4 y = ld_cache4<NT>(kp + kb_off);
     r.ka[0] = x.x; r.ka[1] = x.y; r.ka[2] = x.z; r.ka[3] = x.w;
     r.kb[0] = y.x; r.kb[1] = y.y; r.kb[2] = y.z; r.kb[3] = y.w;
   }
-  const uint2 km = *reinterpret_cast<const uint2*>(hp.km + (uint32_t)blk * kHeadDim +
-                                                   (uint32_t)(2 * lane));
+  const uint2 km = ld_cache2<NT>(hp.km + (uint32_t)blk * kHeadDim + (uint32_t)(2 * lane));
   r.km[0] = km.x; r.km[1] = km.y;
-  const uint4* vp = reinterpret_cast<const uint4*>(hp.vc + (uint32_t)blk * (kHeadDim * VB) +
-                                                   (uint32_t)(lane * 2 * VB));
+  const uint32_t* vp = hp.vc + (uint32_t)blk * (kHeadDim * VB) + (uint32_t)(lane * 2 * VB);
 #pragma unroll
   for (int i = 0; i < VB / 2; ++i) {
-    const uint4 u = vp[i];
+    const uint4 u = ld_cache4<NT>(vp + 4 * i);
     r.vc[4 * i] = u.x; r.vc[4 * i + 1] = u.y; r.vc[4 * i + 2] = u.z; r.vc[4 * i + 3] = u.w;
   }
   const uint32_t* vm = hp.vm + (uint32_t)blk * (kGroup * 4);
-  r.vm[0] = vm[(uint32_t)lane];
-  r.vm[1] = vm[(uint32_t)lane + 64];
+  r.vm[0] = ld_cache<NT>(vm + (uint32_t)lane);
+  r.vm[1] = ld_cache<NT>(vm + (uint32_t)lane + 64);
 }
 
 template <int KB, int VB, int GQ>
@@ -161,7 +159,7 @@ __device__ __forceinline__ void process_block(const BlockRegs<KB, VB>& r, WaveSt
 // tokens) is units [n_blocks + kWindowUnits*c, n_blocks + kWindowUnits*(c+1)), weighted
 // by its larger byte count.  A split covers a contiguous unit range: the packed blocks
 // in it and every window chunk whose first unit falls in it.
-template <int KB, int VB, int GQ, int NW>
+template <int KB, int VB, int GQ, int NW, bool NT>
 __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a) {
   constexpr int CPW = 32 / KB;
   __shared__ __align__(16) uint32_t qh[GQ][64];
@@ -215,7 +213,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   // ---- window chunks first (their loads are short), then the packed blocks
   for (int c = c_first; c < c_end; ++c)
     if (NW - 1 - ((c - c_first) % NW) == wave)
-      process_window<GQ, VB>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
+      process_window<GQ, VB, NT>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
   if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
     const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
@@ -227,16 +225,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
     // for the loads just issued.
     const int last = cnt - 1;
     BlockRegs<KB, VB> r0, r1, r2;
-    load_block<KB, VB>(r0, hp, block_of(deal, s0, 0, last, wave), lane);
-    load_block<KB, VB>(r1, hp, block_of(deal, s0, 1, last, wave), lane);
+    load_block<KB, VB, NT>(r0, hp, block_of(deal, s0, 0, last, wave), lane);
+    load_block<KB, VB, NT>(r1, hp, block_of(deal, s0, 1, last, wave), lane);
     for (int k = 0; k < cnt; k += 3) {
-      load_block<KB, VB>(r2, hp, block_of(deal, s0, k + 2, last, wave), lane);
+      load_block<KB, VB, NT>(r2, hp, block_of(deal, s0, k + 2, last, wave), lane);
       process_block<KB, VB, GQ>(r0, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
       if (k + 1 >= cnt) break;
-      load_block<KB, VB>(r0, hp, block_of(deal, s0, k + 3, last, wave), lane);
+      load_block<KB, VB, NT>(r0, hp, block_of(deal, s0, k + 3, last, wave), lane);
       process_block<KB, VB, GQ>(r1, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
       if (k + 2 >= cnt) break;
-      load_block<KB, VB>(r1, hp, block_of(deal, s0, k + 4, last, wave), lane);
+      load_block<KB, VB, NT>(r1, hp, block_of(deal, s0, k + 4, last, wave), lane);
       process_block<KB, VB, GQ>(r2, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
     }
   }
@@ -318,36 +316,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
 
 }  // namespace
 
+// Streaming (nontemporal) cache loads when one workgroup covers each (batch, kv head);
+// plain loads for split plans.  Measured on MI355X: the hint took the one-workgroup-per-
+// head llama2_7b shapes from 26.3 to 25.1 us (27.8 to 27.0 with a 32-token sink), and the
+// 32-splits-per-head llama2_13b shape from 124.0 to 138.9 us.
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
   const int nw = a.waves_per_group;
+  const bool nt = a.splits == 1;
   dim3 grid((unsigned)wgs), block((unsigned)(nw * kWave));
-#define KVQ_DL(KB_, VB_, G_, NW_)                                                   \
-  if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_) {                    \
-    decode_uniform_kernel<KB_, VB_, G_, NW_><<<grid, block, 0, s>>>(a);             \
+#define KVQ_DL(KB_, VB_, G_, NW_, NT_)                                              \
+  if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_ && nt == NT_) {       \
+    decode_uniform_kernel<KB_, VB_, G_, NW_, NT_><<<grid, block, 0, s>>>(a);        \
     hipError_t e_ = hipGetLastError();                                              \
     if (e_ != hipSuccess || a.splits == 1) return e_;                               \
     return launch_merge_splits(a, s);                                               \
   }
-#define KVQ_DLB(G_, NW_) KVQ_DL(2, 2, G_, NW_) KVQ_DL(2, 4, G_, NW_) KVQ_DL(4, 2, G_, NW_) \
-  KVQ_DL(4, 4, G_, NW_)
-  // 2 and 4 query heads per kv head run on the matrix cores (decode_gqa.hip)
-  KVQ_DLB(1, 4) KVQ_DLB(8, 4)
-  KVQ_DLB(1, 8) KVQ_DLB(1, 16)
+#define KVQ_DLB(G_, NW_, NT_) KVQ_DL(2, 2, G_, NW_, NT_) KVQ_DL(2, 4, G_, NW_, NT_) \
+  KVQ_DL(4, 2, G_, NW_, NT_) KVQ_DL(4, 4, G_, NW_, NT_)
+  // 2 and 4 query heads per kv head run on the matrix cores (decode_gqa.hip); split
+  // plans use 4-wave workgroups
+  KVQ_DLB(1, 4, true) KVQ_DLB(8, 4, true)
+  KVQ_DLB(1, 8, true) KVQ_DLB(1, 16, true)
+  KVQ_DLB(1, 4, false) KVQ_DLB(8, 4, false)
 #undef KVQ_DLB
 #undef KVQ_DL
   return hipErrorInvalidValue;
 }
 
+// The kernel a split plan of nw-wave workgroups launches (for occupancy queries).
 const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw) {
-#define KVQ_DF(KB_, VB_, G_, NW_)                                                   \
+#define KVQ_DF(KB_, VB_, G_, NW_, NT_)                                              \
   if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_)                      \
-    return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_>);
-#define KVQ_DFB(G_, NW_) KVQ_DF(2, 2, G_, NW_) KVQ_DF(2, 4, G_, NW_) KVQ_DF(4, 2, G_, NW_) \
-  KVQ_DF(4, 4, G_, NW_)
-  KVQ_DFB(1, 4) KVQ_DFB(8, 4)
-  KVQ_DFB(1, 8) KVQ_DFB(1, 16)
+    return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_, NT_>);
+#define KVQ_DFB(G_, NW_, NT_) KVQ_DF(2, 2, G_, NW_, NT_) KVQ_DF(2, 4, G_, NW_, NT_) \
+  KVQ_DF(4, 2, G_, NW_, NT_) KVQ_DF(4, 4, G_, NW_, NT_)
+  KVQ_DFB(1, 4, false) KVQ_DFB(8, 4, false)
+  KVQ_DFB(1, 8, true) KVQ_DFB(1, 16, true)
 #undef KVQ_DFB
 #undef KVQ_DF
   return nullptr;

@@ -25,6 +25,37 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// Streaming loads: global loads with the nontemporal hint, for data read once per decode
+// (packed codes, metadata, fp16 windows).  Measured on a 117 MB read by one workgroup
+// per CU: 6.5 TB/s with the hint against 5.8 TB/s without.  Pointers must be aligned to
+// the load width.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t ld_stream(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ uint2 ld_stream2(const void* p) {
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint4 ld_stream4(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+// Cache loads with the hint chosen at compile time (NT = true: streaming loads).
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_cache(const uint32_t* p) {
+  if constexpr (NT) return ld_stream(p); else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld_cache2(const void* p) {
+  if constexpr (NT) return ld_stream2(p); else return *reinterpret_cast<const uint2*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_cache4(const void* p) {
+  if constexpr (NT) return ld_stream4(p); else return *reinterpret_cast<const uint4*>(p);
+}
+
 // ---- launch parameter blocks (host fills, kernels read) ----------------------
 struct QuantArgs {
   const uint16_t* k;        // source keys (NULL: skip keys)
