@@ -19,11 +19,11 @@
 // half by an fp32 operand.  The power of two 2^(24 - pos) is folded into the staged
 // q*scale / p*scale values.  Products are exact; sums are fp32.
 //
-// Work split: a workgroup of 4, 8 or 16 waves handles one (batch, kv head) and a
+// Work split: a workgroup of 4 or 8 waves handles one (batch, kv head) and a
 // range of work units (split-K over the context, as in flash-decoding); a wave
 // streams one 32-token block at a time (keys: a lane covers two tokens x 32
-// channels; values: one 8-token x 8-channel tile), with the next two blocks' loads
-// in flight.  Blocks are dealt to the waves in rounds and the fp16 window chunks go
+// channels; values: one 8-token x 8-channel tile), with the next block's loads in
+// flight (the next two in split plans).  Blocks are dealt to the waves in rounds and the fp16 window chunks go
 // to the last waves, which take correspondingly fewer blocks.  Waves merge in LDS.
 // With one split per (batch, kv head) the workgroup writes the output; otherwise it
 // writes a (max, sum, output) partial and a second small launch merges the splits.
@@ -219,23 +219,26 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
     const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
                          a.k_meta + seg * kHeadDim, a.v_codes + seg * (kHeadDim * VB),
                          a.v_meta + seg * (kGroup * 4)};
-    // Two blocks in flight ahead of the one being processed.  The prefetch index is
-    // clamped rather than guarded so every iteration issues the same loads, and the
-    // loop is unrolled by three with rotating roles so no register copy has to wait
-    // for the loads just issued.
+    // PF blocks in flight ahead of the one being processed: one with streaming loads (a
+    // workgroup per head), two otherwise.  The prefetch index is clamped rather than
+    // guarded so every iteration issues the same loads, and the loop is unrolled by PF + 1
+    // with rotating register sets so no register copy has to wait for the loads just
+    // issued.
+    constexpr int PF = NT ? 1 : 2;
+    constexpr int RS = PF + 1;
     const int last = cnt - 1;
-    BlockRegs<KB, VB> r0, r1, r2;
-    load_block<KB, VB, NT>(r0, hp, block_of(deal, s0, 0, last, wave), lane);
-    load_block<KB, VB, NT>(r1, hp, block_of(deal, s0, 1, last, wave), lane);
-    for (int k = 0; k < cnt; k += 3) {
-      load_block<KB, VB, NT>(r2, hp, block_of(deal, s0, k + 2, last, wave), lane);
-      process_block<KB, VB, GQ>(r0, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
-      if (k + 1 >= cnt) break;
-      load_block<KB, VB, NT>(r0, hp, block_of(deal, s0, k + 3, last, wave), lane);
-      process_block<KB, VB, GQ>(r1, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
-      if (k + 2 >= cnt) break;
-      load_block<KB, VB, NT>(r1, hp, block_of(deal, s0, k + 4, last, wave), lane);
-      process_block<KB, VB, GQ>(r2, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
+    BlockRegs<KB, VB> r[RS];
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      load_block<KB, VB, NT>(r[i], hp, block_of(deal, s0, i, last, wave), lane);
+    for (int k = 0; k < cnt; k += RS) {
+#pragma unroll
+      for (int d = 0; d < RS; ++d) {
+        if (k + d >= cnt) break;
+        load_block<KB, VB, NT>(r[(d + PF) % RS], hp, block_of(deal, s0, k + d + PF, last, wave),
+                               lane);
+        process_block<KB, VB, GQ>(r[d], st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
+      }
     }
   }
 
@@ -316,10 +319,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
 
 }  // namespace
 
-// Streaming (nontemporal) cache loads when one workgroup covers each (batch, kv head);
-// plain loads for split plans.  Measured on MI355X: the hint took the one-workgroup-per-
-// head llama2_7b shapes from 26.3 to 25.1 us (27.8 to 27.0 with a 32-token sink), and the
-// 32-splits-per-head llama2_13b shape from 124.0 to 138.9 us.
+// Streaming (nontemporal) cache loads and one block in flight per wave when one workgroup
+// covers each (batch, kv head); plain loads and two blocks in flight for split plans.
+// Measured on MI355X: the hint took the one-workgroup-per-head llama2_7b shapes from 26.3
+// to 25.1 us (27.8 to 27.0 with a 32-token sink), and the 32-splits-per-head llama2_13b
+// shape from 124.0 to 138.9 us; one block in flight instead of two took llama2_7b from
+// 26.2 to 25.7 us and llama2_13b from 124.8 to 125.4 us.
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
@@ -337,8 +342,7 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
   KVQ_DL(4, 2, G_, NW_, NT_) KVQ_DL(4, 4, G_, NW_, NT_)
   // 2 and 4 query heads per kv head run on the matrix cores (decode_gqa.hip); split
   // plans use 4-wave workgroups
-  KVQ_DLB(1, 4, true) KVQ_DLB(8, 4, true)
-  KVQ_DLB(1, 8, true) KVQ_DLB(1, 16, true)
+  KVQ_DLB(1, 4, true) KVQ_DLB(8, 4, true) KVQ_DLB(1, 8, true)
   KVQ_DLB(1, 4, false) KVQ_DLB(8, 4, false)
 #undef KVQ_DLB
 #undef KVQ_DL
@@ -352,8 +356,7 @@ const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw) {
     return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_, NT_>);
 #define KVQ_DFB(G_, NW_, NT_) KVQ_DF(2, 2, G_, NW_, NT_) KVQ_DF(2, 4, G_, NW_, NT_) \
   KVQ_DF(4, 2, G_, NW_, NT_) KVQ_DF(4, 4, G_, NW_, NT_)
-  KVQ_DFB(1, 4, false) KVQ_DFB(8, 4, false)
-  KVQ_DFB(1, 8, true) KVQ_DFB(1, 16, true)
+  KVQ_DFB(1, 4, false) KVQ_DFB(8, 4, false) KVQ_DFB(1, 8, true)
 #undef KVQ_DFB
 #undef KVQ_DF
   return nullptr;

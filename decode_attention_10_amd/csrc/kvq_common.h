@@ -110,7 +110,7 @@ struct DecodeArgs {
   int32_t n_blocks;         // packed blocks (n_packed / 32)
   int32_t n_resid;
   int32_t splits;           // workgroups per (batch, kv head)
-  int32_t waves_per_group;  // 4, 8 or 16
+  int32_t waves_per_group;  // 4 or 8
   float scale_log2;         // sm_scale * log2(e)
 };
 

@@ -127,6 +127,14 @@ DECODE_CASES = [
     (1, 1, 4, 40960, 100, 2, 2, 128),
     (64, 5, 4, 96, 5, 2, 2, 128),
     (48, 6, 2, 64, 31, 2, 4, 128),
+    # one query head per kv head with a workgroup per head (heads >= CUs: 8-wave groups,
+    # streaming loads, one block in flight): every bit pair, a window-only cache and
+    # mostly idle waves
+    (64, 4, 1, 256, 77, 2, 2, 128),
+    (32, 8, 1, 1024, 128, 2, 4, 128),
+    (20, 16, 1, 512, 5, 4, 2, 128),
+    (128, 2, 1, 96, 0, 4, 4, 128),
+    (64, 4, 1, 0, 100, 2, 2, 128),
 ]
 
 
