@@ -40,6 +40,26 @@ def test_binding_without_library_raises(tmp_path):
     assert r.stdout.strip() == "raised True", r.stdout + r.stderr
 
 
+def test_build_entry_compiles_a_tree_without_built_libraries(tmp_path):
+    """build() must compile from sources alone: the package refuses to import without its
+    library, so the build script may not be reached through the package import."""
+    import shutil
+    for d in ("include", "kvq_synth"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(PKG, tmp_path / "decode_attention_10_amd",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    assert not (tmp_path / "decode_attention_10_amd" / "libkvq.so").exists()
+    code = "import sys; sys.path.insert(0, %r); import __graft_entry__ as g; g.build()" % (
+        str(tmp_path))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=900, cwd=str(tmp_path))
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert (tmp_path / "decode_attention_10_amd" / "libkvq.so").exists()
+    assert (tmp_path / "kvq_synth" / "libkvq_synth.so").exists()
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
