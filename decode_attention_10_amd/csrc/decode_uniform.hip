@@ -319,17 +319,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
 
 }  // namespace
 
-// Streaming (nontemporal) cache loads and one block in flight per wave when one workgroup
-// covers each (batch, kv head); plain loads and two blocks in flight for split plans.
-// Measured on MI355X: the hint took the one-workgroup-per-head llama2_7b shapes from 26.3
-// to 25.1 us (27.8 to 27.0 with a 32-token sink), and the 32-splits-per-head llama2_13b
-// shape from 124.0 to 138.9 us; one block in flight instead of two took llama2_7b from
-// 26.2 to 25.7 us and llama2_13b from 124.8 to 125.4 us.
+// Streaming (nontemporal) cache loads and one block in flight per wave for 8-wave
+// workgroups and when one workgroup covers each (batch, kv head); plain loads and two
+// blocks in flight for 4-wave split plans.  Measured on MI355X: the hint took the
+// one-workgroup-per-head llama2_7b shapes from 26.3 to 25.1 us (27.8 to 27.0 with a
+// 32-token sink), but llama2_13b split over 4-wave workgroups from 124.0 to 138.9 us;
+// one block in flight instead of two took llama2_7b from 26.2 to 25.7 us and that
+// llama2_13b plan from 124.8 to 125.4 us.  llama2_13b over 8-wave workgroups with both:
+// 119.0 us.
 hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, int gq,
                                  hipStream_t s) {
   const int64_t wgs = (int64_t)a.batch * a.kv_heads * a.splits;
   const int nw = a.waves_per_group;
-  const bool nt = a.splits == 1;
+  const bool nt = a.splits == 1 || nw == 8;
   dim3 grid((unsigned)wgs), block((unsigned)(nw * kWave));
 #define KVQ_DL(KB_, VB_, G_, NW_, NT_)                                              \
   if (k_bits == KB_ && v_bits == VB_ && gq == G_ && nw == NW_ && nt == NT_) {       \
@@ -341,9 +343,9 @@ hipError_t launch_decode_uniform(const DecodeArgs& a, int k_bits, int v_bits, in
 #define KVQ_DLB(G_, NW_, NT_) KVQ_DL(2, 2, G_, NW_, NT_) KVQ_DL(2, 4, G_, NW_, NT_) \
   KVQ_DL(4, 2, G_, NW_, NT_) KVQ_DL(4, 4, G_, NW_, NT_)
   // 2 and 4 query heads per kv head run on the matrix cores (decode_gqa.hip); split
-  // plans use 4-wave workgroups
+  // plans use 8-wave workgroups for one query head per kv head, 4-wave ones for eight
   KVQ_DLB(1, 4, true) KVQ_DLB(8, 4, true) KVQ_DLB(1, 8, true)
-  KVQ_DLB(1, 4, false) KVQ_DLB(8, 4, false)
+  KVQ_DLB(8, 4, false)
 #undef KVQ_DLB
 #undef KVQ_DL
   return hipErrorInvalidValue;
@@ -356,7 +358,7 @@ const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw) {
     return reinterpret_cast<const void*>(&decode_uniform_kernel<KB_, VB_, G_, NW_, NT_>);
 #define KVQ_DFB(G_, NW_, NT_) KVQ_DF(2, 2, G_, NW_, NT_) KVQ_DF(2, 4, G_, NW_, NT_) \
   KVQ_DF(4, 2, G_, NW_, NT_) KVQ_DF(4, 4, G_, NW_, NT_)
-  KVQ_DFB(1, 4, false) KVQ_DFB(8, 4, false) KVQ_DFB(1, 8, true)
+  KVQ_DFB(1, 4, true) KVQ_DFB(8, 4, false) KVQ_DFB(1, 8, true)
 #undef KVQ_DFB
 #undef KVQ_DF
   return nullptr;
