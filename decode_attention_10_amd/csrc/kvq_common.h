@@ -210,7 +210,7 @@ hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s);
 hipError_t launch_decode_nuq(const DecodeArgs& a, int gq, int bits, hipStream_t s);
 // The kernel a launcher above would run (for occupancy queries); NULL if none.
 const void* decode_uniform_fn(int k_bits, int v_bits, int gq, int nw);
-const void* decode_gqa_fn(int k_bits, int v_bits, int gq);
+const void* decode_gqa_fn(int k_bits, int v_bits, int gq, int nw);
 const void* decode_nuq_fn(int gq, int nw, int bits);
 
 }  // namespace kvq
