@@ -23,8 +23,9 @@
 // range of work units (split-K over the context, as in flash-decoding); a wave
 // streams one 32-token block at a time (keys: a lane covers two tokens x 32
 // channels; values: one 8-token x 8-channel tile), with the next block's loads in
-// flight (the next two in split plans).  Blocks are dealt to the waves in rounds and the fp16 window chunks go
-// to the last waves, which take correspondingly fewer blocks.  Waves merge in LDS.
+// flight (the next two in 4-wave split plans).  Blocks are dealt to the waves in rounds
+// and the fp16 window chunks go to the last waves, which take correspondingly fewer
+// blocks.  Waves merge in LDS.
 // With one split per (batch, kv head) the workgroup writes the output; otherwise it
 // writes a (max, sum, output) partial and a second small launch merges the splits.
 #include "decode_common.h"
