@@ -214,7 +214,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   // ---- window chunks first (their loads are short), then the packed blocks
   for (int c = c_first; c < c_end; ++c)
     if (NW - 1 - ((c - c_first) % NW) == wave)
-      process_window<GQ, VB, NT>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
+      process_window<GQ, VB>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
   if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
     const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
