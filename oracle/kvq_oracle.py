@@ -410,6 +410,18 @@ def nuq_code(xn: np.ndarray, lut_f32: np.ndarray) -> np.ndarray:
     return (c + tie).astype(np.uint8)
 
 
+def exact_moments(x_dense: np.ndarray):
+    """(E[x], E[x^2] - E[x]^2, clamped at 0) of float values in float64, where sum x and
+    sum x^2 are the exact sums rounded once (math.fsum is correctly rounded; x * x of an
+    fp16 value is exact in float64).  The result does not depend on the order of the
+    entries."""
+    x = np.asarray(x_dense, dtype=np.float64)
+    n = x.shape[0]
+    mean = math.fsum(x.tolist()) / n
+    var = max(math.fsum((x * x).tolist()) / n - mean * mean, 0.0)
+    return mean, var
+
+
 def qnorm_params(x_dense: np.ndarray, codes_dense: np.ndarray, lut: np.ndarray,
                  scale_h, min_h):
     """Q-Norm ([KVQ] "Proposed method" and findings: the dequantized distribution is made to
@@ -422,13 +434,15 @@ def qnorm_params(x_dense: np.ndarray, codes_dense: np.ndarray, lut: np.ndarray,
     dequantized ones from the code histogram (level by level, ascending), each level's
     value lut[c] * scale + min in float32.  a = sqrt(var / var_hat) (1 when var_hat is 0),
     b = mean - a * mean_hat; the new metadata are a * scale and a * min + b rounded to
-    float32, then to fp16.  Returns (scale_h', min_h')."""
+    float32, then to fp16.  Returns (scale_h', min_h').
+
+    Reading of the summation (the page fixes no order): sum x and sum x^2 are the exact
+    sums rounded once to float64 (math.fsum; x^2 of an fp16 value is exact in float64),
+    so the result does not depend on the order in which the entries are added."""
     n = x_dense.shape[0]
     if n == 0:
         return scale_h, min_h
-    x = np.asarray(x_dense, dtype=np.float64)
-    mean = x.sum() / n
-    var = max((x * x).sum() / n - mean * mean, 0.0)
+    mean, var = exact_moments(x_dense)
     s, m = f16_to_f32(scale_h), f16_to_f32(min_h)
     levels = (lut * s + m).astype(np.float32).astype(np.float64)
     cnt = np.bincount(np.asarray(codes_dense, dtype=np.int64), minlength=len(lut))

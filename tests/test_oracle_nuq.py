@@ -273,3 +273,52 @@ def test_qnorm_on_keys_and_values_of_a_head():
     r0 = np.abs(h0["k_hat"].std(0) / x.std(0) - 1).mean()
     r1 = np.abs(h1["k_hat"].std(0) / x.std(0) - 1).mean()
     assert r1 < r0 and r1 < 5e-3
+
+
+def _exact_sum(vals) -> float:
+    """The exact rational sum of float values, rounded once to float64 (Fraction -> float
+    is correctly rounded): an independent route to the definition."""
+    from fractions import Fraction
+    return float(sum((Fraction(float(v)) for v in vals), Fraction(0)))
+
+
+def test_exact_moments_are_correctly_rounded_sums():
+    """Q-Norm's sum x and sum x^2 are the exact sums rounded once.  The vector mixes one
+    large value with many fp16 subnormals, so that adding x^2 left to right and numpy's
+    pairwise sum give different float64 results; the oracle must give the exact one."""
+    big = _f16([256.0, -96.0])
+    tiny = np.full(4096, 1, np.uint16)                 # 2^-24 each (smallest subnormal)
+    x_bits = np.concatenate([big, tiny, _f16(np.linspace(-3.0, 3.0, 1001))])
+    x = O.f16_to_f32(x_bits).astype(np.float64)
+    sq = (x * x)
+    seq = 0.0
+    for v in sq.tolist():
+        seq += v
+    exact_sq = _exact_sum(sq.tolist())
+    assert seq != exact_sq                             # the order matters for this vector
+    mean, var = O.exact_moments(O.f16_to_f32(x_bits))
+    n = len(x)
+    assert mean == _exact_sum(x.tolist()) / n
+    assert var == max(exact_sq / n - mean * mean, 0.0)
+
+
+def test_exact_moments_ignore_the_order():
+    """Permuting the entries leaves the moments (and so the Q-Norm metadata) bit for bit
+    unchanged, on vectors whose naive float64 sums of x^2 depend on the order."""
+    rng = np.random.default_rng(77)
+    mags = np.exp2(rng.integers(-24, 15, 5000).astype(np.float64)) * rng.uniform(1, 2, 5000)
+    x_bits = _f16(mags * np.where(rng.random(5000) < 0.5, -1.0, 1.0))
+    x = O.f16_to_f32(x_bits)
+    naive = set()
+    ref = O.exact_moments(x)
+    lut = S.nuq_lut(2)
+    meta0 = O.nuq_quantize_vector(x_bits, lut, 50, qnorm=True)[1:3]
+    for i in range(6):
+        p = rng.permutation(len(x))
+        acc = 0.0
+        for v in (x[p].astype(np.float64) ** 2).tolist():     # left to right
+            acc += v
+        naive.add(acc)
+        assert O.exact_moments(x[p]) == ref
+        assert O.nuq_quantize_vector(x_bits[p], lut, 50, qnorm=True)[1:3] == meta0
+    assert len(naive) > 1                              # a naive sum would not be stable
