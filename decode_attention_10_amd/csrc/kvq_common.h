@@ -149,6 +149,7 @@ __device__ __forceinline__ Fp16Chunk fp16_chunk(const DecodeArgs& a, int64_t bh,
 constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
 constexpr int kMaxSplits = 2048;               // workgroups per (batch, kv head) at most
 constexpr int kNuqChunk = 2048;                // tokens per chunk in the nuq key passes
+constexpr int64_t kMaxCapacityTokens = (int64_t)1 << 28;   // packed tokens per (batch, head)
 
 struct NuqKeysArgs {
   const uint16_t* k;        // keys of token 0: element (b, h, t, d) at b*sb + h*sh + t*st + d
@@ -176,7 +177,8 @@ struct NuqKeysArgs {
   uint32_t* outmask;        // [bh][cap_tokens][4]
   uint32_t* chunk_cnt;      // [bh][nchunks]
   uint32_t* chunk_off;      // [bh][nchunks]
-  double* qn_sum;           // [bh][nchunks][D][2]: sum x, sum x^2 of dense entries (Q-Norm)
+  uint64_t* qn_sum;         // [bh][nchunks][D][4]: exact sum x (128-bit, 2^-24 units) and
+                            // sum x^2 (128-bit, 2^-48 units) of the dense entries (Q-Norm)
   uint32_t* qn_hist;        // [bh][nchunks][D][16]: dense code counts (Q-Norm)
 };
 

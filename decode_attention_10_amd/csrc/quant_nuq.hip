@@ -98,6 +98,84 @@ __device__ __forceinline__ void params_nuq(float mn, float mx, int bits, uint32_
   *meta = (uint32_t)scale_h | ((uint32_t)min_h << 16);
 }
 
+// Exact sums for Q-Norm.  An fp16 value is an integer multiple of 2^-24 with
+// |x| * 2^24 < 2^40, so sum x is an integer in units of 2^-24 and sum x^2 a 128-bit
+// integer in units of 2^-48.  Both are exact in any order of addition and are rounded
+// once to fp64 at the end (nearest, ties to even), which makes the moments independent
+// of how the tokens are split over chunks, lanes and workgroups.
+struct ExactSums {
+  uint64_t x_lo;   // sum of x * 2^24, 128-bit two's complement
+  int64_t x_hi;
+  uint64_t q_lo;   // sum of (x * 2^24)^2, 128-bit unsigned
+  uint64_t q_hi;
+};
+
+__device__ __forceinline__ void exact_zero(ExactSums& s) { s.x_lo = s.q_lo = s.q_hi = 0; s.x_hi = 0; }
+
+// x * 2^24 of the fp16 value with bits h (finite): (1024 + m) << (e - 1), or m if e = 0.
+__device__ __forceinline__ int64_t f16_units(uint32_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  const uint64_t mag = e ? (uint64_t)(m | 1024u) << (e - 1) : (uint64_t)m;
+  return (h & 0x8000u) ? -(int64_t)mag : (int64_t)mag;
+}
+
+__device__ __forceinline__ void exact_add_parts(ExactSums& s, uint64_t xl, int64_t xh,
+                                                uint64_t ql, uint64_t qh) {
+  const uint64_t a = s.x_lo + xl;
+  s.x_hi += xh + (a < s.x_lo ? 1 : 0);
+  s.x_lo = a;
+  const uint64_t b = s.q_lo + ql;
+  s.q_hi += qh + (b < s.q_lo ? 1u : 0u);
+  s.q_lo = b;
+}
+
+// one fp16 value
+__device__ __forceinline__ void exact_add(ExactSums& s, uint32_t h) {
+  const int64_t x = f16_units(h);
+  const uint64_t mag = (uint64_t)(x < 0 ? -x : x);
+  exact_add_parts(s, (uint64_t)x, x < 0 ? -1 : 0, mag * mag, __umul64hi(mag, mag));
+}
+
+__device__ __forceinline__ void exact_merge(ExactSums& s, const ExactSums& o) {
+  exact_add_parts(s, o.x_lo, o.x_hi, o.q_lo, o.q_hi);
+}
+
+// the sums of the lane `mask` apart added in (all lanes of the pattern take part)
+__device__ __forceinline__ void exact_merge_xor(ExactSums& s, int mask) {
+  ExactSums o;
+  o.x_lo = __shfl_xor(s.x_lo, mask);
+  o.x_hi = __shfl_xor(s.x_hi, mask);
+  o.q_lo = __shfl_xor(s.q_lo, mask);
+  o.q_hi = __shfl_xor(s.q_hi, mask);
+  exact_merge(s, o);
+}
+
+// Nearest fp64 (ties to even) of the 128-bit unsigned (hi, lo): the top 64 bits with
+// every lower bit folded into bit 0 (a sticky bit below the 53 kept bits), converted,
+// then scaled by the power of two shifted out.
+__device__ __forceinline__ double u128_to_f64(uint64_t lo, uint64_t hi) {
+  if (hi == 0) return (double)lo;
+  const int lz = __clzll((long long)hi);
+  const int sh = 64 - lz;
+  uint64_t v = lz ? (hi << lz) | (lo >> sh) : hi;
+  const uint64_t rest = lz ? (lo << lz) : lo;
+  v |= rest != 0 ? 1u : 0u;
+  return ldexp((double)v, sh);
+}
+
+// (sum x, sum x^2) in fp64, each the exact sum rounded once.
+__device__ __forceinline__ void exact_to_f64(const ExactSums& s, double* sx, double* sxx) {
+  uint64_t lo = s.x_lo, hi = (uint64_t)s.x_hi;
+  const bool neg = s.x_hi < 0;
+  if (neg) {
+    lo = ~lo + 1u;
+    hi = ~hi + (lo == 0 ? 1u : 0u);
+  }
+  const double m = u128_to_f64(lo, hi);
+  *sx = ldexp(neg ? -m : m, -24);
+  *sxx = ldexp(u128_to_f64(s.q_lo, s.q_hi), -48);
+}
+
 // Q-Norm of one vector ("KVQuant" review, "Proposed method": the dequantized
 // distribution matched to the statistics before quantization): from the dense
 // entries' sum and sum of squares (fp64) and their code histogram, the metadata
@@ -356,7 +434,8 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
   const Mids<B> md = load_mids<B>(a.lut);
-  double qsx = 0.0, qsxx = 0.0;
+  ExactSums qs;
+  exact_zero(qs);
   if (a.qnorm)
     for (int i = tid; i < kHeadDim * 16; i += kThreads) (&qh[0][0])[i] = 0u;
   // per-channel state of this lane's channel (two lanes per channel)
@@ -414,9 +493,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         const int j = 16 * half + jj;
         if (out) atomicOr(&om[j][ch >> 5], 1u << (ch & 31));
         if (a.qnorm && !out) {
-          const double xf = (double)f16_bits_to_f32((uint16_t)x);
-          qsx += xf;
-          qsxx += xf * xf;
+          exact_add(qs, x);
           atomicAdd(&qh[ch][c], 1u);
         }
       }
@@ -442,14 +519,15 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   }
   if (a.qnorm) {
     // the two lanes of a channel combine their sums; the block's atomics on qh are done
-    qsx += __shfl_xor(qsx, 1);
-    qsxx += __shfl_xor(qsxx, 1);
+    exact_merge_xor(qs, 1);
     __syncthreads();
     if ((tid & 1) == 0) {
       const int ch = tid >> 1;
       const int64_t q = (bh * a.nchunks + chunk) * kHeadDim + ch;
-      a.qn_sum[q * 2] = qsx;
-      a.qn_sum[q * 2 + 1] = qsxx;
+      a.qn_sum[q * 4] = qs.x_lo;
+      a.qn_sum[q * 4 + 1] = (uint64_t)qs.x_hi;
+      a.qn_sum[q * 4 + 2] = qs.q_lo;
+      a.qn_sum[q * 4 + 3] = qs.q_hi;
 #pragma unroll
       for (int c = 0; c < 16; ++c) a.qn_hist[q * 16 + c] = qh[ch][c];
     }
@@ -462,20 +540,23 @@ __global__ void nuq_qnorm_keys_kernel(NuqKeysArgs a) {
   if (i >= (int64_t)a.bh_count * kHeadDim) return;
   const int64_t bh = i / kHeadDim;
   const int d = (int)(i % kHeadDim);
-  double sx = 0.0, sxx = 0.0;
+  ExactSums es;
+  exact_zero(es);
   uint32_t hist[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) hist[c] = 0u;
   for (int ch = 0; ch < a.nchunks; ++ch) {
     const int64_t q = (bh * a.nchunks + ch) * kHeadDim + d;
-    sx += a.qn_sum[q * 2];
-    sxx += a.qn_sum[q * 2 + 1];
+    exact_add_parts(es, a.qn_sum[q * 4], (int64_t)a.qn_sum[q * 4 + 1], a.qn_sum[q * 4 + 2],
+                    a.qn_sum[q * 4 + 3]);
 #pragma unroll
     for (int c = 0; c < 16; ++c) hist[c] += a.qn_hist[q * 16 + c];
   }
   uint32_t n = 0;
 #pragma unroll
   for (int c = 0; c < 16; ++c) n += hist[c];
+  double sx, sxx;
+  exact_to_f64(es, &sx, &sxx);
   uint32_t* meta = a.k_meta + bh * kHeadDim + d;
   *meta = qnorm_meta(*meta, sx, sxx, hist, n, a.lut, a.bits);
 }
@@ -731,21 +812,19 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   __syncthreads();
   if (a.qnorm) {
     // Q-Norm: the token's dense sums and code counts, then its metadata again
-    double sx = 0.0, sxx = 0.0;
+    ExactSums es;
+    exact_zero(es);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (!((outm >> j) & 1u)) {
-        const double xf = (double)xv(j);
-        sx += xf;
-        sxx += xf * xf;
+        exact_add(es, (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
         atomicAdd(&qh[t][code[j]], 1u);
       }
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      sx += __shfl_xor(sx, o);
-      sxx += __shfl_xor(sxx, o);
-    }
+    for (int o = 1; o < 8; o <<= 1) exact_merge_xor(es, o);
+    double sx, sxx;
+    exact_to_f64(es, &sx, &sxx);
     __syncthreads();
     if ((tid & 7) == 0) {
       uint32_t n = 0;

@@ -249,3 +249,31 @@ def test_layout_bytes_nuq_widths_and_value_outliers(bits):
     s = K.kvq_layout_bytes(c)
     assert s[K.KVQ_BUF_K_CODES] == s[K.KVQ_BUF_V_CODES] == 2 * 1024 * 128 * bits // 8
     assert s[K.KVQ_BUF_V_OUT] == 2 * 1024 * 2 * 4          # 2 outliers per 128-channel token
+
+
+def test_capacity_and_csr_limits():
+    """The decode kernels form 32-bit word offsets within a head (block index times at most
+    512 words) and the CSR row pointers are int32: capacity_tokens is capped at 2^28 and a
+    head's outlier entries at 2^31 - 1, both rejected on the host."""
+    c = _desc(B=1, H=1, cap=1 << 28, R=0)
+    K.kvq_layout_bytes(c)                                  # the largest capacity is valid
+    c.capacity_tokens = (1 << 28) + 32
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_layout_bytes(c)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    c = _desc(B=1, H=1, cap=1024, R=0)
+    c.csr_capacity = 1 << 31
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_layout_bytes(c)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    # nuq keys: 128 channels x ceil(2^28 * 700 / 1e4) outliers per head > 2^31 - 1
+    c = _desc(kind=K.KVQ_NUQ, kb=3, vb=3, B=1, H=1, cap=1 << 28, R=0)
+    c.kq.outlier_bp = 700
+    c.csr_capacity = (1 << 31) - 1
+    _fake_buffers(c)
+    c.k_csr_rowptr = FAKE + 0x900000
+    c.k_csr_ent = FAKE + 0xA00000
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_quantize_keys(c, FAKE, 0, 0, 128, 0, 1 << 28, FAKE, 1 << 40, stream=0)
+    assert e.value.status == K.KVQ_ERR_CAPACITY
+    assert "int32" in K.kvq_last_error()
