@@ -48,7 +48,9 @@
  *    a = sqrt(var / var_hat) (1 if var_hat = 0) and b = mean - a * mean_hat, so
  *    that the dequantized dense entries get the mean and variance of the original
  *    ones; each result rounded to fp32, then fp16.  mean and var of the original
- *    dense entries in fp64 (E[x^2] - E[x]^2); mean_hat and var_hat from the code
+ *    dense entries in fp64 (E[x^2] - E[x]^2), where sum x and sum x^2 are the
+ *    exact sums rounded once to fp64 (independent of the order of addition);
+ *    mean_hat and var_hat from the code
  *    histogram, level values lut[c] * scale + min in fp32, summed in fp64 over c
  *    ascending.  Codes are unchanged.
  *  - Value outliers (nuq values, outlier_bp > 0): per (batch, head, token) the
@@ -174,7 +176,7 @@ typedef struct {
   int32_t kv_heads;        /* >= 1 */
   int32_t head_dim;        /* 128 on the GPU (the layouts allow any multiple of 32) */
   int32_t residual_len;    /* fp16 window R: 0 or a multiple of 32, <= 1024 */
-  int64_t capacity_tokens; /* packed capacity, a multiple of 32 */
+  int64_t capacity_tokens; /* packed capacity, a multiple of 32, <= 2^28 */
   kvq_qparams kq, vq;
   void* k_codes;           /* device buffers, sizes from kvq_layout_bytes */
   void* k_meta;
@@ -184,7 +186,8 @@ typedef struct {
   uint16_t* v_resid;
   int32_t* k_csr_rowptr;   /* NUQ keys with outlier_bp > 0, else NULL */
   uint32_t* k_csr_ent;
-  int64_t csr_capacity;    /* entries per (batch, head) segment of k_csr_ent */
+  int64_t csr_capacity;    /* entries per (batch, head) segment of k_csr_ent, < 2^31
+                              (the row pointers are int32) */
   uint32_t* v_out;         /* NUQ values with vq.outlier_bp > 0, else NULL */
   int64_t n_packed;        /* tokens in the packed part (multiple of 32) */
   int32_t n_resid;         /* tokens in the window, 0..residual_len */
@@ -197,24 +200,30 @@ typedef struct {
   int32_t reserved;        /* 0 */
 } kvq_cache;
 
-/* Bytes of each buffer slot for the descriptor's shape and settings (0 for slots
+/* Passage: the bit budgets of KIVI "Experiments" (2-bit codes, group 32, fp zero
+ * point) and of the KVQuant review's results table (KV-cache size per width).
+ * Bytes of each buffer slot for the descriptor's shape and settings (0 for slots
  * the settings do not use).  Reads no pointer.  The CSR entry slot is sized for
  * c->csr_capacity entries per head. */
 kvq_status kvq_layout_bytes(const kvq_cache* c, size_t sizes_out[KVQ_NUM_BUFS]);
 
-/* Smallest csr_capacity that holds the outliers of a full cache:
+/* Passage: KVQuant review, abstract item (iv) (per-vector dense-and-sparse, 1 %).
+ * Smallest csr_capacity that holds the outliers of a full cache:
  * head_dim * ceil(capacity_tokens * outlier_bp / 10000); 0 without outliers, -1
  * for an invalid descriptor. */
 int64_t kvq_csr_entries_needed(const kvq_cache* c);
 
-/* Device scratch bytes that `op` needs for this descriptor (decode: for any
+/* No passage: the split-K partials and the nuq select passes are this library's
+ * design.  Device scratch bytes that `op` needs for this descriptor (decode: for any
  * n_packed <= capacity_tokens and n_resid <= residual_len; q_heads is ignored by
  * the quantize op).  The decode workspace holds per-split partial results; its
  * contents need no initialization and are overwritten by every call.  Returns 0
  * if the op needs none or on invalid input. */
 size_t kvq_workspace_bytes(const kvq_cache* c, int32_t q_heads, int32_t op);
 
-/* Quantize keys of tokens [token_offset, token_offset + n_tokens) into the packed
+/* Passage: KIVI "Method" and "The KV cache has a geometry problem", section on keys
+ * (keys per channel); KVQuant review, abstract items (i)-(iv) for NUQ.
+ * Quantize keys of tokens [token_offset, token_offset + n_tokens) into the packed
  * part (k_codes, k_meta and, for NUQ, the CSR).  k points at the key of token
  * token_offset: element (b, h, t, d) is k[b*stride_b + h*stride_h + t*stride_t + d]
  * (fp16, channels contiguous).  UNIFORM: offset and count are multiples of 32,
@@ -226,13 +235,18 @@ kvq_status kvq_quantize_keys(const kvq_cache* c, const uint16_t* k, int64_t stri
                              int64_t n_tokens, void* workspace, size_t ws_bytes,
                              void* stream);
 
-/* Quantize values of tokens [token_offset, token_offset + n_tokens) into v_codes and
+/* Passage: KIVI "Method" and "The KV cache has a geometry problem", section on values
+ * (values per token); KVQuant review, abstract items (iii)-(iv) for NUQ.
+ * Quantize values of tokens [token_offset, token_offset + n_tokens) into v_codes and
  * v_meta; arguments as for kvq_quantize_keys (no workspace). */
 kvq_status kvq_quantize_values(const kvq_cache* c, const uint16_t* v, int64_t stride_b,
                                int64_t stride_h, int64_t stride_t, int64_t token_offset,
                                int64_t n_tokens, void* stream);
 
-/* Append one token per (batch, kv head): k_new, v_new are fp16 [batch][kv_heads][D],
+/* Passage: KIVI "Method" (the newest tokens, up to 128, stay in full precision and are
+ * quantized together when the window fills); "The KV cache has a geometry problem",
+ * section "The systems tax".
+ * Append one token per (batch, kv head): k_new, v_new are fp16 [batch][kv_heads][D],
  * contiguous.  While the sink has room (n_sink < sink_len) the token goes to sink
  * slot n_sink and n_sink += 1; nothing else changes.  Otherwise, if the window is
  * full (n_resid == residual_len) it is first
@@ -247,7 +261,10 @@ kvq_status kvq_quantize_values(const kvq_cache* c, const uint16_t* v, int64_t st
 kvq_status kvq_append_flush(kvq_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                             void* stream);
 
-/* Decode attention of one query token per (batch, query head) over the whole
+/* Passage: "The KV cache has a geometry problem", section "Why the KV cache is a
+ * problem" (each generated token reads the whole cache) and its section on rotary
+ * embeddings with KVQuant review abstract item (ii) (RoPE after dequantization).
+ * Decode attention of one query token per (batch, query head) over the whole
  * cache: q fp16 [batch][q_heads][D], out fp32 [batch][q_heads][D], both contiguous.
  * q_heads is a multiple of kv_heads (at most 8 query heads per kv head).
  * rope_theta: 0 = no rotation; > 0 (NUQ caches only) rotates key t at position t.
@@ -258,7 +275,8 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const uint16_t* q, int32_t q_head
                            float sm_scale, float rope_theta, float* out, void* workspace,
                            size_t ws_bytes, void* stream);
 
-/* Message for the calling thread's last non-OK status ("" if none). */
+/* No passage (error reporting).  Message for the calling thread's last non-OK status
+ * ("" if none). */
 const char* kvq_last_error(void);
 
 #ifdef __cplusplus

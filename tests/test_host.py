@@ -84,3 +84,18 @@ def test_algorithmic_bytes_match_the_configs():
         assert round(got[n] / unit, digits) == value, n
     # per-unit figure used for the roofline: 459,520 B per (batch, kv head) of llama2_7b
     assert got["llama2_7b"] == 256 * 459520          # q and out shares included per unit
+
+
+def test_bench_cpu_baseline_legs_run_the_oracle():
+    """The bench's oracle legs: worker processes from a fork server, 1 and 2 workers on the
+    tiny workload, each reporting decode and quantize rates in GB/s and its core count."""
+    import multiprocessing as mp
+    sys.path.insert(0, ROOT)
+    import bench
+    ctx = mp.get_context("forkserver")
+    for workers in (1, 2):
+        r = bench.finish_cpu_leg(bench.start_cpu_leg(ctx, "tiny", workers, 0.5), "tiny",
+                                 timeout_s=240)
+        assert r["cores"] == workers and r["unit_runs"] >= workers
+        assert r["decode_gbs"] > 0 and r["quantize_gbs"] > 0
+        assert "tiny" in r["sample"]
