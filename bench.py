@@ -25,7 +25,8 @@ bracketed by device synchronizations: ms_per_step = wall / steps.
 
 value / decode GB/s: algorithmic bytes of one decode (codes, metadata, CSR, fp16 window
 and sink, q, out) / mean decode time, from HIP events on the launch stream around each
-of >= 10 replays of a decode-only graph; p10 / p50 / p90 of the per-replay means.
+of >= 10 replays of a decode-only graph (each >= 64 decodes over the rotating layer
+copies; 4 decodes for kvquant_1m); p10 / p50 / p90 of the per-replay means.
 quantize GB/s: fp16 K/V read + everything written, over the whole context.
 
 cpu_baseline: the oracle (oracle/kvq_oracle.py, unchanged) timed on the host on a bounded
@@ -63,6 +64,7 @@ HEADLINE = "kvquant_1m"
 MIN_ROTATION_BYTES = 768e6
 MAX_LAYERS = 256
 MIN_DECODE_REPLAYS = 10
+MIN_DECODES_PER_REPLAY = 64
 NUQ_CPU_TOKENS = 65536      # oracle sample of a 1M-token head: its first 65,536 tokens
 
 
@@ -222,7 +224,7 @@ def _cpu_nuq_unit(w, k, v, q):
     s, m = (O.f16_to_f32(x) for x in O.unpack_meta(pk[1]))
     kd = lut[O.unpack_nuq(pk[0], w.k_bits)] * s[None, :] + m[None, :]
     rows = np.repeat(np.arange(n), np.diff(rp))
-    kd[rows, (ent & 0xFFFF).astype(np.int64)] = O.f16_to_f32((ent >> 16).astype(np.uint16))
+    kd[rows, (ent & 0xFF).astype(np.int64)] = O.f16_to_f32((ent >> 16).astype(np.uint16))
     s, m = (O.f16_to_f32(x) for x in O.unpack_meta(pv[1]))
     vd = lut[O.unpack_nuq(pv[0], w.v_bits)] * s[:, None] + m[:, None]
     kr = O.rope_f64(kd, np.arange(n), w.rope_theta)
@@ -354,14 +356,16 @@ class LayerArena:
     per buffer slot (device memory plumbing only)."""
 
     def __init__(self, K, template, layers: int, device):
-        import copy
+        import ctypes
 
         import torch
         sizes = K.kvq_layout_bytes(template)
         names = ["k_codes", "k_meta", "v_codes", "v_meta", "k_resid", "v_resid",
                  "k_csr_rowptr", "k_csr_ent", "k_sink", "v_sink", "v_out"]
         self.layers, self.slots = layers, {}
-        descs = [copy.copy(template) for _ in range(layers)]
+        descs = [K.kvq_cache() for _ in range(layers)]
+        for d in descs:
+            ctypes.memmove(ctypes.byref(d), ctypes.byref(template), ctypes.sizeof(template))
         for i, n in enumerate(names):
             if not sizes[i]:
                 continue
@@ -467,17 +471,19 @@ def gpu_uniform(w, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     cap_stream = torch.cuda.Stream()
     step_graph, dec_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    # a decode-only replay goes over every layer copy `rounds` times (>= 64 decodes)
+    rounds = max(1, math.ceil(MIN_DECODES_PER_REPLAY / layers))
     with torch.cuda.stream(cap_stream):
         with torch.cuda.graph(step_graph, stream=cap_stream):
             nbytes = [step(i) for i in range(steps)]
         with torch.cuda.graph(dec_graph, stream=cap_stream):
-            for c in arena.descs:
-                K.kvq_decode_attn(c, q, Hq, sm, 0.0, out, ws, ws_bytes)
+            for _ in range(rounds):
+                for c in arena.descs:
+                    K.kvq_decode_attn(c, q, Hq, sm, 0.0, out, ws, ws_bytes)
     torch.cuda.synchronize()
     wall, dev_s = timed_steps(step_graph, steps, stream)
-    replays = max(MIN_DECODE_REPLAYS, math.ceil(200 / layers))
     dec_graph.replay()
-    mean_dec_s, pct = time_replays(dec_graph, replays, layers, stream)
+    mean_dec_s, pct = time_replays(dec_graph, MIN_DECODE_REPLAYS, rounds * layers, stream)
     dec_bytes = decode_bytes(w, N, w.n_resid)
     gbs = dec_bytes / mean_dec_s / 1e9
     kern = uniform_decode_kernel(w)
@@ -491,7 +497,8 @@ def gpu_uniform(w, steps: int, warmup: int) -> dict:
         "step_bytes_mean": int(np.mean(nbytes)), "flushes_in_timed_steps": (steps + R - 1) // R,
         "decode_us": round(mean_dec_s * 1e6, 3),
         "decode_us_p10_p50_p90": [round(x * 1e6, 3) for x in pct],
-        "decode_replays": replays, "decodes_per_replay": layers, "layers_rotated": layers,
+        "decode_replays": MIN_DECODE_REPLAYS, "decodes_per_replay": rounds * layers,
+        "layers_rotated": layers,
         "decode_gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_ctx_per_s": round(B * T / mean_dec_s, 1),
         "quantize_gbs": round(quant_gbs, 1), "quantize_ms_prefill": round(quant_ms, 4),
@@ -557,7 +564,7 @@ def gpu_nuq(w, steps: int, warmup: int) -> dict:
     for _ in range(max(warmup, 1)):
         decode()
     torch.cuda.synchronize()
-    per_replay = 2
+    per_replay = 4
     step_graph, dec_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     cap_stream = torch.cuda.Stream()
     with torch.cuda.stream(cap_stream):

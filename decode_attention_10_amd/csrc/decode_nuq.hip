@@ -6,13 +6,16 @@
 // Key t (position t) after dequantization: k~_d = lut[c_td] * s_d + m_d, or the exact
 // fp16 value at an outlier.  With RoPE on interleaved pairs, q . R(t) k~ is
 //   sum_i Re(a_i(t)) k~_2i + Im(a_i(t)) k~_2i+1,   a_i(t) = (q_2i + i q_2i+1) e^(-i t th_i)
-// so one lane owns a channel pair i, keeps a_i for the current token and advances it
-// by e^(-i th_i) per token (a complex product); each block restarts it from an angle
-// t0 * th_i reduced modulo 2 pi in fp64.  Per-pair partial scores of the block's 32
-// tokens are then summed across lanes (lanes 2t and 2t+1 end with token t).
+// so one lane owns a channel pair i.  Each block starts from a_i(t0) = q e^(-i t0 th_i),
+// where e^(-i t0 th_i) is carried from block to block in fp64 (one complex product by
+// e^(-i 32 th_i) per block, started from an angle reduced modulo 2 pi at the wave's
+// first block); inside the block four independent chains (tokens 0, 8, 16, 24 on)
+// advance by e^(-i th_i) per token.  Per-pair partial scores of the block's 32 tokens
+// are then summed across lanes (lanes 2t and 2t+1 end with token t).
 // Outliers: the dense pass uses the stored code everywhere; one lane per CSR entry
-// then computes a_col(t) * (x - dequant(code)) and token t adds its row's
-// corrections in row order.
+// (which carries its token's place in the block) then computes
+// a_col(t) * (x - dequant(code)), and the two lanes of token t add their row's
+// corrections, every other entry each, in row order.
 //
 // Values: one lane per channel pair as well; o_d += (p_t * s_t) * lut[c_td] plus the
 // per-token minimum term sum_t p_t m_t, identical for every channel; each token's
@@ -98,6 +101,13 @@ __device__ __forceinline__ uint32_t codes4_3(const uint32_t* w, int m) {
   return ((w[m >> 2] >> (2 * (m & 3))) & 0x03030303u) | (hs & 0x04040404u);
 }
 
+// codes of tokens 4m..4m+3 (one per byte) for any width
+template <int B>
+__device__ __forceinline__ uint32_t codes_of(const uint32_t* w, int m) {
+  if constexpr (B == 3) return codes4_3(w, m);
+  else return codes4<B>(w, m);
+}
+
 template <int B>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
   if constexpr (B == 4) {
@@ -116,25 +126,31 @@ __device__ __forceinline__ float lut_value(const uint16_t* lut, uint32_t c) {
   return f16_bits_to_f32(lut[c]);
 }
 
-// e^(-i phi) for phi = t * theta reduced modulo 2 pi in fp64 (Cody-Waite: 2 pi as a
-// 24-bit head, so that k * head is exact for the k < 2^29 of any position below 2^31,
-// plus a tail; the reduced angle lies in [-pi, pi]).
+// e^(-i phi) in fp64 for phi = t * theta reduced modulo 2 pi in fp64 (Cody-Waite: 2 pi
+// as a 24-bit head, so that k * head is exact for the k < 2^29 of any position below
+// 2^31, plus a tail; the reduced angle lies in [-pi, pi]).
 constexpr double kTwoPiHi = 0x1.921fb4p+2;
 constexpr double kTwoPiLo = 0x1.4442d18469899p-22;
 constexpr double kInvTwoPi = 0x1.45f306dc9c883p-3;
 
-__device__ __forceinline__ float2 rot_at(int64_t t, double theta) {
-  const double x = (double)t * theta;
-  const double k = rint(x * kInvTwoPi);
-  const double ph = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x));
-  float s, c;
-  sincosf((float)ph, &s, &c);
-  return make_float2(c, -s);
-}
-
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
 }
+
+__device__ __forceinline__ double2 rot_at64(int64_t t, double theta) {
+  const double x = (double)t * theta;
+  const double k = rint(x * kInvTwoPi);
+  const double ph = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, x));
+  double s, c;
+  sincos(ph, &s, &c);
+  return make_double2(c, -s);
+}
+
+__device__ __forceinline__ double2 cmul64(double2 a, double2 b) {
+  return make_double2(fma(a.x, b.x, -(a.y * b.y)), fma(a.x, b.y, a.y * b.x));
+}
+
+__device__ __forceinline__ float2 to_f32(double2 a) { return make_float2((float)a.x, (float)a.y); }
 
 __device__ __forceinline__ float sum32(float x) {
 #pragma unroll
@@ -217,9 +233,28 @@ __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float
 struct PairConsts {
   float2 q[8];        // (q_2i, q_2i+1) per query head
   float2 step;        // e^(-i theta_i)
+  float2 r8, r16, r24;        // e^(-i 8 theta_i), e^(-i 16 theta_i), e^(-i 24 theta_i)
+  double2 step32;     // e^(-i 32 theta_i): from one block to the next
   double theta;       // theta_i
   float ks0, km0, ks1, km1;   // key scale / min of channels 2i, 2i+1
 };
+
+// The block's partial scores of this lane's pair for one head: four chains of eight
+// tokens (from tokens 0, 8, 16, 24), each advanced by e^(-i theta) per token, so that
+// no product waits on more than seven others.
+__device__ __forceinline__ void pair_scores(float (&part)[32], float2 qb, const PairConsts& pc,
+                                            const float (&k0)[32], const float (&k1)[32]) {
+  float2 c[4] = {qb, cmul(qb, pc.r8), cmul(qb, pc.r16), cmul(qb, pc.r24)};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) part[8 * m + k] = fmaf(c[m].x, k0[8 * m + k], c[m].y * k1[8 * m + k]);
+    if (k < 7) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) c[m] = cmul(c[m], pc.step);
+    }
+  }
+}
 
 // Softmax over the block's scores and the value accumulation shared by packed blocks
 // and window chunks: s[] holds this lane's token (lane >> 1) score per head (log2
@@ -246,7 +281,6 @@ struct NuqWaveScratch {
   float2 qb[GQ][64];         // q e^(-i t0 theta_i) per head and pair: the block's first token
   uint32_t kc[kHeadDim][B];  // the block's key (later value) code words, per channel
   float corr[GQ][64];        // per CSR entry of the window: its score correction
-  uint8_t tok[64];           // per CSR entry of the window: its token in the block
   float pv[GQ][kGroup];      // p_t of the block's tokens (value outliers)
   uint32_t vmeta[kGroup];    // value scale / min of the block's tokens
   float vcorr[GQ][kHeadDim]; // value-outlier corrections of the block, per channel
@@ -294,7 +328,7 @@ __device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const DecodeA
 
 template <int GQ, int B>
 __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
-                                  const NuqBlockRegs<B>& r, const PairConsts& pc,
+                                  const NuqBlockRegs<B>& r, const PairConsts& pc, float2 base,
                                   const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
                                   const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
@@ -318,48 +352,68 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
 
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
-  float kd0[32], kd1[32];
-#pragma unroll
-  for (int m4 = 0; m4 < 8; ++m4) {
-    uint32_t a01, a23, b01, b23;
-    if constexpr (B == 3) {
-      lut4<B>(lk, codes4_3(kw0, m4), a01, a23);
-      lut4<B>(lk, codes4_3(kw1, m4), b01, b23);
-    } else {
-      lut4<B>(lk, codes4<B>(kw0, m4), a01, a23);
-      lut4<B>(lk, codes4<B>(kw1, m4), b01, b23);
-    }
-    kd0[4 * m4 + 0] = fmaf(lo_f16(a01), pc.ks0, pc.km0);
-    kd0[4 * m4 + 1] = fmaf(hi_f16(a01), pc.ks0, pc.km0);
-    kd0[4 * m4 + 2] = fmaf(lo_f16(a23), pc.ks0, pc.km0);
-    kd0[4 * m4 + 3] = fmaf(hi_f16(a23), pc.ks0, pc.km0);
-    kd1[4 * m4 + 0] = fmaf(lo_f16(b01), pc.ks1, pc.km1);
-    kd1[4 * m4 + 1] = fmaf(hi_f16(b01), pc.ks1, pc.km1);
-    kd1[4 * m4 + 2] = fmaf(lo_f16(b23), pc.ks1, pc.km1);
-    kd1[4 * m4 + 3] = fmaf(hi_f16(b23), pc.ks1, pc.km1);
-  }
-  const float2 base = rot_at(t0, pc.theta);
   float s[GQ];
   float2 qb[GQ];
-#pragma unroll
-  for (int j = 0; j < GQ; ++j) {
+  if constexpr (GQ == 1) {
+    // one head: the lookups of each chain step are used at once (16 live values, not 64)
     float part[32];
-    qb[j] = cmul(pc.q[j], base);
-    float2 ar = qb[j];
+    qb[0] = cmul(pc.q[0], base);
+    float2 c[4] = {qb[0], cmul(qb[0], pc.r8), cmul(qb[0], pc.r16), cmul(qb[0], pc.r24)};
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      part[k] = fmaf(ar.x, kd0[k], ar.y * kd1[k]);
-      ar = cmul(ar, pc.step);
+    for (int h = 0; h < 2; ++h) {                    // tokens 4h..4h+3 of every chain
+      uint32_t a[4][2], b[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        lut4<B>(lk, codes_of<B>(kw0, 2 * m + h), a[m][0], a[m][1]);
+        lut4<B>(lk, codes_of<B>(kw1, 2 * m + h), b[m][0], b[m][1]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t wa = a[m][kk >> 1], wb = b[m][kk >> 1];
+          const float x0 = fmaf((kk & 1) ? hi_f16(wa) : lo_f16(wa), pc.ks0, pc.km0);
+          const float x1 = fmaf((kk & 1) ? hi_f16(wb) : lo_f16(wb), pc.ks1, pc.km1);
+          part[8 * m + 4 * h + kk] = fmaf(c[m].x, x0, c[m].y * x1);
+        }
+        if (4 * h + kk < 7) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) c[m] = cmul(c[m], pc.step);
+        }
+      }
     }
-    s[j] = transpose_sum32(part, lane);
+    s[0] = transpose_sum32(part, lane);
+  } else {
+    float kd0[32], kd1[32];
+#pragma unroll
+    for (int m4 = 0; m4 < 8; ++m4) {
+      uint32_t a01, a23, b01, b23;
+      lut4<B>(lk, codes_of<B>(kw0, m4), a01, a23);
+      lut4<B>(lk, codes_of<B>(kw1, m4), b01, b23);
+      kd0[4 * m4 + 0] = fmaf(lo_f16(a01), pc.ks0, pc.km0);
+      kd0[4 * m4 + 1] = fmaf(hi_f16(a01), pc.ks0, pc.km0);
+      kd0[4 * m4 + 2] = fmaf(lo_f16(a23), pc.ks0, pc.km0);
+      kd0[4 * m4 + 3] = fmaf(hi_f16(a23), pc.ks0, pc.km0);
+      kd1[4 * m4 + 0] = fmaf(lo_f16(b01), pc.ks1, pc.km1);
+      kd1[4 * m4 + 1] = fmaf(hi_f16(b01), pc.ks1, pc.km1);
+      kd1[4 * m4 + 2] = fmaf(lo_f16(b23), pc.ks1, pc.km1);
+      kd1[4 * m4 + 3] = fmaf(hi_f16(b23), pc.ks1, pc.km1);
+    }
+#pragma unroll
+    for (int j = 0; j < GQ; ++j) {
+      float part[32];
+      qb[j] = cmul(pc.q[j], base);
+      pair_scores(part, qb[j], pc, kd0, kd1);
+      s[j] = transpose_sum32(part, lane);
+    }
   }
 
   // ---- outliers: token t's CSR entries replace the dequantized code by the exact value.
-  // Entries are taken in windows of 64, one per lane: the lanes of each token mark its
-  // row's slots with the token, every entry lane computes its correction
-  // comp(q e^(-i (t0 + t) theta)) * (x - dequant(code)) (the real part for an even
-  // channel, the imaginary part for an odd one), and the lanes of token t add their
-  // row's corrections in row order.
+  // Entries are taken in windows of 64, one per lane: every entry lane computes its
+  // correction comp(q e^(-i (t0 + te) theta)) * (x - dequant(code)) (the real part for an
+  // even channel, the imaginary part for an odd one; te is the token's place in the
+  // block, stored in the entry), and the two lanes of token t add the corrections of its
+  // row, every other entry each in row order, then exchange their sums.
   if (e_begin < e_end) {
 #pragma unroll
     for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
@@ -368,16 +422,13 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
       ws.kc[2 * lane][i] = kw0[i];
       ws.kc[2 * lane + 1][i] = kw1[i];
     }
+    __builtin_amdgcn_wave_barrier();
     for (int64_t w0 = e_begin; w0 < e_end; w0 += 64) {
       const bool has = w0 + lane < e_end;
       uint32_t ent = ent_first;
       if (w0 != e_begin) ent = has ? a.csr_ent[bh * a.csr_capacity + w0 + lane] : 0u;
-      const int64_t lo = max((int64_t)r.r0, w0), hi = min((int64_t)r.r1, min(e_end, w0 + 64));
-      if (!(lane & 1))
-        for (int64_t e = lo; e < hi; ++e) ws.tok[e - w0] = (uint8_t)t;
-      __builtin_amdgcn_wave_barrier();
       if (has) {
-        const int te = ws.tok[lane] & (kGroup - 1);
+        const int te = (int)((ent >> 8) & (kGroup - 1));
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
@@ -393,10 +444,17 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
         }
       }
       __builtin_amdgcn_wave_barrier();
-      for (int64_t e = lo; e < hi; ++e) {
+      const int lo = (int)(max((int64_t)r.r0, w0) - w0);
+      const int hi = (int)(min((int64_t)r.r1, min(e_end, w0 + 64)) - w0);
+      float acc[GQ];
 #pragma unroll
-        for (int j = 0; j < GQ; ++j) s[j] += ws.corr[j][e - w0];
+      for (int j = 0; j < GQ; ++j) acc[j] = 0.f;
+      for (int e = lo + (lane & 1); e < hi; e += 2) {
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) acc[j] += ws.corr[j][e];
       }
+#pragma unroll
+      for (int j = 0; j < GQ; ++j) s[j] += acc[j] + dpp<0xB1>(0.f, acc[j]);
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -494,17 +552,18 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
 #pragma unroll
   for (int k = 0; k < 32; ++k)
     kv[k] = *reinterpret_cast<const uint32_t*>(kr + min(k, nvalid - 1) * kHeadDim);
-  const float2 base = rot_at(pos0, pc.theta);
+  const float2 base = to_f32(rot_at64(pos0, pc.theta));
+  float k0[32], k1[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    k0[k] = lo_f16(kv[k]);
+    k1[k] = hi_f16(kv[k]);
+  }
   float s[GQ], p[GQ], alpha[GQ];
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
     float part[32];
-    float2 ar = cmul(pc.q[j], base);
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      part[k] = fmaf(ar.x, lo_f16(kv[k]), ar.y * hi_f16(kv[k]));
-      ar = cmul(ar, pc.step);
-    }
+    pair_scores(part, cmul(pc.q[j], base), pc, k0, k1);
     s[j] = transpose_sum32(part, lane) * a.scale_log2;
     if (t >= nvalid) s[j] = kNegInf;
   }
@@ -533,7 +592,7 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
 }
 
 template <int GQ, int NW, int B>
-__global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel(DecodeArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ NuqShared<GQ> sh;
   __shared__ __align__(16) NuqWaveScratch<GQ, B> wsc[NW];
@@ -556,10 +615,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     pc.q[j] = make_float2(lo_f16(qq), hi_f16(qq));
   }
   pc.theta = a.rope_theta > 0.f ? pow((double)a.rope_theta, -2.0 * lane / kHeadDim) : 0.0;
-  {
-    const float2 r1 = rot_at(1, pc.theta);
-    pc.step = r1;
-  }
+  pc.step = to_f32(rot_at64(1, pc.theta));
+  pc.r8 = to_f32(rot_at64(8, pc.theta));
+  pc.r16 = to_f32(rot_at64(16, pc.theta));
+  pc.r24 = to_f32(rot_at64(24, pc.theta));
+  pc.step32 = rot_at64(kGroup, pc.theta);
   if (a.n_blocks > 0) {
     const uint2 km = *reinterpret_cast<const uint2*>(a.k_meta + bh * kHeadDim + 2 * lane);
     pc.ks0 = lo_f16(km.x); pc.km0 = hi_f16(km.x);
@@ -569,7 +629,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
   }
   const Lut<B> lk = load_lut<B>(a.lut_k);
   const Lut<B> lv = load_lut<B>(a.lut_v);
-  for (int j = wave; j < kGroup; j += NW) sh.rot[j][lane] = rot_at(j, pc.theta);
+  for (int j = wave; j < kGroup; j += NW) sh.rot[j][lane] = to_f32(rot_at64(j, pc.theta));
   if (wave == 0) {
     sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
     sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
@@ -605,14 +665,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_nuq_kernel(DecodeArgs a) {
     const int last = b1 - 1;
     NuqBlockRegs<B> r0, r1;
     load_nuq_block<B>(r0, a, bh, b0, lane);
+    // e^(-i t0 theta) of the current block, in fp64 from block to block
+    double2 base = rot_at64(a.n_sink + (int64_t)b0 * kGroup, pc.theta);
     for (int i = b0; i < b1; i += 2) {
       load_nuq_block<B>(r1, a, bh, min(i + 1, last), lane);
-      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, lk, lv, st, sh, wsc[wave],
-                            lane);
+      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, to_f32(base), lk,
+                               lv, st, sh, wsc[wave], lane);
+      base = cmul64(base, pc.step32);
       if (i + 1 >= b1) break;
       load_nuq_block<B>(r0, a, bh, min(i + 2, last), lane);
-      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, lk, lv, st, sh,
-                            wsc[wave], lane);
+      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, to_f32(base),
+                               lk, lv, st, sh, wsc[wave], lane);
+      base = cmul64(base, pc.step32);
     }
   }
 

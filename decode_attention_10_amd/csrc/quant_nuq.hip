@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void csr_scan_kernel(NuqKeysArgs a) {
   a.rowptr[bh * (a.cap_tokens + 1) + a.n_tokens] = (int32_t)run;
 }
 
-// Row pointers and entries of one chunk (entries: channel | fp16 value << 16).
+// Row pointers and entries of one chunk (entries: channel | token % 32 << 8 | fp16 << 16).
 __global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
   constexpr int PER = kNuqChunk / kThreads;   // consecutive tokens per thread
   __shared__ uint32_t scan[kThreads];
@@ -638,7 +638,8 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
       while (bits) {
         const int d = 32 * w + __builtin_ctz(bits);
         bits &= bits - 1;
-        if (pos < a.csr_capacity) ent[pos] = (uint32_t)d | ((uint32_t)row[d] << 16);
+        if (pos < a.csr_capacity)
+          ent[pos] = (uint32_t)d | ((uint32_t)(t & (kGroup - 1)) << 8) | ((uint32_t)row[d] << 16);
         ++pos;
       }
     }

@@ -94,8 +94,9 @@
  *    k_meta  [batch][kv_heads][D] words (one scale/min per channel).
  *    k_csr_rowptr [batch][kv_heads][capacity_tokens + 1] int32, rows = tokens,
  *      offsets relative to the head's segment of k_csr_ent;
- *    k_csr_ent [batch][kv_heads][csr_capacity] uint32: channel in bits 0..15,
- *      fp16 value in bits 16..31, channels ascending within a row.
+ *    k_csr_ent [batch][kv_heads][csr_capacity] uint32: channel in bits 0..7, the
+ *      row's token modulo 32 (its place in its 32-token block) in bits 8..12, fp16
+ *      value in bits 16..31, channels ascending within a row.
  *  NUQ value outliers: v_out [batch][kv_heads][capacity_tokens][kv] uint32,
  *      entries as for the keys, channels ascending (a CSR whose rows all hold kv).
  *  NUQ values (per token over all D channels):

@@ -497,8 +497,9 @@ def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int,
     """Keys of one head [N][D]: per channel over the whole context, with outliers.
 
     Returns codes [N][D], scale/min [D], CSR (row_ptr int32 [N+1], entries uint32: column in
-    bits 0..15 and the fp16 value in bits 16..31, rows = tokens, columns ascending), and
-    the dequantized keys x_hat float32 [N][D] (pre-RoPE)."""
+    bits 0..7, the row's token modulo 32 (its place in its 32-token block) in bits 8..12 and
+    the fp16 value in bits 16..31, rows = tokens, columns ascending), and the dequantized
+    keys x_hat float32 [N][D] (pre-RoPE)."""
     n, d = k_bits.shape
     k = outlier_count(n, outlier_bp)
     codes = np.zeros((n, d), np.uint8)
@@ -514,7 +515,8 @@ def nuq_quantize_keys(k_bits: np.ndarray, lut_bits: np.ndarray, outlier_bp: int,
     row_ptr = np.zeros(n + 1, np.int32)
     row_ptr[1:] = np.cumsum(counts)
     tt, cc = np.nonzero(is_out)                   # row-major: tokens, then channels ascending
-    ent = cc.astype(np.uint32) | (k_bits[tt, cc].astype(np.uint32) << np.uint32(16))
+    ent = (cc.astype(np.uint32) | ((tt % GROUP).astype(np.uint32) << np.uint32(8))
+           | (k_bits[tt, cc].astype(np.uint32) << np.uint32(16)))
     return codes, scale, mins, row_ptr, ent.astype(np.uint32), xhat
 
 

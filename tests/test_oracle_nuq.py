@@ -88,10 +88,11 @@ def test_outlier_invariants_keys(bp):
     codes, sc, mn, rp, ent, xh = O.nuq_quantize_keys(k, lut, bp)
     kk = O.outlier_count(N, bp)
     assert rp[0] == 0 and rp[-1] == D * kk and np.all(np.diff(rp) >= 0)
-    cols = (ent & 0xFFFF).astype(np.int64)
+    cols = (ent & 0xFF).astype(np.int64)
     vals = (ent >> 16).astype(np.uint16)
     rows = np.repeat(np.arange(N), np.diff(rp))
     assert np.array_equal(vals, k[rows, cols])                  # exact fp16 values
+    assert np.array_equal((ent >> 8) & 0xFF, rows % 32)         # token within its block
     for t in range(N):                                          # columns ascending per row
         seg = cols[rp[t]:rp[t + 1]]
         assert np.all(np.diff(seg) > 0)
