@@ -69,6 +69,8 @@ _sig = {
     "kvq_append_flush": (C.c_int, [_P, C.c_void_p, C.c_void_p, C.c_void_p]),
     "kvq_decode_attn": (C.c_int, [_P, C.c_void_p, C.c_int32, C.c_float, C.c_float, C.c_void_p,
                                   C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kvq_decode_attn_noalloc": (C.c_int, [_P, C.c_void_p, C.c_int32, C.c_float, C.c_float,
+                                          C.c_void_p, C.c_void_p]),
     "kvq_last_error": (C.c_char_p, []),
 }
 for _n, (_r, _a) in _sig.items():
@@ -149,6 +151,12 @@ def kvq_decode_attn(c: kvq_cache, q, q_heads: int, sm_scale: float, rope_theta: 
                     workspace=None, ws_bytes: int = 0, stream=None) -> None:
     _check(_lib.kvq_decode_attn(C.byref(c), _ptr(q), q_heads, sm_scale, rope_theta, _ptr(out),
                                 _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def kvq_decode_attn_noalloc(c: kvq_cache, q, q_heads: int, sm_scale: float,
+                            rope_theta: float, out, stream=None) -> None:
+    _check(_lib.kvq_decode_attn_noalloc(C.byref(c), _ptr(q), q_heads, sm_scale, rope_theta,
+                                        _ptr(out), _stream(stream)))
 
 
 # ---- device-memory plumbing --------------------------------------------------------

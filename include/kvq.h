@@ -276,6 +276,20 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const uint16_t* q, int32_t q_head
                            float sm_scale, float rope_theta, float* out, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): kvq_decode_attn without a workspace.
+ * The split partials go to a file-scope device array of the library, 8 MiB per GPU (a
+ * copy on every GPU the library runs on, held until the process ends); its address is
+ * taken once per device, on the first call there.  Arguments, results and errors as for
+ * kvq_decode_attn, plus KVQ_ERR_CAPACITY when the decode's split plan needs more than
+ * 8 MiB of partials (batch * q_heads * splits * 528 bytes; such a call changes nothing).
+ * Calls on one GPU share the array: calls that overlap in time on one GPU (different
+ * streams, or host threads without ordering) race and may return wrong results.  The
+ * array needs no initialization: every split writes its partial before the merge reads
+ * it.  Allocates nothing and calls no allocating routine. */
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* c, const uint16_t* q, int32_t q_heads,
+                                   float sm_scale, float rope_theta, float* out, void* stream);
+
 /* No passage (error reporting).  Message for the calling thread's last non-OK status
  * ("" if none). */
 const char* kvq_last_error(void);
