@@ -20,8 +20,9 @@ of one allocation per buffer, > 768 MB in all, at most 256 copies) so that the d
 streams its cache from HBM rather than the 256 MB Infinity Cache; each layer's counters
 are restored after its step.  A step of kvquant_1m is one decode over the one-shot
 quantized context (quantize is timed separately).  Exactly --steps steps are captured in
-one HIP graph and replayed once in the timed region (after --warmup eager steps),
-bracketed by device synchronizations: ms_per_step = wall / steps.
+one HIP graph and replayed once in the timed region (after --warmup eager steps and one
+untimed replay that uploads the graph), bracketed by device synchronizations:
+ms_per_step = wall / steps.
 
 value / decode GB/s: algorithmic bytes of one decode (codes, metadata, CSR, fp16 window
 and sink, q, out) / mean decode time, from HIP events on the launch stream around each
@@ -336,11 +337,16 @@ def time_replays(graph, replays: int, per_replay: int, stream):
     return mean, [float(np.percentile(per, p)) for p in (10, 50, 90)]
 
 
-def timed_steps(graph, steps: int, stream):
+def timed_steps(graph, steps: int, stream, restore=None):
     """The timed region: one replay of the ``steps``-step graph between two device
-    synchronizations.  Returns (wall seconds, device seconds from events)."""
+    synchronizations, after one untimed replay (the graph's first launch uploads it) and
+    ``restore`` (which puts back any state the untimed replay changed).  Returns (wall
+    seconds, device seconds from events)."""
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph.replay()
+    if restore is not None:
+        restore()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)

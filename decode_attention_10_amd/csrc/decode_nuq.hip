@@ -93,12 +93,12 @@ __device__ __forceinline__ uint32_t codes4(const uint32_t* w, int m) {
   }
 }
 
-// codes4 for nuq3 with the high bits moved straight to bit 2 of each byte by one shift
-// (right by m - 2, or left by 2 - m: m is a constant of the unrolled loop) and merged by
-// one AND-OR.
+// codes4 for nuq3 (m is a constant of the unrolled loops): for m < 6 one shift and one
+// mask of word m / 2; for m = 6, 7 the low bits from bits 6..7 of each byte of word
+// m - 6 and the high bit from bit m of each byte of word 2, merged by one AND-OR.
 __device__ __forceinline__ uint32_t codes4_3(const uint32_t* w, int m) {
-  const uint32_t hs = m >= 2 ? (w[2] >> (m - 2)) : (w[2] << (2 - m));
-  return ((w[m >> 2] >> (2 * (m & 3))) & 0x03030303u) | (hs & 0x04040404u);
+  if (m < 6) return (w[m >> 1] >> (3 * (m & 1))) & 0x07070707u;
+  return ((w[m - 6] >> 6) & 0x03030303u) | ((w[2] >> (m - 2)) & 0x04040404u);
 }
 
 // codes of tokens 4m..4m+3 (one per byte) for any width
@@ -113,12 +113,13 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
   if constexpr (B == 4) {
     const int jj = j & 7;
     return (w[j >> 3] >> (8 * (jj & 3) + 4 * (jj >> 2))) & 15u;
-  } else {
+  } else if constexpr (B == 2) {
     const int jj = j & 15;
-    const uint32_t lo = (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
-    if constexpr (B == 2) return lo;
-    const uint32_t hi = (w[2] >> (8 * (j & 3) + (j >> 2))) & 1u;
-    return lo | (hi << 2);
+    return (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
+  } else {
+    const int k = j & 3, m = j >> 2;
+    if (m < 6) return (w[m >> 1] >> (8 * k + 3 * (m & 1))) & 7u;
+    return ((w[m - 6] >> (8 * k + 6)) & 3u) | (((w[2] >> (8 * k + m)) & 1u) << 2);
   }
 }
 

@@ -401,10 +401,12 @@ __global__ void nuq_finalize_kernel(NuqKeysArgs a) {
   a.norm[i * 2 + 1] = inv;
 }
 
-// Pack one channel's 32 codes (LDS tile [token][channel] of bytes) into word w of the
-// channel's B words (B = 2: words 0/1 hold tokens 0..15 / 16..31 at 8*(j%4) + 2*(j/4);
-// B = 3: the same for the low two bits, word 2 the high bits at 8*(j%4) + j/4; B = 4:
-// word w holds tokens 8w..8w+7 at 8*(j%4) + 4*(j/4)).
+// Word w of one channel's B code words of a block from the codes ct[token][channel]:
+// token j in byte j % 4 of its words (B = 2: words 0/1 hold tokens 0..15 / 16..31 at
+// 8*(j%4) + 2*(j%16/4); B = 4: word w holds tokens 8w..8w+7 at 8*(j%4) + 4*(j%8/4);
+// B = 3, m = j / 4: for m < 6 the code at 8*(j%4) + 3*(m%2) of word m/2, for m = 6, 7
+// the low two bits at 8*(j%4) + 6 of word m - 6 and the high bit at 8*(j%4) + m of
+// word 2).
 __device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim], int d, int w,
                                                   int bits_per_code) {
   uint32_t bits = 0;
@@ -412,14 +414,22 @@ __device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim],
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       bits |= (uint32_t)(ct[8 * w + j][d] & 15u) << (8 * (j & 3) + 4 * (j >> 2));
-  } else if (w < 2) {
+  } else if (bits_per_code == 2) {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       bits |= (uint32_t)(ct[16 * w + j][d] & 3u) << (8 * (j & 3) + 2 * (j >> 2));
   } else {
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      bits |= (uint32_t)(ct[j][d] >> 2) << (8 * (j & 3) + (j >> 2));
+    for (int k = 0; k < 4; ++k) {
+      // whole codes of m = 2w, 2w + 1
+      bits |= (uint32_t)(ct[8 * w + k][d] & 7u) << (8 * k);
+      bits |= (uint32_t)(ct[8 * w + 4 + k][d] & 7u) << (8 * k + 3);
+      if (w < 2) bits |= (uint32_t)(ct[24 + 4 * w + k][d] & 3u) << (8 * k + 6);   // m = 6 + w
+      else {
+        bits |= (uint32_t)(ct[24 + k][d] >> 2) << (8 * k + 6);                     // m = 6
+        bits |= (uint32_t)(ct[28 + k][d] >> 2) << (8 * k + 7);                     // m = 7
+      }
+    }
   }
   return bits;
 }
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
       }
       const uint32_t other_ties = __shfl_xor(my_ties, 1);
       uint32_t r = crank + (half ? other_ties : 0u);
-      uint32_t lo = 0u, hi = 0u, w4[2] = {0u, 0u};
+      uint32_t lo = 0u, w4[2] = {0u, 0u}, w3[3] = {0u, 0u, 0u};
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const uint32_t x = xs[jj];
@@ -486,9 +496,20 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         // the bit positions of pack_nuq_word for token j = 16 * half + jj
         if constexpr (B == 4) {
           w4[jj >> 3] |= (c & 15u) << (8 * (jj & 3) + 4 * ((jj & 7) >> 2));
-        } else {
+        } else if constexpr (B == 2) {
           lo |= (c & 3u) << (8 * (jj & 3) + 2 * (jj >> 2));
-          if constexpr (B == 3) hi |= (c >> 2) << (8 * (jj & 3) + (jj >> 2));
+        } else {
+          // m = 4 * half + jj / 4: half 0 fills words 0 and 1 (m = 0..3); half 1 fills word
+          // 2 (m = 4, 5) and the m = 6, 7 fields split over words 0 / 1 and 2
+          const int k = jj & 3, mm = jj >> 2;
+          if (half == 0) {
+            w3[mm >> 1] |= c << (8 * k + 3 * (mm & 1));
+          } else if (mm < 2) {
+            w3[2] |= c << (8 * k + 3 * mm);
+          } else {
+            w3[mm - 2] |= (c & 3u) << (8 * k + 6);
+            w3[2] |= (c >> 2) << (8 * k + 4 + mm);
+          }
         }
         const int j = 16 * half + jj;
         if (out) atomicOr(&om[j][ch >> 5], 1u << (ch & 31));
@@ -502,13 +523,19 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
       if constexpr (B == 4) {
         kw[2 * half] = w4[0];
         kw[2 * half + 1] = w4[1];
-      } else {
+      } else if constexpr (B == 2) {
         kw[half] = lo;
-        if constexpr (B == 3) {
-          // high bits of token 16 * half + jj sit at 8 * (jj & 3) + 4 * half + (jj >> 2)
-          const uint32_t h = hi << (4 * half);
-          const uint32_t both = h | __shfl_xor(h, 1);
-          if (half == 0) kw[2] = both;
+      } else {
+        // the two halves' fields are disjoint: OR them, half 0 writes words 0 and 1,
+        // half 1 word 2
+        const uint32_t x0 = w3[0] | __shfl_xor(w3[0], 1);
+        const uint32_t x1 = w3[1] | __shfl_xor(w3[1], 1);
+        const uint32_t x2 = w3[2] | __shfl_xor(w3[2], 1);
+        if (half == 0) {
+          kw[0] = x0;
+          kw[1] = x1;
+        } else {
+          kw[2] = x2;
         }
       }
     }

@@ -222,38 +222,30 @@ def unpack_v_codes(words: np.ndarray, bits: int) -> np.ndarray:
     return c.reshape(*lead, nb * GROUP, d).astype(np.uint8)
 
 
-def nuq3_bit_positions():
-    """Bit positions (word, low bit) of token j's code in a channel's three 3-bit-code words.
-
-    Word 0 holds the low two bits of tokens 0..15, word 1 those of tokens 16..31: token
-    j of the half sits at bit 8*(j % 4) + 2*(j // 4).  Word 2 holds the high bits of all
-    32 tokens: token j at bit 8*(j % 4) + j // 4.  (So a shift and one mask bring four
-    consecutive tokens' bits into the four bytes of a word.)"""
-    lo = [(j // 16, 8 * ((j % 16) % 4) + 2 * ((j % 16) // 4)) for j in range(32)]
-    hi = [(2, 8 * (j % 4) + j // 4) for j in range(32)]
-    return lo, hi
-
-
 def nuq_code_fields(bits: int):
     """Where token j's code lives in a channel's ``bits`` words of a 32-token block: a list
-    per token of (word, bit position, field width, first code bit) pieces.
+    per token of (word, bit position, field width, first code bit) pieces.  Token j sits in
+    byte j % 4 of its words, so that the codes of four consecutive tokens 4m..4m+3 come
+    out of a word as the four bytes of one shifted and masked word.
 
-    nuq2: words 0 and 1 as the low words of nuq3 (token j of its half at bit
-    8*(j % 4) + 2*(j // 4)).  nuq3: those two plus word 2 for the high bits.  nuq4: word i
-    holds tokens 8i..8i+7, token j of its octet at bit 8*(j % 4) + 4*(j // 4).  In every
-    width a shift and one mask bring four consecutive tokens' fields into the four bytes
-    of a word."""
+    nuq2: words 0 and 1 hold tokens 0..15 / 16..31, token j of its half at bit
+    8*(j % 4) + 2*(j % 16 // 4).  nuq3 (tokens 4m..4m+3, m = j // 4): for m < 6 the whole
+    3-bit code at bit 8*(j % 4) + 3*(m % 2) of word m // 2; for m = 6 and 7 the low two
+    bits at bit 8*(j % 4) + 6 of word m - 6 and the high bit at bit 8*(j % 4) + m of word
+    2.  nuq4: word i holds tokens 8i..8i+7, token j of its octet at bit
+    8*(j % 4) + 4*(j % 8 // 4)."""
     fields = []
     for j in range(GROUP):
+        k, m = j % 4, j // 4
         if bits == 4:
-            jj = j % 8
-            fields.append([(j // 8, 8 * (jj % 4) + 4 * (jj // 4), 4, 0)])
-            continue
-        jj = j % 16
-        f = [(j // 16, 8 * (jj % 4) + 2 * (jj // 4), 2, 0)]
-        if bits == 3:
-            f.append((2, 8 * (j % 4) + j // 4, 1, 2))
-        fields.append(f)
+            fields.append([(j // 8, 8 * k + 4 * ((j % 8) // 4), 4, 0)])
+        elif bits == 3:
+            if m < 6:
+                fields.append([(m // 2, 8 * k + 3 * (m % 2), 3, 0)])
+            else:
+                fields.append([(m - 6, 8 * k + 6, 2, 0), (2, 8 * k + m, 1, 2)])
+        else:
+            fields.append([(j // 16, 8 * k + 2 * ((j % 16) // 4), 2, 0)])
     return fields
 
 

@@ -54,23 +54,28 @@ def test_nuq3_pack_round_trip():
 
 def test_nuq3_layout_bit_positions_by_hand():
     c = np.zeros((32, 128), np.uint8)
-    c[0, 3] = 7          # token 0: word 0 bits 0-1 (=3), word 2 bit 0
-    c[5, 3] = 2          # token 5: byte 1, bits 8+2 = 10..11 of word 0
-    c[21, 3] = 5         # token 21 (16 + 5): word 1 bits 10..11 (=1); high bit: byte 1, bit 5 -> 13
-    c[31, 4] = 4         # token 31: high bit only, byte 3, bit 7 -> bit 31 of word 2
+    c[0, 3] = 7          # token 0 (m 0, byte 0): word 0 bits 0..2
+    c[5, 3] = 2          # token 5 (m 1, byte 1): word 0 bits 8 + 3 = 11..13
+    c[21, 3] = 5         # token 21 (m 5, byte 1): word 2 bits 8 + 3 = 11..13
+    c[25, 3] = 6         # token 25 (m 6, byte 1): low bits 2 at word 0 bits 14..15,
+                         #   high bit at word 2 bit 8 + 6 = 14
+    c[31, 4] = 4         # token 31 (m 7, byte 3): high bit only, word 2 bit 24 + 7 = 31
     w = O.pack_nuq3(c)[0]
-    assert int(w[3, 0]) == 0x3 | (2 << 10)
-    assert int(w[3, 1]) == (1 << 10)
-    assert int(w[3, 2]) == 1 | (1 << 13)
+    assert int(w[3, 0]) == 7 | (2 << 11) | (2 << 14)
+    assert int(w[3, 1]) == 0
+    assert int(w[3, 2]) == (5 << 11) | (1 << 14)
     assert int(w[4, 2]) == 1 << 31 and int(w[4, 0]) == 0 and int(w[4, 1]) == 0
-    # one shift and mask give four consecutive tokens' low bits in the four bytes
+    # one shift and one mask give four consecutive tokens' codes in the four bytes (m < 6);
+    # m = 6, 7 take their low bits from words 0 / 1 and their high bit from word 2
     rng = np.random.default_rng(4)
     cc = rng.integers(0, 8, (32, 128)).astype(np.uint8)
     ww = O.pack_nuq3(cc)[0]
     for m in range(8):
-        lo = (int(ww[9, m // 4]) >> (2 * (m % 4))) & 0x03030303
-        hi = (int(ww[9, 2]) >> m) & 0x01010101
-        codes = lo | (hi << 2)
+        w0, w1, w2 = (int(x) for x in ww[9])
+        if m < 6:
+            codes = ((w0, w1, w2)[m // 2] >> (3 * (m % 2))) & 0x07070707
+        else:
+            codes = (((w0, w1)[m - 6] >> 6) & 0x03030303) | ((w2 >> (m - 2)) & 0x04040404)
         assert [(codes >> (8 * k)) & 0xFF for k in range(4)] == list(cc[4 * m:4 * m + 4, 9])
 
 
