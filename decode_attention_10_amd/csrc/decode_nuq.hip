@@ -19,7 +19,9 @@
 //
 // Values: one lane per channel pair as well; o_d += (p_t * s_t) * lut[c_td] plus the
 // per-token minimum term sum_t p_t m_t, identical for every channel; each token's
-// value outliers (if any) add p_t * (x - dequant(code)) to their channels.
+// value outliers (if any) add p_t * (x - dequant(code)) to their channels.  The weights
+// p_t * s_t enter as fp16 (scaled by a per-wave power of two that keeps them below 2^15)
+// in fp16 dot products with fp32 accumulation, two tokens per instruction.
 // Code-book lookups: four codes in the four bytes of a word select bytes of the fp16
 // table with v_perm_b32 (4 or 8 entries in one source pair; 16 entries in two).
 // Code widths B = 2, 3, 4 (kernel template); sink and window tokens are fp16 chunks.
@@ -213,9 +215,14 @@ __device__ __forceinline__ float transpose_sum32(float (&v)[32], int lane) {
   return v[0] + dpp<0xB1>(0.f, v[0]);          // quad_perm [1,0,3,2]
 }
 
+// Running state of a wave.  The value sums o are kept scaled by 2^-e (per head): the
+// packed blocks' weights p_t * scale_t enter the fp16 dot products as p_t * scale_t * 2^-e,
+// with e raised (and o rescaled) whenever a weight would reach 2^15, so no weight
+// overflows fp16 and the largest keep 11 significant bits.
 template <int GQ>
 struct NuqState {
   float m[GQ], l[GQ], o[GQ][2], mv[GQ];
+  int e[GQ];
 };
 
 __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float& alpha) {
@@ -278,7 +285,8 @@ struct NuqShared {
 // Per-wave scratch (LDS).
 template <int GQ, int B>
 struct NuqWaveScratch {
-  float ps[GQ][kGroup];      // p_t * scale_t of the block's tokens
+  float ps[GQ][kGroup];      // window chunks: p_t of the chunk's tokens (scaled by 2^-e)
+  uint16_t psh[GQ][kGroup];  // packed blocks: fp16 p_t * scale_t * 2^-e of the block's tokens
   float2 qb[GQ][64];         // q e^(-i t0 theta_i) per head and pair: the block's first token
   uint32_t kc[kHeadDim][B];  // the block's key (later value) code words, per channel
   float corr[GQ][64];        // per CSR entry of the window: its score correction
@@ -466,32 +474,48 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   for (int j = 0; j < GQ; ++j) s[j] *= a.scale_log2;
   softmax_block<GQ>(st, s, p, alpha);
 
-  // ---- values: p * scale per token into LDS, p * min per lane
+  // ---- values: fp16 weights p * scale * 2^-e per token into LDS, p * min per lane
   const float vs = lo_f16(r.vmeta), vm = hi_f16(r.vmeta);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    ws.ps[j][t] = p[j] * vs;
+    const float w = p[j] * vs;
+    float wsc = ldexpf(w, -st.e[j]);
+    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
+    if (__any(wsc >= 32768.0f)) {
+      // a weight would reach 2^15: raise e so that the block's largest weight lands in
+      // [2^14, 2^15), and rescale the sums (powers of two: exact)
+      int x;
+      (void)frexpf(wave_max(w), &x);
+      const int e1 = x - 15;
+      o0 = ldexpf(o0, st.e[j] - e1);
+      o1 = ldexpf(o1, st.e[j] - e1);
+      st.e[j] = e1;
+      wsc = ldexpf(w, -e1);
+    }
+    ws.psh[j][t] = __builtin_bit_cast(uint16_t, (_Float16)wsc);
     st.mv[j] = fmaf(p[j], vm, st.mv[j] * alpha[j]);     // every token counted twice
+    st.o[j][0] = o0;
+    st.o[j][1] = o1;
   }
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    float o0 = st.o[j][0] * alpha[j], o1 = st.o[j][1] * alpha[j];
-    const float4* pp = reinterpret_cast<const float4*>(&ws.ps[j][0]);
+    float o0 = st.o[j][0], o1 = st.o[j][1];
+    const uint4* pp = reinterpret_cast<const uint4*>(&ws.psh[j][0]);
 #pragma unroll
-    for (int m4 = 0; m4 < 8; ++m4) {
-      const float4 w4 = pp[m4];
-      uint32_t a01, a23, b01, b23;
-      if constexpr (B == 3) {
-        lut4<B>(lv, codes4_3(vw0, m4), a01, a23);
-        lut4<B>(lv, codes4_3(vw1, m4), b01, b23);
-      } else {
-        lut4<B>(lv, codes4<B>(vw0, m4), a01, a23);
-        lut4<B>(lv, codes4<B>(vw1, m4), b01, b23);
+    for (int i = 0; i < 4; ++i) {                // tokens 8i..8i+7
+      const uint4 w8 = pp[i];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {              // tokens 4m4..4m4+3, m4 = 2i + h
+        const int m4 = 2 * i + h;
+        const uint32_t w01 = h ? w8.z : w8.x, w23 = h ? w8.w : w8.y;
+        uint32_t a01, a23, b01, b23;
+        lut4<B>(lv, codes_of<B>(vw0, m4), a01, a23);
+        lut4<B>(lv, codes_of<B>(vw1, m4), b01, b23);
+        o0 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(a01), o0, false);
+        o0 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(a23), o0, false);
+        o1 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(b01), o1, false);
+        o1 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(b23), o1, false);
       }
-      o0 = fmaf(w4.x, lo_f16(a01), o0); o0 = fmaf(w4.y, hi_f16(a01), o0);
-      o0 = fmaf(w4.z, lo_f16(a23), o0); o0 = fmaf(w4.w, hi_f16(a23), o0);
-      o1 = fmaf(w4.x, lo_f16(b01), o1); o1 = fmaf(w4.y, hi_f16(b01), o1);
-      o1 = fmaf(w4.z, lo_f16(b23), o1); o1 = fmaf(w4.w, hi_f16(b23), o1);
     }
     st.o[j][0] = o0;
     st.o[j][1] = o1;
@@ -530,8 +554,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
 #pragma unroll
     for (int j = 0; j < GQ; ++j) {
       const float2 cv = *reinterpret_cast<const float2*>(&ws.vcorr[j][2 * lane]);
-      st.o[j][0] += cv.x;
-      st.o[j][1] += cv.y;
+      st.o[j][0] += ldexpf(cv.x, -st.e[j]);
+      st.o[j][1] += ldexpf(cv.y, -st.e[j]);
       *reinterpret_cast<float2*>(&ws.vcorr[j][2 * lane]) = make_float2(0.f, 0.f);
     }
     __builtin_amdgcn_wave_barrier();
@@ -571,7 +595,7 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
   softmax_block<GQ>(st, s, p, alpha);
 #pragma unroll
   for (int j = 0; j < GQ; ++j) {
-    psL[j][t] = p[j];
+    psL[j][t] = ldexpf(p[j], -st.e[j]);      // the sums are kept scaled by 2^-e
     st.mv[j] *= alpha[j];
   }
   uint32_t vv[32];
@@ -646,6 +670,7 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
     st.l[j] = 0.f;
     st.o[j][0] = st.o[j][1] = 0.f;
     st.mv[j] = 0.f;
+    st.e[j] = -24;
     *reinterpret_cast<float2*>(&wsc[wave].vcorr[j][2 * lane]) = make_float2(0.f, 0.f);
   }
 
@@ -692,7 +717,7 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
       wl[wave][j] = ltall;
     }
     *reinterpret_cast<float2*>(&wo[wave][j][2 * lane]) =
-        make_float2(st.o[j][0] + mvall, st.o[j][1] + mvall);
+        make_float2(ldexpf(st.o[j][0], st.e[j]) + mvall, ldexpf(st.o[j][1], st.e[j]) + mvall);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < GQ * kHeadDim; idx += NT) {
