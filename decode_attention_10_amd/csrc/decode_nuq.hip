@@ -229,11 +229,12 @@ __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float
   alpha = 1.0f;
   if (__any(s > m + 8.0f)) {               // the max may lag by 8 (log2): p < 2^8
     const float mn = fmaxf(m, wave_max(s));
-    alpha = exp2f(m - mn);
+    alpha = __builtin_amdgcn_exp2f(m - mn);   // v_exp_f32: 0 while m = -inf
     m = mn;
     l *= alpha;
   }
-  const float p = exp2f(s - m);
+  // s - m <= 8; results below 2^-126 flush to 0, a weight no output can feel
+  const float p = __builtin_amdgcn_exp2f(s - m);
   l += p;
   return p;
 }

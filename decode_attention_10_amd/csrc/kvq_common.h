@@ -174,7 +174,6 @@ struct NuqKeysArgs {
   float* norm;              // [bh][D][2]: min, 1/scale
   uint32_t* chunk_stats;    // [bh][nchunks][D][8]
   uint32_t* tie_prefix;     // [bh][nchunks][D]
-  uint32_t* outmask;        // [bh][cap_tokens][4]
   uint32_t* chunk_cnt;      // [bh][nchunks]
   uint32_t* chunk_off;      // [bh][nchunks]
   uint64_t* qn_sum;         // [bh][nchunks][D][4]: exact sum x (128-bit, 2^-24 units) and

@@ -14,10 +14,13 @@
 //   2. the bin that holds the k-th largest magnitude
 //   3. histogram of the low 7 bits inside that bin  ->  exact threshold T and the
 //      number of elements equal to T that are outliers (the earliest tokens)
-//   4. per chunk of tokens: ties to T, the last positive/negative tie, dense min/max
-//   5. per channel: tie prefix of every chunk, dense min/max -> (scale, min)
-//   6. codes for every element, outlier bitmask per token
-//   7. CSR: per-chunk outlier counts, their scan, then row pointers and entries
+//   4. per chunk of tokens: ties to T, magnitudes above T, the last positive/negative
+//      tie, dense min/max
+//   5. per channel: tie prefix of every chunk, dense min/max -> (scale, min), and each
+//      chunk's outlier count (above T plus the ties ranked below the tie quota)
+//   6. per (batch, head): scan of the chunk counts -> each chunk's first CSR entry
+//   7. codes for every element; the rows of the CSR (row pointers and entries, exact
+//      values from the tile) written in token order by the same pass
 // Every pass reads the keys with coalesced rows; histograms live in LDS and only
 // their non-zero bins reach global memory.
 #include "kvq_common.h"
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a
   const int d = threadIdx.x;
   int T = 0x8000;
   if (d < kHeadDim) T = a.thr[(bh * kHeadDim + d) * 4];
-  uint32_t ties = 0;
+  uint32_t ties = 0, above = 0;
   int32_t last_pos = -1, last_neg = -1;
   float dmin = __builtin_inff(), dmax = -__builtin_inff();
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
@@ -352,6 +355,8 @@ __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a
         } else if (mag == T) {
           if (x & 0x8000u) last_neg = (int32_t)ties; else last_pos = (int32_t)ties;
           ++ties;
+        } else {
+          ++above;
         }
       }
     }
@@ -364,6 +369,7 @@ __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a
     cs[2] = (uint32_t)last_neg;
     cs[3] = __builtin_bit_cast(uint32_t, dmin);
     cs[4] = __builtin_bit_cast(uint32_t, dmax);
+    cs[5] = above;
   }
 }
 
@@ -380,6 +386,12 @@ __global__ void nuq_finalize_kernel(NuqKeysArgs a) {
   for (int c = 0; c < a.nchunks; ++c) {
     const uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + c) * kHeadDim + d) * 8;
     a.tie_prefix[(bh * a.nchunks + c) * kHeadDim + d] = (uint32_t)prefix;
+    if (a.rowptr != nullptr) {
+      // this channel's outliers in chunk c: the magnitudes above T and the ties ranked
+      // below need (ranks prefix .. prefix + ties - 1 fall in this chunk)
+      const int64_t taken = min(max(need - prefix, (int64_t)0), (int64_t)cs[0]);
+      a.chunk_stats[((bh * a.nchunks + c) * kHeadDim + d) * 8 + 6] = cs[5] + (uint32_t)taken;
+    }
     const int32_t lp = (int32_t)cs[1], ln = (int32_t)cs[2];
     if (lp >= 0) last_pos = max(last_pos, prefix + lp);
     if (ln >= 0) last_neg = max(last_neg, prefix + ln);
@@ -434,11 +446,14 @@ __device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim],
   return bits;
 }
 
-// ---- 6: codes and outlier bitmask ---------------------------------------------------
+// ---- 7: codes and CSR rows ---------------------------------------------------------
 template <int B>
 __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a) {
-  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
-  __shared__ uint32_t om[kGroup][4];
+  // two tiles and outlier masks: the CSR rows of one tile are written while the next is
+  // loaded and coded
+  __shared__ __align__(16) uint16_t tiles[2][kGroup][kHeadDim];
+  __shared__ uint32_t oms[2][kGroup][4];
+  __shared__ int64_t rs[kGroup];            // first CSR entry of each token of the tile
   __shared__ uint32_t qh[kHeadDim][16];     // Q-Norm: dense code counts per channel
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
@@ -463,7 +478,12 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   }
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
   const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  // CSR: this chunk's first entry (the scan of the per-chunk counts), kept by wave 0
+  int64_t run = a.rowptr != nullptr ? (int64_t)a.chunk_off[bh * a.nchunks + chunk] : 0;
   for (int64_t tb = t0; tb < t1; tb += kGroup) {
+    const int buf = (int)(((tb - t0) / kGroup) & 1);
+    uint16_t (*tile)[kHeadDim] = tiles[buf];
+    uint32_t (*om)[4] = oms[buf];
     load_key_tile(tile, a, bh, tb);
     if (tid < kGroup * 4) om[tid >> 2][tid & 3] = 0;
     __syncthreads();
@@ -540,9 +560,42 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
       }
     }
     __syncthreads();
-    if (tid < kGroup * 4)
-      a.outmask[(bh * a.cap_tokens + tb + (tid >> 2)) * 4 + (tid & 3)] = om[tid >> 2][tid & 3];
-    __syncthreads();
+    if (a.rowptr != nullptr) {
+      // each token's first entry: wave 0 scans the 32 row lengths; then 128 threads (token
+      // j, mask word w) write the entries of channels 32w..32w+31 (ascending, the exact
+      // fp16 value from the tile) and w = 0 the row pointer.  No barrier after: the next
+      // tile goes to the other buffers, and rs is rewritten only after that tile's codes.
+      if (tid < kWave) {
+        const int j = tid;
+        const uint32_t cnt = j < kGroup ? (uint32_t)(__popc(om[j][0]) + __popc(om[j][1]) +
+                                                     __popc(om[j][2]) + __popc(om[j][3]))
+                                        : 0u;
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kGroup; o <<= 1) {
+          const uint32_t x = __shfl_up(incl, o);
+          if (j >= o) incl += x;
+        }
+        if (j < kGroup) rs[j] = run + (incl - cnt);
+        run += __shfl(incl, kGroup - 1);
+      }
+      __syncthreads();
+      if (tid < kGroup * 4) {
+        const int j = tid >> 2, w = tid & 3;
+        int64_t pos = rs[j];
+        for (int i = 0; i < w; ++i) pos += __popc(om[j][i]);
+        if (w == 0) a.rowptr[bh * (a.cap_tokens + 1) + tb + j] = (int32_t)pos;
+        uint32_t* ent = a.ent + bh * a.csr_capacity;
+        uint32_t bits = om[j][w];
+        while (bits) {
+          const int d = 32 * w + __builtin_ctz(bits);
+          bits &= bits - 1;
+          if (pos < a.csr_capacity)
+            ent[pos] = (uint32_t)d | ((uint32_t)j << 8) | ((uint32_t)tile[j][d] << 16);
+          ++pos;
+        }
+      }
+    }
   }
   if (a.qnorm) {
     // the two lanes of a channel combine their sums; the block's atomics on qh are done
@@ -588,28 +641,17 @@ __global__ void nuq_qnorm_keys_kernel(NuqKeysArgs a) {
   *meta = qnorm_meta(*meta, sx, sxx, hist, n, a.lut, a.bits);
 }
 
-// ---- 7: CSR -------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t row_count(const NuqKeysArgs& a, int64_t bh, int64_t t) {
-  const uint4 m = *reinterpret_cast<const uint4*>(a.outmask + (bh * a.cap_tokens + t) * 4);
-  return __popc(m.x) + __popc(m.y) + __popc(m.z) + __popc(m.w);
-}
-
-__global__ __launch_bounds__(kThreads) void csr_count_kernel(NuqKeysArgs a) {
-  __shared__ uint32_t part[kThreads / kWave];
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int chunk = blockIdx.x % a.nchunks;
-  const int64_t t0 = (int64_t)chunk * kNuqChunk;
-  const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
-  uint32_t s = 0;
-  for (int64_t t = t0 + threadIdx.x; t < t1; t += kThreads) s += row_count(a, bh, t);
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+// ---- 6: CSR chunk offsets -----------------------------------------------------------
+// One workgroup of kHeadDim threads per (batch, head, chunk): the chunk's outlier count,
+// summed over its channels.
+__global__ __launch_bounds__(kHeadDim) void csr_chunk_count_kernel(NuqKeysArgs a) {
+  __shared__ uint32_t part[kHeadDim / kWave];
+  const int64_t q = blockIdx.x;                 // bh * nchunks + chunk
+  uint32_t v = a.chunk_stats[(q * kHeadDim + threadIdx.x) * 8 + 6];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0;
-    for (int w = 0; w < kThreads / kWave; ++w) tot += part[w];
-    a.chunk_cnt[bh * a.nchunks + chunk] = tot;
-  }
+  if (threadIdx.x == 0) a.chunk_cnt[q] = part[0] + part[1];
 }
 
 // One workgroup per (batch, head): exclusive scan of the chunk counts.
@@ -623,54 +665,6 @@ __global__ __launch_bounds__(kThreads) void csr_scan_kernel(NuqKeysArgs a) {
     run += v;
   }
   a.rowptr[bh * (a.cap_tokens + 1) + a.n_tokens] = (int32_t)run;
-}
-
-// Row pointers and entries of one chunk (entries: channel | token % 32 << 8 | fp16 << 16).
-__global__ __launch_bounds__(kThreads) void csr_fill_kernel(NuqKeysArgs a) {
-  constexpr int PER = kNuqChunk / kThreads;   // consecutive tokens per thread
-  __shared__ uint32_t scan[kThreads];
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int chunk = blockIdx.x % a.nchunks;
-  const int64_t t0 = (int64_t)chunk * kNuqChunk + (int64_t)threadIdx.x * PER;
-  const int64_t tend = min((int64_t)a.n_tokens, (int64_t)(chunk + 1) * kNuqChunk);
-  uint32_t cnt[PER];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    cnt[i] = (t0 + i < tend) ? row_count(a, bh, t0 + i) : 0u;
-    mine += cnt[i];
-  }
-  scan[threadIdx.x] = mine;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {       // inclusive Hillis-Steele scan
-    const uint32_t v = threadIdx.x >= o ? scan[threadIdx.x - o] : 0u;
-    __syncthreads();
-    scan[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int64_t pos = (int64_t)a.chunk_off[bh * a.nchunks + chunk] + scan[threadIdx.x] - mine;
-  int32_t* rp = a.rowptr + bh * (a.cap_tokens + 1);
-  uint32_t* ent = a.ent + bh * a.csr_capacity;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int64_t t = t0 + i;
-    if (t >= tend) break;
-    rp[t] = (int32_t)pos;
-    if (cnt[i] == 0) continue;
-    const uint4 m = *reinterpret_cast<const uint4*>(a.outmask + (bh * a.cap_tokens + t) * 4);
-    const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
-    const uint16_t* row = key_row(a, bh, t);
-    for (int w = 0; w < 4; ++w) {
-      uint32_t bits = mw[w];
-      while (bits) {
-        const int d = 32 * w + __builtin_ctz(bits);
-        bits &= bits - 1;
-        if (pos < a.csr_capacity)
-          ent[pos] = (uint32_t)d | ((uint32_t)(t & (kGroup - 1)) << 8) | ((uint32_t)row[d] << 16);
-        ++pos;
-      }
-    }
-  }
 }
 
 // Outliers of one token's vector ("KVQuant" review, abstract item (iv): the largest
@@ -882,15 +876,14 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
   nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 1);
   nuq_chunk_stats_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   nuq_finalize_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
+  if (a.rowptr != nullptr) {
+    csr_chunk_count_kernel<<<dim3(jobs), dim3(kHeadDim), 0, s>>>(a);
+    csr_scan_kernel<<<dim3((unsigned)a.bh_count), dim3(kThreads), 0, s>>>(a);
+  }
   if (a.bits == 2) nuq_quant_keys_kernel<2><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   else if (a.bits == 3) nuq_quant_keys_kernel<3><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   else nuq_quant_keys_kernel<4><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   if (a.qnorm) nuq_qnorm_keys_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
-  if (a.rowptr != nullptr) {
-    csr_count_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
-    csr_scan_kernel<<<dim3((unsigned)a.bh_count), dim3(kThreads), 0, s>>>(a);
-    csr_fill_kernel<<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
-  }
   return hipGetLastError();
 }
 
