@@ -9,8 +9,11 @@
 // so one lane owns a channel pair i.  Each block starts from a_i(t0) = q e^(-i t0 th_i),
 // where e^(-i t0 th_i) is carried from block to block in fp64 (one complex product by
 // e^(-i 32 th_i) per block, started from an angle reduced modulo 2 pi at the wave's
-// first block); inside the block four independent chains (tokens 0, 8, 16, 24 on)
-// advance by e^(-i th_i) per token.  Per-pair partial scores of the block's 32 tokens
+// first block).  Inside the block two chains (tokens 0 and 16 on) advance by the
+// three-term recurrence x(t+1) = 2 cos(th_i) x(t) - x(t-1), which every real-linear
+// function of a_i(t) obeys; with one query head the chains carry s_2i Re(a), s_2i+1 Im(a)
+// and m_2i Re(a) + m_2i+1 Im(a) (key scales and minima folded in), so a token costs three
+// fmas of recurrence and two of score.  Per-pair partial scores of the block's 32 tokens
 // are then summed across lanes (lanes 2t and 2t+1 end with token t).
 // Outliers: the dense pass uses the stored code everywhere; one lane per CSR entry
 // (which carries its token's place in the block) then computes
@@ -242,27 +245,61 @@ __device__ __forceinline__ float softmax_step(float s, float& m, float& l, float
 struct PairConsts {
   float2 q[8];        // (q_2i, q_2i+1) per query head
   float2 step;        // e^(-i theta_i)
-  float2 r8, r16, r24;        // e^(-i 8 theta_i), e^(-i 16 theta_i), e^(-i 24 theta_i)
+  float2 r16;         // e^(-i 16 theta_i)
+  float tc;           // 2 cos(theta_i)
   double2 step32;     // e^(-i 32 theta_i): from one block to the next
   double theta;       // theta_i
   float ks0, km0, ks1, km1;   // key scale / min of channels 2i, 2i+1
 };
 
-// The block's partial scores of this lane's pair for one head: four chains of eight
-// tokens (from tokens 0, 8, 16, 24), each advanced by e^(-i theta) per token, so that
-// no product waits on more than seven others.
+// Any real-linear function x(t) of q e^(-i t theta) (its real part, its imaginary part,
+// a combination of both) satisfies x(t+1) = 2 cos(theta) x(t) - x(t-1): one fma per
+// token instead of a complex product.  An error made at token s reaches token t scaled
+// by sin((t-s) theta) / sin(theta), at most t - s, so over the 16 tokens of a chain the
+// recurrence keeps a relative error of ~1e-5 even where theta is tiny.
+__device__ __forceinline__ float cheb_next(float tc, float cur, float prev) {
+  return fmaf(tc, cur, -prev);
+}
+
+// The block's partial scores of this lane's pair for one head, from dequantized keys:
+// two chains (tokens 0..15 and 16..31) of the rotated query q e^(-i t theta).
 __device__ __forceinline__ void pair_scores(float (&part)[32], float2 qb, const PairConsts& pc,
                                             const float (&k0)[32], const float (&k1)[32]) {
-  float2 c[4] = {qb, cmul(qb, pc.r8), cmul(qb, pc.r16), cmul(qb, pc.r24)};
+  float2 a[2], b[2];           // the chain's values at tokens k and k + 1
+  a[0] = qb;
+  a[1] = cmul(qb, pc.r16);
+  b[0] = cmul(a[0], pc.step);
+  b[1] = cmul(a[1], pc.step);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 16; ++k) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) part[8 * m + k] = fmaf(c[m].x, k0[8 * m + k], c[m].y * k1[8 * m + k]);
-    if (k < 7) {
+    for (int ch = 0; ch < 2; ++ch)
+      part[16 * ch + k] = fmaf(a[ch].x, k0[16 * ch + k], a[ch].y * k1[16 * ch + k]);
+    if (k < 15) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) c[m] = cmul(c[m], pc.step);
+      for (int ch = 0; ch < 2; ++ch) {
+        float2 n = b[ch];
+        if (k < 14)
+          n = make_float2(cheb_next(pc.tc, b[ch].x, a[ch].x), cheb_next(pc.tc, b[ch].y, a[ch].y));
+        a[ch] = b[ch];
+        b[ch] = n;
+      }
     }
   }
+}
+
+// (u, v, w) of a rotated query c for one head with the key metadata folded in:
+// u = s_2i Re(c), v = s_2i+1 Im(c), w = m_2i Re(c) + m_2i+1 Im(c), so that the pair's
+// score of codes (l0, l1) is u l0 + v l1 + w.  All three are real-linear in c.
+struct Uvw {
+  float u, v, w;
+};
+__device__ __forceinline__ Uvw uvw_of(float2 c, const PairConsts& pc) {
+  return Uvw{pc.ks0 * c.x, pc.ks1 * c.y, fmaf(pc.km0, c.x, pc.km1 * c.y)};
+}
+__device__ __forceinline__ Uvw cheb_next(float tc, const Uvw& cur, const Uvw& prev) {
+  return Uvw{cheb_next(tc, cur.u, prev.u), cheb_next(tc, cur.v, prev.v),
+             cheb_next(tc, cur.w, prev.w)};
 }
 
 // Softmax over the block's scores and the value accumulation shared by packed blocks
@@ -365,30 +402,39 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   float s[GQ];
   float2 qb[GQ];
   if constexpr (GQ == 1) {
-    // one head: the lookups of each chain step are used at once (16 live values, not 64)
+    // one head: the key metadata ride in the chains (u, v, w), and the lookups of each
+    // chain step are used at once
     float part[32];
     qb[0] = cmul(pc.q[0], base);
-    float2 c[4] = {qb[0], cmul(qb[0], pc.r8), cmul(qb[0], pc.r16), cmul(qb[0], pc.r24)};
+    const float2 c16 = cmul(qb[0], pc.r16);
+    Uvw ca[2] = {uvw_of(qb[0], pc), uvw_of(c16, pc)};                    // token k
+    Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {                    // tokens 4h..4h+3 of every chain
-      uint32_t a[4][2], b[4][2];
+    for (int m4 = 0; m4 < 4; ++m4) {                 // tokens 4 m4 .. 4 m4 + 3 of each chain
+      uint32_t a[2][2], b[2][2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        lut4<B>(lk, codes_of<B>(kw0, 2 * m + h), a[m][0], a[m][1]);
-        lut4<B>(lk, codes_of<B>(kw1, 2 * m + h), b[m][0], b[m][1]);
+      for (int ch = 0; ch < 2; ++ch) {
+        lut4<B>(lk, codes_of<B>(kw0, m4 + 4 * ch), a[ch][0], a[ch][1]);
+        lut4<B>(lk, codes_of<B>(kw1, m4 + 4 * ch), b[ch][0], b[ch][1]);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        const int k = 4 * m4 + kk;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t wa = a[m][kk >> 1], wb = b[m][kk >> 1];
-          const float x0 = fmaf((kk & 1) ? hi_f16(wa) : lo_f16(wa), pc.ks0, pc.km0);
-          const float x1 = fmaf((kk & 1) ? hi_f16(wb) : lo_f16(wb), pc.ks1, pc.km1);
-          part[8 * m + 4 * h + kk] = fmaf(c[m].x, x0, c[m].y * x1);
+        for (int ch = 0; ch < 2; ++ch) {
+          const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
+          const float l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
+          const float l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
+          part[16 * ch + k] = fmaf(ca[ch].u, l0, fmaf(ca[ch].v, l1, ca[ch].w));
         }
-        if (4 * h + kk < 7) {
+        if (k < 15) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) c[m] = cmul(c[m], pc.step);
+          for (int ch = 0; ch < 2; ++ch) {
+            Uvw n = cb[ch];
+            if (k < 14) n = cheb_next(pc.tc, cb[ch], ca[ch]);
+            ca[ch] = cb[ch];
+            cb[ch] = n;
+          }
         }
       }
     }
@@ -641,10 +687,10 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
     pc.q[j] = make_float2(lo_f16(qq), hi_f16(qq));
   }
   pc.theta = a.rope_theta > 0.f ? pow((double)a.rope_theta, -2.0 * lane / kHeadDim) : 0.0;
-  pc.step = to_f32(rot_at64(1, pc.theta));
-  pc.r8 = to_f32(rot_at64(8, pc.theta));
+  const double2 step64 = rot_at64(1, pc.theta);
+  pc.step = to_f32(step64);
+  pc.tc = (float)(2.0 * step64.x);
   pc.r16 = to_f32(rot_at64(16, pc.theta));
-  pc.r24 = to_f32(rot_at64(24, pc.theta));
   pc.step32 = rot_at64(kGroup, pc.theta);
   if (a.n_blocks > 0) {
     const uint2 km = *reinterpret_cast<const uint2*>(a.k_meta + bh * kHeadDim + 2 * lane);
