@@ -340,6 +340,15 @@ struct NuqBlockRegs {
   int32_t r0, r1;            // CSR row of token lane >> 1
 };
 
+// The block's outlier entries: key CSR entries [e_begin, e_end) and the first 64 of
+// them (one per lane), the first 64 value-outlier entries.  They are loaded once the
+// block's row pointers are in and before the next block's loads are issued, so that
+// waiting for them never waits for the prefetch.
+struct NuqBlockEntries {
+  int64_t e_begin, e_end;
+  uint32_t ent, vent;
+};
+
 // 2B consecutive code words of a lane's channel pair.
 template <int B>
 __device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
@@ -365,17 +374,39 @@ __device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const DecodeA
   load_words<B>(r.kw, a.k_codes + (gblk * kHeadDim + 2 * lane) * B);
   load_words<B>(r.vw, a.v_codes + (gblk * kHeadDim + 2 * lane) * B);
   r.vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
-  r.r0 = r.r1 = 0;
+  // Unconditional, from a uniformly chosen global address (without key outliers any
+  // two words of the value metadata, ignored by load_block_entries), so that no register
+  // copy of a conditionally loaded value makes the wave wait for the loads just issued.
+  const int32_t* rp = a.csr_rowptr
+                          ? a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1) + t0 + t
+                          : reinterpret_cast<const int32_t*>(a.v_meta);
+  r.r0 = rp[0];
+  r.r1 = rp[1];
+}
+
+template <int B>
+__device__ __forceinline__ NuqBlockEntries load_block_entries(const DecodeArgs& a, int64_t bh,
+                                                              int64_t t0,
+                                                              const NuqBlockRegs<B>& r,
+                                                              int lane) {
+  NuqBlockEntries e;
+  e.e_begin = e.e_end = 0;
   if (a.csr_rowptr) {
-    const int32_t* rp = a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1);
-    r.r0 = rp[t0 + t];
-    r.r1 = rp[t0 + t + 1];
+    e.e_begin = max((int64_t)__builtin_amdgcn_readlane(r.r0, 0), (int64_t)0);
+    e.e_end = min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), a.csr_capacity);
   }
+  e.ent = 0;
+  if (e.e_begin + lane < e.e_end) e.ent = a.csr_ent[bh * a.csr_capacity + e.e_begin + lane];
+  e.vent = 0;
+  if (a.v_out != nullptr && lane < kGroup * a.v_kv)
+    e.vent = a.v_out[(bh * (a.cap_blocks * kGroup) + (t0 - a.n_sink)) * a.v_kv + lane];
+  return e;
 }
 
 template <int GQ, int B>
 __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
-                                  const NuqBlockRegs<B>& r, const PairConsts& pc, float2 base,
+                                  const NuqBlockRegs<B>& r, const NuqBlockEntries& be,
+                                  const PairConsts& pc, float2 base,
                                   const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
                                   const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
@@ -384,18 +415,11 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   const uint32_t* vw0 = r.vw;
   const uint32_t* vw1 = r.vw + B;
 
-  // The block's CSR entries [e_begin, e_end): the first 64 are loaded now, one per
-  // lane, so that the dense work below covers the load.
-  const int64_t e_begin = max((int64_t)__builtin_amdgcn_readlane(r.r0, 0), (int64_t)0);
-  const int64_t e_end =
-      min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), a.csr_capacity);
-  uint32_t ent_first = 0;
-  if (e_begin + lane < e_end) ent_first = a.csr_ent[bh * a.csr_capacity + e_begin + lane];
-  // The block's value outliers: v_kv per token, 32 * v_kv entries from vbase.
+  // The block's CSR entries [e_begin, e_end) (the first 64 already requested) and
+  // value outliers: v_kv per token, 32 * v_kv entries from vbase.
+  const int64_t e_begin = be.e_begin, e_end = be.e_end;
   const int v_ne = a.v_out != nullptr ? kGroup * a.v_kv : 0;
   const int64_t vbase = (bh * (a.cap_blocks * kGroup) + (t0 - a.n_sink)) * a.v_kv;
-  uint32_t vent_first = 0;
-  if (lane < v_ne) vent_first = a.v_out[vbase + lane];
 
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
@@ -479,11 +503,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
       ws.kc[2 * lane + 1][i] = kw1[i];
     }
     __builtin_amdgcn_wave_barrier();
-    for (int64_t w0 = e_begin; w0 < e_end; w0 += 64) {
-      const bool has = w0 + lane < e_end;
-      uint32_t ent = ent_first;
-      if (w0 != e_begin) ent = has ? a.csr_ent[bh * a.csr_capacity + w0 + lane] : 0u;
-      if (has) {
+    auto window = [&](int64_t w0, uint32_t ent) {
+      if (w0 + lane < e_end) {
         const int te = (int)((ent >> 8) & (kGroup - 1));
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
@@ -512,7 +533,12 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
 #pragma unroll
       for (int j = 0; j < GQ; ++j) s[j] += acc[j] + dpp<0xB1>(0.f, acc[j]);
       __builtin_amdgcn_wave_barrier();
-    }
+    };
+    // the first window from the entries already in registers; more than 64 entries in
+    // a block (rare) are loaded window by window
+    window(e_begin, be.ent);
+    for (int64_t w0 = e_begin + 64; w0 < e_end; w0 += 64)
+      window(w0, w0 + lane < e_end ? a.csr_ent[bh * a.csr_capacity + w0 + lane] : 0u);
   }
 
   // ---- softmax (lanes 2t and 2t+1 both carry the corrected score of token t)
@@ -587,7 +613,7 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     for (int e0 = 0; e0 < v_ne; e0 += 64) {
       const int e = e0 + lane;
       if (e < v_ne) {
-        const uint32_t ent = e0 == 0 ? vent_first : a.v_out[vbase + e];
+        const uint32_t ent = e0 == 0 ? be.vent : a.v_out[vbase + e];
         const int te = (e / a.v_kv) & (kGroup - 1);
         const int d = (int)(ent & (kHeadDim - 1));
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
@@ -741,14 +767,18 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
     // e^(-i t0 theta) of the current block, in fp64 from block to block
     double2 base = rot_at64(a.n_sink + (int64_t)b0 * kGroup, pc.theta);
     for (int i = b0; i < b1; i += 2) {
+      const int64_t ta = a.n_sink + (int64_t)i * kGroup;
+      const NuqBlockEntries e0 = load_block_entries<B>(a, bh, ta, r0, lane);
       load_nuq_block<B>(r1, a, bh, min(i + 1, last), lane);
-      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)i * kGroup, r0, pc, to_f32(base), lk,
-                               lv, st, sh, wsc[wave], lane);
+      process_nuq_block<GQ, B>(a, bh, ta, r0, e0, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
+                               lane);
       base = cmul64(base, pc.step32);
       if (i + 1 >= b1) break;
+      const int64_t tb = ta + kGroup;
+      const NuqBlockEntries e1 = load_block_entries<B>(a, bh, tb, r1, lane);
       load_nuq_block<B>(r0, a, bh, min(i + 2, last), lane);
-      process_nuq_block<GQ, B>(a, bh, a.n_sink + (int64_t)(i + 1) * kGroup, r1, pc, to_f32(base),
-                               lk, lv, st, sh, wsc[wave], lane);
+      process_nuq_block<GQ, B>(a, bh, tb, r1, e1, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
+                               lane);
       base = cmul64(base, pc.step32);
     }
   }
