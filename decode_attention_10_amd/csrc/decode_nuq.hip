@@ -349,6 +349,21 @@ struct NuqBlockEntries {
   uint32_t ent, vent;
 };
 
+// A wave's (batch, kv head) streams, uniform: resolved once so that the block loop
+// keeps a few base pointers in scalar registers instead of the whole argument block.
+struct NuqStreams {
+  const uint32_t* kc;        // key code words of packed block 0
+  const uint32_t* vc;        // value code words of packed block 0
+  const uint32_t* vm;        // value scale / min of packed token 0
+  const int32_t* rp;         // CSR row pointers of packed token 0 (vm without key outliers)
+  const uint32_t* ent;       // CSR entries
+  const uint32_t* vout;      // value-outlier entries of packed token 0 (NULL: none)
+  int64_t csr_cap;
+  int rp_step;               // 1; 0 without key outliers (both row loads read vm)
+  int v_kv;                  // value outliers per token
+  float scale_log2;
+};
+
 // 2B consecutive code words of a lane's channel pair.
 template <int B>
 __device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
@@ -366,46 +381,39 @@ __device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
 }
 
 template <int B>
-__device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const DecodeArgs& a,
-                                               int64_t bh, int64_t blk, int lane) {
+__device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const NuqStreams& S,
+                                               int64_t blk, int lane) {
   const int t = lane >> 1;
-  const int64_t gblk = bh * a.cap_blocks + blk;
   const int64_t t0 = blk * kGroup;
-  load_words<B>(r.kw, a.k_codes + (gblk * kHeadDim + 2 * lane) * B);
-  load_words<B>(r.vw, a.v_codes + (gblk * kHeadDim + 2 * lane) * B);
-  r.vmeta = a.v_meta[bh * (a.cap_blocks * kGroup) + t0 + t];
-  // Unconditional, from a uniformly chosen global address (without key outliers any
-  // two words of the value metadata, ignored by load_block_entries), so that no register
-  // copy of a conditionally loaded value makes the wave wait for the loads just issued.
-  const int32_t* rp = a.csr_rowptr
-                          ? a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1) + t0 + t
-                          : reinterpret_cast<const int32_t*>(a.v_meta);
-  r.r0 = rp[0];
-  r.r1 = rp[1];
+  load_words<B>(r.kw, S.kc + blk * (kHeadDim * B) + 2 * lane * B);
+  load_words<B>(r.vw, S.vc + blk * (kHeadDim * B) + 2 * lane * B);
+  r.vmeta = S.vm[t0 + t];
+  // Unconditional (without key outliers both read a value-metadata word, ignored by
+  // load_block_entries), so that no register copy of a conditionally loaded value makes
+  // the wave wait for the loads just issued.
+  r.r0 = S.rp[t0 + t];
+  r.r1 = S.rp[t0 + t + S.rp_step];
 }
 
 template <int B>
-__device__ __forceinline__ NuqBlockEntries load_block_entries(const DecodeArgs& a, int64_t bh,
-                                                              int64_t t0,
+__device__ __forceinline__ NuqBlockEntries load_block_entries(const NuqStreams& S, int64_t blk,
                                                               const NuqBlockRegs<B>& r,
                                                               int lane) {
   NuqBlockEntries e;
   e.e_begin = e.e_end = 0;
-  if (a.csr_rowptr) {
+  if (S.rp_step) {
     e.e_begin = max((int64_t)__builtin_amdgcn_readlane(r.r0, 0), (int64_t)0);
-    e.e_end = min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), a.csr_capacity);
+    e.e_end = min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), S.csr_cap);
   }
   e.ent = 0;
-  if (e.e_begin + lane < e.e_end) e.ent = a.csr_ent[bh * a.csr_capacity + e.e_begin + lane];
+  if (e.e_begin + lane < e.e_end) e.ent = S.ent[e.e_begin + lane];
   e.vent = 0;
-  if (a.v_out != nullptr && lane < kGroup * a.v_kv)
-    e.vent = a.v_out[(bh * (a.cap_blocks * kGroup) + (t0 - a.n_sink)) * a.v_kv + lane];
+  if (S.vout != nullptr && lane < kGroup * S.v_kv) e.vent = S.vout[blk * kGroup * S.v_kv + lane];
   return e;
 }
 
 template <int GQ, int B>
-__device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
-                                  const NuqBlockRegs<B>& r, const NuqBlockEntries& be,
+__device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlockRegs<B>& r, const NuqBlockEntries& be,
                                   const PairConsts& pc, float2 base,
                                   const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
                                   const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
@@ -418,8 +426,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
   // The block's CSR entries [e_begin, e_end) (the first 64 already requested) and
   // value outliers: v_kv per token, 32 * v_kv entries from vbase.
   const int64_t e_begin = be.e_begin, e_end = be.e_end;
-  const int v_ne = a.v_out != nullptr ? kGroup * a.v_kv : 0;
-  const int64_t vbase = (bh * (a.cap_blocks * kGroup) + (t0 - a.n_sink)) * a.v_kv;
+  const int v_ne = S.vout != nullptr ? kGroup * S.v_kv : 0;
+  const int64_t vbase = blk * kGroup * S.v_kv;
 
   // ---- keys: dequantize this lane's pair for the 32 tokens, then per head the
   // rotated-query partial scores and their sum across lanes
@@ -538,13 +546,13 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     // a block (rare) are loaded window by window
     window(e_begin, be.ent);
     for (int64_t w0 = e_begin + 64; w0 < e_end; w0 += 64)
-      window(w0, w0 + lane < e_end ? a.csr_ent[bh * a.csr_capacity + w0 + lane] : 0u);
+      window(w0, w0 + lane < e_end ? S.ent[w0 + lane] : 0u);
   }
 
   // ---- softmax (lanes 2t and 2t+1 both carry the corrected score of token t)
   float p[GQ], alpha[GQ];
 #pragma unroll
-  for (int j = 0; j < GQ; ++j) s[j] *= a.scale_log2;
+  for (int j = 0; j < GQ; ++j) s[j] *= S.scale_log2;
   softmax_block<GQ>(st, s, p, alpha);
 
   // ---- values: fp16 weights p * scale * 2^-e per token into LDS, p * min per lane
@@ -613,8 +621,8 @@ __device__ void process_nuq_block(const DecodeArgs& a, int64_t bh, int64_t t0,
     for (int e0 = 0; e0 < v_ne; e0 += 64) {
       const int e = e0 + lane;
       if (e < v_ne) {
-        const uint32_t ent = e0 == 0 ? be.vent : a.v_out[vbase + e];
-        const int te = (e / a.v_kv) & (kGroup - 1);
+        const uint32_t ent = e0 == 0 ? be.vent : S.vout[vbase + e];
+        const int te = (e / S.v_kv) & (kGroup - 1);
         const int d = (int)(ent & (kHeadDim - 1));
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
         const uint32_t vmw = ws.vmeta[te];
@@ -762,22 +770,32 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
     // One block in flight ahead of the one being processed (clamped index, unrolled by
     // two so no register copy waits on the loads just issued).
     const int last = b1 - 1;
+    NuqStreams S;
+    const int64_t bt = bh * (a.cap_blocks * kGroup);      // this head's first token slot
+    S.kc = a.k_codes + bh * a.cap_blocks * (kHeadDim * B);
+    S.vc = a.v_codes + bh * a.cap_blocks * (kHeadDim * B);
+    S.vm = a.v_meta + bt;
+    S.rp = a.csr_rowptr ? a.csr_rowptr + bh * (a.cap_blocks * kGroup + 1)
+                        : reinterpret_cast<const int32_t*>(S.vm);
+    S.rp_step = a.csr_rowptr ? 1 : 0;
+    S.ent = a.csr_ent + bh * a.csr_capacity;
+    S.csr_cap = a.csr_capacity;
+    S.vout = a.v_out ? a.v_out + bt * a.v_kv : nullptr;
+    S.v_kv = a.v_kv;
+    S.scale_log2 = a.scale_log2;
     NuqBlockRegs<B> r0, r1;
-    load_nuq_block<B>(r0, a, bh, b0, lane);
+    load_nuq_block<B>(r0, S, b0, lane);
     // e^(-i t0 theta) of the current block, in fp64 from block to block
     double2 base = rot_at64(a.n_sink + (int64_t)b0 * kGroup, pc.theta);
     for (int i = b0; i < b1; i += 2) {
-      const int64_t ta = a.n_sink + (int64_t)i * kGroup;
-      const NuqBlockEntries e0 = load_block_entries<B>(a, bh, ta, r0, lane);
-      load_nuq_block<B>(r1, a, bh, min(i + 1, last), lane);
-      process_nuq_block<GQ, B>(a, bh, ta, r0, e0, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
-                               lane);
+      const NuqBlockEntries e0 = load_block_entries<B>(S, i, r0, lane);
+      load_nuq_block<B>(r1, S, min(i + 1, last), lane);
+      process_nuq_block<GQ, B>(S, i, r0, e0, pc, to_f32(base), lk, lv, st, sh, wsc[wave], lane);
       base = cmul64(base, pc.step32);
       if (i + 1 >= b1) break;
-      const int64_t tb = ta + kGroup;
-      const NuqBlockEntries e1 = load_block_entries<B>(a, bh, tb, r1, lane);
-      load_nuq_block<B>(r0, a, bh, min(i + 2, last), lane);
-      process_nuq_block<GQ, B>(a, bh, tb, r1, e1, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
+      const NuqBlockEntries e1 = load_block_entries<B>(S, i + 1, r1, lane);
+      load_nuq_block<B>(r0, S, min(i + 2, last), lane);
+      process_nuq_block<GQ, B>(S, i + 1, r1, e1, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
                                lane);
       base = cmul64(base, pc.step32);
     }
