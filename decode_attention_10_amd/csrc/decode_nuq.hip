@@ -113,6 +113,57 @@ __device__ __forceinline__ uint32_t codes_of(const uint32_t* w, int m) {
   else return codes4<B>(w, m);
 }
 
+// nuq3 pair-table indices, one per byte: for tokens 4m..4m+3, the key code of channel
+// 2i plus 8 times that of channel 2i+1 (w0, w1: the two channels' words).  For m < 6
+// one mask and one masked merge, the second field taken in place (bits 3..5 of a byte).
+__device__ __forceinline__ uint32_t key_pair_index4(const uint32_t* w0, const uint32_t* w1,
+                                                    int m) {
+  if (m < 6) {
+    const uint32_t a = w0[m >> 1], b = w1[m >> 1];
+    if (m & 1) return ((a >> 3) & 0x07070707u) | (b & 0x38383838u);
+    return (a & 0x07070707u) | ((b << 3) & 0x38383838u);
+  }
+  return codes4_3(w0, m) | (codes4_3(w1, m) << 3);
+}
+
+// nuq3 value pair-table indices of one channel, one per byte: byte k pairs tokens
+// 8q + k and 8q + 4 + k.  For q < 3 these are the two whole codes at bits 0..5 of byte k
+// of word q; for q = 3 they are assembled from the split codes of tokens 24..31.
+__device__ __forceinline__ uint32_t value_pair_index4(const uint32_t* w, int q) {
+  if (q < 3) return w[q] & 0x3F3F3F3Fu;
+  uint32_t x = ((w[0] >> 6) & 0x03030303u) | ((w[2] >> 4) & 0x04040404u);   // token 24 + k
+  x |= (w[1] >> 3) & 0x18181818u;                                          // 28 + k, low
+  return x | ((w[2] >> 2) & 0x20202020u);                                  // 28 + k, high
+}
+
+// 4 * (byte k of x): one v_lshlrev_b32 with a byte-select operand (SDWA).  Written out
+// because the compiler, knowing the top bits of each index byte are clear, otherwise
+// prefers a shift and a mask.  Arithmetic only, no memory access.
+template <int K>
+__device__ __forceinline__ uint32_t byte_times4(uint32_t x) {
+  uint32_t r;
+  if constexpr (K == 0)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:BYTE_0" : "=v"(r) : "v"(x));
+  else if constexpr (K == 1)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:BYTE_1" : "=v"(r) : "v"(x));
+  else if constexpr (K == 2)
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:BYTE_2" : "=v"(r) : "v"(x));
+  else
+    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+        "src1_sel:BYTE_3" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// The table entry selected by byte K of a word of table indices (< 64 each).
+template <int K>
+__device__ __forceinline__ uint32_t pair_entry(const uint32_t* table, uint32_t idx4) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) +
+                                            byte_times4<K>(idx4));
+}
+
 template <int B>
 __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
   if constexpr (B == 4) {
@@ -318,6 +369,9 @@ struct NuqShared {
   float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
   float lutk[16], lutv[16];
+  // nuq3 code-book pairs: entry a + 8 b holds (lut[a], lut[b]) as fp16 halves.  Keys look
+  // up the two channels of a lane's pair at one token, values two tokens of one channel.
+  uint32_t tk[64], tv[64];
 };
 
 // Per-wave scratch (LDS).
@@ -443,20 +497,34 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) {                 // tokens 4 m4 .. 4 m4 + 3 of each chain
-      uint32_t a[2][2], b[2][2];
+      uint32_t a[2][2], b[2][2], ix[2];
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        lut4<B>(lk, codes_of<B>(kw0, m4 + 4 * ch), a[ch][0], a[ch][1]);
-        lut4<B>(lk, codes_of<B>(kw1, m4 + 4 * ch), b[ch][0], b[ch][1]);
+        if constexpr (B == 3) {
+          ix[ch] = key_pair_index4(kw0, kw1, m4 + 4 * ch);
+        } else {
+          lut4<B>(lk, codes_of<B>(kw0, m4 + 4 * ch), a[ch][0], a[ch][1]);
+          lut4<B>(lk, codes_of<B>(kw1, m4 + 4 * ch), b[ch][0], b[ch][1]);
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = 4 * m4 + kk;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
-          const float l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
-          const float l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
+          float l0, l1;
+          if constexpr (B == 3) {
+            const uint32_t e = kk == 0   ? pair_entry<0>(sh.tk, ix[ch])
+                               : kk == 1 ? pair_entry<1>(sh.tk, ix[ch])
+                               : kk == 2 ? pair_entry<2>(sh.tk, ix[ch])
+                                         : pair_entry<3>(sh.tk, ix[ch]);
+            l0 = lo_f16(e);
+            l1 = hi_f16(e);
+          } else {
+            const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
+            l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
+            l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
+          }
           part[16 * ch + k] = fmaf(ca[ch].u, l0, fmaf(ca[ch].v, l1, ca[ch].w));
         }
         if (k < 15) {
@@ -573,7 +641,10 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
       st.e[j] = e1;
       wsc = ldexpf(w, -e1);
     }
-    ws.psh[j][t] = __builtin_bit_cast(uint16_t, (_Float16)wsc);
+    // nuq3 pairs tokens 8q + k and 8q + 4 + k (the value pair-table order): token
+    // t = 8q + 4h + k goes to half h of pair 4q + k
+    const int slot = B == 3 ? ((t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1)) : t;
+    ws.psh[j][slot] = __builtin_bit_cast(uint16_t, (_Float16)wsc);
     st.mv[j] = fmaf(p[j], vm, st.mv[j] * alpha[j]);     // every token counted twice
     st.o[j][0] = o0;
     st.o[j][1] = o1;
@@ -585,17 +656,35 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                // tokens 8i..8i+7
       const uint4 w8 = pp[i];
+      if constexpr (B == 3) {
+        const uint32_t x0 = value_pair_index4(vw0, i), x1 = value_pair_index4(vw1, i);
+        const uint32_t wk[4] = {w8.x, w8.y, w8.z, w8.w};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {              // tokens 4m4..4m4+3, m4 = 2i + h
-        const int m4 = 2 * i + h;
-        const uint32_t w01 = h ? w8.z : w8.x, w23 = h ? w8.w : w8.y;
-        uint32_t a01, a23, b01, b23;
-        lut4<B>(lv, codes_of<B>(vw0, m4), a01, a23);
-        lut4<B>(lv, codes_of<B>(vw1, m4), b01, b23);
-        o0 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(a01), o0, false);
-        o0 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(a23), o0, false);
-        o1 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(b01), o1, false);
-        o1 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(b23), o1, false);
+        for (int k = 0; k < 4; ++k) {            // tokens 8i + k, 8i + 4 + k
+          const uint32_t e0 = k == 0   ? pair_entry<0>(sh.tv, x0)
+                              : k == 1 ? pair_entry<1>(sh.tv, x0)
+                              : k == 2 ? pair_entry<2>(sh.tv, x0)
+                                       : pair_entry<3>(sh.tv, x0);
+          const uint32_t e1 = k == 0   ? pair_entry<0>(sh.tv, x1)
+                              : k == 1 ? pair_entry<1>(sh.tv, x1)
+                              : k == 2 ? pair_entry<2>(sh.tv, x1)
+                                       : pair_entry<3>(sh.tv, x1);
+          o0 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e0), o0, false);
+          o1 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e1), o1, false);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {            // tokens 4m4..4m4+3, m4 = 2i + h
+          const int m4 = 2 * i + h;
+          const uint32_t w01 = h ? w8.z : w8.x, w23 = h ? w8.w : w8.y;
+          uint32_t a01, a23, b01, b23;
+          lut4<B>(lv, codes_of<B>(vw0, m4), a01, a23);
+          lut4<B>(lv, codes_of<B>(vw1, m4), b01, b23);
+          o0 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(a01), o0, false);
+          o0 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(a23), o0, false);
+          o1 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(b01), o1, false);
+          o1 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(b23), o1, false);
+        }
       }
     }
     st.o[j][0] = o0;
@@ -698,7 +787,7 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
 }
 
 template <int GQ, int NW, int B>
-__global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel(DecodeArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ NuqShared<GQ> sh;
   __shared__ __align__(16) NuqWaveScratch<GQ, B> wsc[NW];
@@ -741,6 +830,10 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 3 : 1) void decode_nuq_kernel
     sh.ks[2 * lane + 1] = pc.ks1; sh.km[2 * lane + 1] = pc.km1;
     if (lane < (1 << B)) sh.lutk[lane] = lut_value(a.lut_k, lane);
     if (lane < (1 << B)) sh.lutv[lane] = lut_value(a.lut_v, lane);
+    if constexpr (B == 3) {
+      sh.tk[lane] = a.lut_k[lane & 7] | ((uint32_t)a.lut_k[lane >> 3] << 16);
+      sh.tv[lane] = a.lut_v[lane & 7] | ((uint32_t)a.lut_v[lane >> 3] << 16);
+    }
   }
   __syncthreads();
 
