@@ -173,9 +173,15 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
     const int jj = j & 15;
     return (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
   } else {
+    // without branches (the entry lanes of a wave hold any mix of tokens): m < 6, the
+    // whole code at bit 8k + 3(m % 2) of word m / 2; m = 6, 7, two bits at 8k + 6 of word
+    // m - 6 and the high bit at 8k + m of word 2
     const int k = j & 3, m = j >> 2;
-    if (m < 6) return (w[m >> 1] >> (8 * k + 3 * (m & 1))) & 7u;
-    return ((w[m - 6] >> (8 * k + 6)) & 3u) | (((w[2] >> (8 * k + m)) & 1u) << 2);
+    const bool whole = m < 6;
+    const uint32_t a = (w[whole ? m >> 1 : m - 6] >> (8 * k + (whole ? 3 * (m & 1) : 6))) &
+                       (whole ? 7u : 3u);
+    const uint32_t h = (w[2] >> (8 * k + (m & 7))) & (whole ? 0u : 1u);
+    return a | (h << 2);
   }
 }
 
@@ -394,12 +400,12 @@ struct NuqBlockRegs {
   int32_t r0, r1;            // CSR row of token lane >> 1
 };
 
-// The block's outlier entries: key CSR entries [e_begin, e_end) and the first 64 of
+// The block's outlier entries: key CSR entries [e_begin, e_begin + n) and the first 64 of
 // them (one per lane), the first 64 value-outlier entries.  They are loaded once the
 // block's row pointers are in and before the next block's loads are issued, so that
 // waiting for them never waits for the prefetch.
 struct NuqBlockEntries {
-  int64_t e_begin, e_end;
+  int32_t e_begin, n;        // n entries from e_begin (at most one per code of the block)
   uint32_t ent, vent;
 };
 
@@ -412,7 +418,7 @@ struct NuqStreams {
   const int32_t* rp;         // CSR row pointers of packed token 0 (vm without key outliers)
   const uint32_t* ent;       // CSR entries
   const uint32_t* vout;      // value-outlier entries of packed token 0 (NULL: none)
-  int64_t csr_cap;
+  int32_t csr_cap;           // at most INT32_MAX (checked by the host)
   int rp_step;               // 1; 0 without key outliers (both row loads read vm)
   int v_kv;                  // value outliers per token
   float scale_log2;
@@ -454,13 +460,15 @@ __device__ __forceinline__ NuqBlockEntries load_block_entries(const NuqStreams& 
                                                               const NuqBlockRegs<B>& r,
                                                               int lane) {
   NuqBlockEntries e;
-  e.e_begin = e.e_end = 0;
+  e.e_begin = e.n = 0;
   if (S.rp_step) {
-    e.e_begin = max((int64_t)__builtin_amdgcn_readlane(r.r0, 0), (int64_t)0);
-    e.e_end = min((int64_t)__builtin_amdgcn_readlane(r.r1, 63), S.csr_cap);
+    const int32_t b0 = max(__builtin_amdgcn_readlane(r.r0, 0), 0);
+    const int32_t b1 = min(__builtin_amdgcn_readlane(r.r1, 63), S.csr_cap);
+    e.e_begin = b0;
+    e.n = min(max(b1 - b0, 0), kGroup * kHeadDim);
   }
   e.ent = 0;
-  if (e.e_begin + lane < e.e_end) e.ent = S.ent[e.e_begin + lane];
+  if (lane < e.n) e.ent = (S.ent + e.e_begin)[lane];
   e.vent = 0;
   if (S.vout != nullptr && lane < kGroup * S.v_kv) e.vent = S.vout[blk * kGroup * S.v_kv + lane];
   return e;
@@ -468,7 +476,8 @@ __device__ __forceinline__ NuqBlockEntries load_block_entries(const NuqStreams& 
 
 template <int GQ, int B>
 __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlockRegs<B>& r, const NuqBlockEntries& be,
-                                  const PairConsts& pc, float2 base,
+                                  const PairConsts& pc,
+                                  float2 base,   // e^(-i t0 theta); q e^(-i t0 theta) if GQ == 1
                                   const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
                                   const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
@@ -477,9 +486,9 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
   const uint32_t* vw0 = r.vw;
   const uint32_t* vw1 = r.vw + B;
 
-  // The block's CSR entries [e_begin, e_end) (the first 64 already requested) and
+  // The block's CSR entries [e_begin, e_begin + n_ent) (the first 64 already requested) and
   // value outliers: v_kv per token, 32 * v_kv entries from vbase.
-  const int64_t e_begin = be.e_begin, e_end = be.e_end;
+  const int32_t e_begin = be.e_begin, n_ent = be.n;
   const int v_ne = S.vout != nullptr ? kGroup * S.v_kv : 0;
   const int64_t vbase = blk * kGroup * S.v_kv;
 
@@ -491,7 +500,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     // one head: the key metadata ride in the chains (u, v, w), and the lookups of each
     // chain step are used at once
     float part[32];
-    qb[0] = cmul(pc.q[0], base);
+    qb[0] = base;                                    // q e^(-i t0 theta), see the caller
     const float2 c16 = cmul(qb[0], pc.r16);
     Uvw ca[2] = {uvw_of(qb[0], pc), uvw_of(c16, pc)};                    // token k
     Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
@@ -570,7 +579,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
   // even channel, the imaginary part for an odd one; te is the token's place in the
   // block, stored in the entry), and the two lanes of token t add the corrections of its
   // row, every other entry each in row order, then exchange their sums.
-  if (e_begin < e_end) {
+  if (n_ent > 0) {
 #pragma unroll
     for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
 #pragma unroll
@@ -579,8 +588,12 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
       ws.kc[2 * lane + 1][i] = kw1[i];
     }
     __builtin_amdgcn_wave_barrier();
-    auto window = [&](int64_t w0, uint32_t ent) {
-      if (w0 + lane < e_end) {
+    // this lane's token row relative to e_begin (unsigned: wraps, never traps; the
+    // clamps below keep every LDS index inside the window)
+    const int rlo = (int)((uint32_t)r.r0 - (uint32_t)e_begin);
+    const int rhi = (int)((uint32_t)r.r1 - (uint32_t)e_begin);
+    auto window = [&](int off, uint32_t ent) {
+      if (off + lane < n_ent) {
         const int te = (int)((ent >> 8) & (kGroup - 1));
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
@@ -597,8 +610,8 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
         }
       }
       __builtin_amdgcn_wave_barrier();
-      const int lo = (int)(max((int64_t)r.r0, w0) - w0);
-      const int hi = (int)(min((int64_t)r.r1, min(e_end, w0 + 64)) - w0);
+      const int lo = max(rlo, off) - off;
+      const int hi = min(rhi, min(n_ent, off + 64)) - off;
       float acc[GQ];
 #pragma unroll
       for (int j = 0; j < GQ; ++j) acc[j] = 0.f;
@@ -612,9 +625,9 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     };
     // the first window from the entries already in registers; more than 64 entries in
     // a block (rare) are loaded window by window
-    window(e_begin, be.ent);
-    for (int64_t w0 = e_begin + 64; w0 < e_end; w0 += 64)
-      window(w0, w0 + lane < e_end ? S.ent[w0 + lane] : 0u);
+    window(0, be.ent);
+    for (int off = 64; off < n_ent; off += 64)
+      window(off, off + lane < n_ent ? (S.ent + e_begin)[off + lane] : 0u);
   }
 
   // ---- softmax (lanes 2t and 2t+1 both carry the corrected score of token t)
@@ -872,14 +885,16 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel
                         : reinterpret_cast<const int32_t*>(S.vm);
     S.rp_step = a.csr_rowptr ? 1 : 0;
     S.ent = a.csr_ent + bh * a.csr_capacity;
-    S.csr_cap = a.csr_capacity;
+    S.csr_cap = (int32_t)a.csr_capacity;
     S.vout = a.v_out ? a.v_out + bt * a.v_kv : nullptr;
     S.v_kv = a.v_kv;
     S.scale_log2 = a.scale_log2;
     NuqBlockRegs<B> r0, r1;
     load_nuq_block<B>(r0, S, b0, lane);
-    // e^(-i t0 theta) of the current block, in fp64 from block to block
+    // e^(-i t0 theta) of the current block, in fp64 from block to block; with one query
+    // head the query is folded in (the block then starts from q e^(-i t0 theta) itself)
     double2 base = rot_at64(a.n_sink + (int64_t)b0 * kGroup, pc.theta);
+    if constexpr (GQ == 1) base = cmul64(base, make_double2(pc.q[0].x, pc.q[0].y));
     for (int i = b0; i < b1; i += 2) {
       const NuqBlockEntries e0 = load_block_entries<B>(S, i, r0, lane);
       load_nuq_block<B>(r1, S, min(i + 1, last), lane);
