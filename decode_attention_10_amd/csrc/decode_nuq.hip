@@ -164,27 +164,6 @@ __device__ __forceinline__ uint32_t pair_entry(const uint32_t* table, uint32_t i
                                             byte_times4<K>(idx4));
 }
 
-template <int B>
-__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int j) {
-  if constexpr (B == 4) {
-    const int jj = j & 7;
-    return (w[j >> 3] >> (8 * (jj & 3) + 4 * (jj >> 2))) & 15u;
-  } else if constexpr (B == 2) {
-    const int jj = j & 15;
-    return (w[j >> 4] >> (8 * (jj & 3) + 2 * (jj >> 2))) & 3u;
-  } else {
-    // without branches (the entry lanes of a wave hold any mix of tokens): m < 6, the
-    // whole code at bit 8k + 3(m % 2) of word m / 2; m = 6, 7, two bits at 8k + 6 of word
-    // m - 6 and the high bit at 8k + m of word 2
-    const int k = j & 3, m = j >> 2;
-    const bool whole = m < 6;
-    const uint32_t a = (w[whole ? m >> 1 : m - 6] >> (8 * k + (whole ? 3 * (m & 1) : 6))) &
-                       (whole ? 7u : 3u);
-    const uint32_t h = (w[2] >> (8 * k + (m & 7))) & (whole ? 0u : 1u);
-    return a | (h << 2);
-  }
-}
-
 __device__ __forceinline__ float lut_value(const uint16_t* lut, uint32_t c) {
   return f16_bits_to_f32(lut[c]);
 }
@@ -386,7 +365,6 @@ struct NuqWaveScratch {
   float ps[GQ][kGroup];      // window chunks: p_t of the chunk's tokens (scaled by 2^-e)
   uint16_t psh[GQ][kGroup];  // packed blocks: fp16 p_t * scale_t * 2^-e of the block's tokens
   float2 qb[GQ][64];         // q e^(-i t0 theta_i) per head and pair: the block's first token
-  uint32_t kc[kHeadDim][B];  // the block's key (later value) code words, per channel
   float corr[GQ][64];        // per CSR entry of the window: its score correction
   float pv[GQ][kGroup];      // p_t of the block's tokens (value outliers)
   uint32_t vmeta[kGroup];    // value scale / min of the block's tokens
@@ -575,18 +553,14 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
 
   // ---- outliers: token t's CSR entries replace the dequantized code by the exact value.
   // Entries are taken in windows of 64, one per lane: every entry lane computes its
-  // correction comp(q e^(-i (t0 + te) theta)) * (x - dequant(code)) (the real part for an
-  // even channel, the imaginary part for an odd one; te is the token's place in the
-  // block, stored in the entry), and the two lanes of token t add the corrections of its
-  // row, every other entry each in row order, then exchange their sums.
+  // correction comp(q e^(-i (t0 + te) theta)) * (x - dequant(0)) (an outlier's position
+  // stores code 0; the real part for an even channel, the imaginary part for an odd one;
+  // te is the token's place in the block, stored in the entry), and the two lanes of
+  // token t add the corrections of its row, every other entry each in row order, then
+  // exchange their sums.
   if (n_ent > 0) {
 #pragma unroll
     for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      ws.kc[2 * lane][i] = kw0[i];
-      ws.kc[2 * lane + 1][i] = kw1[i];
-    }
     __builtin_amdgcn_wave_barrier();
     // this lane's token row relative to e_begin (unsigned: wraps, never traps; the
     // clamps below keep every LDS index inside the window)
@@ -598,7 +572,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
-        const float khat = fmaf(sh.lutk[code_at<B>(ws.kc[col], te)], sh.ks[col], sh.km[col]);
+        const float khat = fmaf(sh.lutk[0], sh.ks[col], sh.km[col]);
         const float d = x - khat;
         const float2 e = sh.rot[te][pr];
         const bool odd = col & 1;
@@ -704,16 +678,11 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     st.o[j][1] = o1;
   }
 
-  // ---- value outliers: each token's entries replace the dequantized value by the exact
-  // one.  One lane per entry adds p_t * (x - v_hat) for its channel into LDS (the key
-  // code-word scratch now holds the value code words); each lane then takes its two
-  // channels' sums.
+  // ---- value outliers: each token's entries replace the dequantized value (of code 0,
+  // the code stored at an outlier) by the exact one.  One lane per entry adds
+  // p_t * (x - v_hat) for its channel into LDS; each lane then takes its two channels'
+  // sums.
   if (v_ne > 0) {
-#pragma unroll
-    for (int i = 0; i < B; ++i) {
-      ws.kc[2 * lane][i] = vw0[i];
-      ws.kc[2 * lane + 1][i] = vw1[i];
-    }
     if (!(lane & 1)) {
       ws.vmeta[t] = r.vmeta;
 #pragma unroll
@@ -728,7 +697,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
         const int d = (int)(ent & (kHeadDim - 1));
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
         const uint32_t vmw = ws.vmeta[te];
-        const float vhat = sh.lutv[code_at<B>(ws.kc[d], te)] * lo_f16(vmw) + hi_f16(vmw);
+        const float vhat = sh.lutv[0] * lo_f16(vmw) + hi_f16(vmw);
 #pragma unroll
         for (int j = 0; j < GQ; ++j) atomicAdd(&ws.vcorr[j][d], ws.pv[j][te] * (x - vhat));
       }

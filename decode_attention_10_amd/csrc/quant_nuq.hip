@@ -511,8 +511,10 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
           out = r < (uint32_t)cneed;
           ++r;
         }
-        const uint32_t c =
-            cinv == 0.0f ? 0u : nuq_code<B>((f16_bits_to_f32((uint16_t)x) - cmn) * cinv, md);
+        // an outlier's position stores code 0 (its exact value replaces the dequantized one)
+        const uint32_t c = (out || cinv == 0.0f)
+                               ? 0u
+                               : nuq_code<B>((f16_bits_to_f32((uint16_t)x) - cmn) * cinv, md);
         // the bit positions of pack_nuq_word for token j = 16 * half + jj
         if constexpr (B == 4) {
           w4[jj >> 3] |= (c & 15u) << (8 * (jj & 3) + 4 * ((jj & 7) >> 2));
@@ -826,7 +828,8 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
     uint32_t cw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      code[j] = g.y == 0.0f ? 0u : nuq_code<B>((xv(j) - g.x) * g.y, md);
+      // an outlier channel stores code 0 (its exact value replaces the dequantized one)
+      code[j] = (((outm >> j) & 1u) || g.y == 0.0f) ? 0u : nuq_code<B>((xv(j) - g.x) * g.y, md);
       cw[j >> 2] |= code[j] << (8 * (j & 3));
     }
     *reinterpret_cast<uint4*>(&ct[t][c0]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);

@@ -40,8 +40,8 @@
  *  - Outliers (nuq keys, outlier_bp > 0): per (batch, head, channel) the
  *    ceil(n * outlier_bp / 10000) entries of largest fp16 magnitude over the
  *    n quantized tokens (ties: lower token first) are kept exactly in a CSR
- *    matrix and excluded from the channel's min/max.  A code is still stored
- *    for them; attention uses the exact value.
+ *    matrix and excluded from the channel's min/max.  Their positions store
+ *    code 0; attention uses the exact value.  (Value outliers likewise.)
  *  - Q-Norm (nuq, qnorm = 1; KVQuant review, "Proposed method": the dequantized
  *    distribution is matched to the statistics taken before quantization): per
  *    vector, after its codes, (scale, min) become (a * scale, a * min + b) with

@@ -377,7 +377,7 @@ class StreamingCache:
 # book reproduces the uniform quantizer; each element goes to the nearest code
 # book level (ties to the even index); outliers are the ceil(n * bp / 10000)
 # largest magnitudes of the vector (ties: lower index first), kept exactly and
-# excluded from the min/max; codes are still stored at outlier positions.
+# excluded from the min/max; outlier positions store code 0.
 # --------------------------------------------------------------------------
 def outlier_count(n: int, bp: int) -> int:
     """ceil(n * bp / 10000) in integer arithmetic."""
@@ -476,6 +476,11 @@ def nuq_quantize_vector(x_bits: np.ndarray, lut_bits: np.ndarray, n_outliers: in
         inv = np.float32(1.0) / s
         xn = (x - mn) * inv
         codes = nuq_code(xn, lut)
+    # An outlier's exact value replaces its dequantized one in attention, so the code
+    # stored at its position is never read for its value; the pages leave it open.  Code 0
+    # is stored there (reading: any fixed code works), which lets a decoder form the
+    # replaced value from the metadata alone.
+    codes[out_idx] = 0
     if qnorm:
         scale_h, min_h = qnorm_params(x[dense], codes[dense], lut, scale_h, min_h)
         s, mn = f16_to_f32(scale_h), f16_to_f32(min_h)

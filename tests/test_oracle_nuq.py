@@ -108,6 +108,7 @@ def test_outlier_invariants_keys(bp):
             assert O.f16_to_f32(mn[d]) == xd.min() + np.float32(0)
     x = O.f16_to_f32(k)
     assert np.array_equal(xh[is_out], x[is_out])
+    assert not codes[is_out].any()                              # outlier positions: code 0
     if bp == 0:
         c0, s0, m0, _, xh0 = O.nuq_quantize_vector(k[:, 5], lut, 0)
         assert np.array_equal(codes[:, 5], c0) and sc[5] == s0
@@ -183,6 +184,7 @@ def test_value_outliers_by_hand():
     assert xh[0, 2] == 9.0
     s = O.f16_to_f32(sc[0])
     assert np.array_equal(codes[0, [0, 1, 3]], np.rint((np.float32([1, 2, 3]) - 1) / s))
+    assert codes[0, 2] == 0                       # an outlier's position stores code 0
 
 
 def test_nuq_head_value_outliers_change_only_the_outlier_values():
