@@ -45,46 +45,15 @@ __device__ __forceinline__ Mids<B> load_mids(const uint16_t* lut) {
   return r;
 }
 
-// Index of the nearest code-book level (ties to the even index).  The code is the
-// number of midpoints below xn, found by a binary search over the ascending midpoints:
-// bit by bit from the top, each step comparing with the midpoint its higher bits pick.
-// The picks are select trees on those comparison results (constant indices, so the
-// midpoints stay in registers).  A value exactly on the midpoint above an odd level goes
-// to the even level above it.
+// Index of the nearest code-book level (ties to the even index): the number of
+// midpoints below xn, plus one for a midpoint equal to xn above an odd level (the tie
+// then goes to the even level above).  The code book ascends strictly, so its midpoints
+// do too (each is the exact fp32 half-sum of two fp16 levels) and the count is the code.
 template <int B>
 __device__ __forceinline__ uint32_t nuq_code(float xn, const Mids<B>& md) {
-  // the midpoints as values: a conditional between two array elements would otherwise be
-  // a select of their addresses, which keeps the array out of registers
-  float m[(1 << B) - 1];
+  uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < (1 << B) - 1; ++i) m[i] = md.m[i];
-  const auto v = [&](int i) -> float { return m[i]; };
-  uint32_t c;
-  float mo;                                        // midpoint above level c when c is odd
-  if constexpr (B == 2) {
-    const bool b1 = xn > v(1);
-    const bool b2 = xn > (b1 ? v(2) : v(0));
-    c = 2u * b1 + b2;
-    mo = v(1);
-  } else if constexpr (B == 3) {
-    const bool b1 = xn > v(3);
-    const bool b2 = xn > (b1 ? v(5) : v(1));
-    const bool b3 = xn > (b1 ? (b2 ? v(6) : v(4)) : (b2 ? v(2) : v(0)));
-    c = 4u * b1 + 2u * b2 + b3;
-    mo = b1 ? v(5) : (b2 ? v(3) : v(1));
-  } else {
-    const bool b1 = xn > v(7);
-    const bool b2 = xn > (b1 ? v(11) : v(3));
-    const bool b3 = xn > (b1 ? (b2 ? v(13) : v(9)) : (b2 ? v(5) : v(1)));
-    const float q0 = b2 ? (b3 ? v(6) : v(4)) : (b3 ? v(2) : v(0));
-    const float q1 = b2 ? (b3 ? v(14) : v(12)) : (b3 ? v(10) : v(8));
-    const bool b4 = xn > (b1 ? q1 : q0);
-    c = 8u * b1 + 4u * b2 + 2u * b3 + b4;
-    const float o0 = b2 ? (b3 ? v(7) : v(5)) : (b3 ? v(3) : v(1));
-    const float o1 = b2 ? (b3 ? v(14) : v(13)) : (b3 ? v(11) : v(9));
-    mo = b1 ? o1 : o0;
-  }
-  if ((c & 1u) && c < (uint32_t)((1 << B) - 1) && xn == mo) c += 1;
+  for (int i = 0; i < (1 << B) - 1; ++i) c += (i & 1) ? (xn >= md.m[i]) : (xn > md.m[i]);
   return c;
 }
 
@@ -490,7 +459,8 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
     {
       // Two lanes of one wave per channel, tokens 0..15 and 16..31.  The outlier rank of
       // ties at the threshold runs in token order: the second half's continues from the
-      // first half's count.  Codes go straight into the channel's B code words.
+      // first half's count.  Codes are gathered one per byte (token 4mm + k of the half
+      // in byte k of cb[mm]) and turned into the channel's B code words at the end.
       const int ch = tid >> 1, half = tid & 1;
       uint32_t xs[16];
       uint32_t my_ties = 0;
@@ -500,59 +470,70 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         my_ties += (int)(xs[jj] & 0x7FFFu) == cT ? 1u : 0u;
       }
       const uint32_t other_ties = __shfl_xor(my_ties, 1);
-      uint32_t r = crank + (half ? other_ties : 0u);
-      uint32_t lo = 0u, w4[2] = {0u, 0u}, w3[3] = {0u, 0u, 0u};
+      uint32_t cb[4] = {0u, 0u, 0u, 0u};
+      uint32_t outbits = 0u, tiebits = 0u;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
         const uint32_t x = xs[jj];
         const int mag = (int)(x & 0x7FFFu);
-        bool out = mag > cT;
-        if (mag == cT) {
-          out = r < (uint32_t)cneed;
-          ++r;
-        }
+        const bool out = mag > cT;                 // ties at cT: below
+        tiebits |= (uint32_t)(mag == cT) << jj;
+        outbits |= (uint32_t)out << jj;
         // an outlier's position stores code 0 (its exact value replaces the dequantized one)
         const uint32_t c = (out || cinv == 0.0f)
                                ? 0u
                                : nuq_code<B>((f16_bits_to_f32((uint16_t)x) - cmn) * cinv, md);
-        // the bit positions of pack_nuq_word for token j = 16 * half + jj
-        if constexpr (B == 4) {
-          w4[jj >> 3] |= (c & 15u) << (8 * (jj & 3) + 4 * ((jj & 7) >> 2));
-        } else if constexpr (B == 2) {
-          lo |= (c & 3u) << (8 * (jj & 3) + 2 * (jj >> 2));
-        } else {
-          // m = 4 * half + jj / 4: half 0 fills words 0 and 1 (m = 0..3); half 1 fills word
-          // 2 (m = 4, 5) and the m = 6, 7 fields split over words 0 / 1 and 2
-          const int k = jj & 3, mm = jj >> 2;
-          if (half == 0) {
-            w3[mm >> 1] |= c << (8 * k + 3 * (mm & 1));
-          } else if (mm < 2) {
-            w3[2] |= c << (8 * k + 3 * mm);
-          } else {
-            w3[mm - 2] |= (c & 3u) << (8 * k + 6);
-            w3[2] |= (c >> 2) << (8 * k + 4 + mm);
+        cb[jj >> 2] |= c << (8 * (jj & 3));
+      }
+      if (__any(tiebits != 0u)) {
+        // ties at the threshold, in token order: the first cneed of the channel's ties
+        // (counted from crank, the ties of the earlier chunks) are outliers
+        uint32_t r = crank + (half ? other_ties : 0u);
+        uint32_t tbits = tiebits;
+        while (tbits) {
+          const int jj = __builtin_ctz(tbits);
+          tbits &= tbits - 1u;
+          if (r < (uint32_t)cneed) {
+            outbits |= 1u << jj;
+            cb[jj >> 2] &= ~(0xFFu << (8 * (jj & 3)));
           }
-        }
-        const int j = 16 * half + jj;
-        if (out) atomicOr(&om[j][ch >> 5], 1u << (ch & 31));
-        if (a.qnorm && !out) {
-          exact_add(qs, x);
-          atomicAdd(&qh[ch][c], 1u);
+          ++r;
         }
       }
       crank += my_ties + other_ties;
+      for (uint32_t ob = outbits; ob != 0u; ob &= ob - 1u) {
+        const int jj = __builtin_ctz(ob);
+        atomicOr(&om[16 * half + jj][ch >> 5], 1u << (ch & 31));
+      }
+      if (a.qnorm) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          if (!((outbits >> jj) & 1u)) {
+            exact_add(qs, xs[jj]);
+            atomicAdd(&qh[ch][(cb[jj >> 2] >> (8 * (jj & 3))) & 0xFFu], 1u);
+          }
+        }
+      }
       uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
       if constexpr (B == 4) {
-        kw[2 * half] = w4[0];
-        kw[2 * half + 1] = w4[1];
+        // word 2 half + i holds tokens 8i..8i+7 of the half, token 4mm + k at 8k + 4(mm % 2)
+        kw[2 * half] = cb[0] | (cb[1] << 4);
+        kw[2 * half + 1] = cb[2] | (cb[3] << 4);
       } else if constexpr (B == 2) {
-        kw[half] = lo;
+        kw[half] = cb[0] | (cb[1] << 2) | (cb[2] << 4) | (cb[3] << 6);
       } else {
-        // the two halves' fields are disjoint: OR them, half 0 writes words 0 and 1,
-        // half 1 word 2
-        const uint32_t x0 = w3[0] | __shfl_xor(w3[0], 1);
-        const uint32_t x1 = w3[1] | __shfl_xor(w3[1], 1);
-        const uint32_t x2 = w3[2] | __shfl_xor(w3[2], 1);
+        // half 0: m = mm, words 0 and 1 (m = 0..3).  Half 1: m = 4 + mm, word 2 (m = 4, 5)
+        // and the m = 6, 7 fields split over words 0 / 1 (low bits at 8k + 6) and word 2
+        // (high bit at 8k + m).  The halves' fields are disjoint: OR them.
+        const uint32_t p01 = cb[0] | (cb[1] << 3), p23 = cb[2] | (cb[3] << 3);
+        const uint32_t h6 = ((cb[2] >> 2) & 0x01010101u) << 6;
+        const uint32_t h7 = ((cb[3] >> 2) & 0x01010101u) << 7;
+        const uint32_t w0 = half ? (cb[2] & 0x03030303u) << 6 : p01;
+        const uint32_t w1 = half ? (cb[3] & 0x03030303u) << 6 : p23;
+        const uint32_t w2 = half ? p01 | h6 | h7 : 0u;
+        const uint32_t x0 = w0 | __shfl_xor(w0, 1);
+        const uint32_t x1 = w1 | __shfl_xor(w1, 1);
+        const uint32_t x2 = w2 | __shfl_xor(w2, 1);
         if (half == 0) {
           kw[0] = x0;
           kw[1] = x1;
