@@ -57,6 +57,53 @@ __device__ __forceinline__ uint32_t nuq_code(float xn, const Mids<B>& md) {
   return c;
 }
 
+// The same search in one comparison.  The level axis [0, 2^B) is cut into cells of half a
+// level; a cell holds at most one midpoint of a code book whose levels lie in [0, 2^B - 1]
+// at least half a level apart (checked when the cells are built: otherwise the counting
+// search above is used).  Cell i keeps the number of midpoints below it and its own
+// midpoint (+inf if none), one ulp lower above an odd level so that xn > it settles a tie
+// toward the even level.  xn * 2 is exact, so every xn lands in the cell that holds it.
+template <int B>
+struct CodeCells {
+  static constexpr int N = 2 << B;
+  float2 e[N];                      // (threshold, code below the cell as float bits)
+};
+
+// Built by the first N threads; returns, to every thread of the block (a barrier), whether
+// the cells decide every code.
+template <int B>
+__device__ bool build_code_cells(CodeCells<B>& cc, const Mids<B>& md, int tid) {
+  constexpr int NM = (1 << B) - 1;
+  int bad = 0;
+  if (tid < CodeCells<B>::N) {
+    const float lo = 0.5f * (float)tid, hi = 0.5f * (float)(tid + 1);
+    uint32_t below = 0;
+    int inside = 0;
+    float thr = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      const float m = md.m[j];
+      if (m < lo) {
+        ++below;
+      } else if (m < hi) {
+        ++inside;
+        thr = (j & 1) ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, m) - 1u) : m;
+      }
+    }
+    bad = inside > 1 || (tid == 0 && (below > 0 || (inside == 1 && thr <= 0.0f))) ||
+          (tid == CodeCells<B>::N - 1 && md.m[NM - 1] >= hi);
+    cc.e[tid] = make_float2(thr, __builtin_bit_cast(float, below));
+  }
+  return !__syncthreads_or(bad);
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t nuq_code_cells(float xn, const CodeCells<B>& cc) {
+  const int cell = min(max((int)(xn * 2.0f), 0), CodeCells<B>::N - 1);
+  const float2 e = cc.e[cell];
+  return __builtin_bit_cast(uint32_t, e.y) + (xn > e.x ? 1u : 0u);
+}
+
 // (scale, min) of a dense range for B-bit codes: scale = (max - min) / (2^B - 1).
 __device__ __forceinline__ void params_nuq(float mn, float mx, int bits, uint32_t* meta,
                                            float* mn_o, float* inv_o) {
@@ -424,10 +471,12 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
   __shared__ uint32_t oms[2][kGroup][4];
   __shared__ int64_t rs[kGroup];            // first CSR entry of each token of the tile
   __shared__ uint32_t qh[kHeadDim][16];     // Q-Norm: dense code counts per channel
+  __shared__ CodeCells<B> cells;
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
   const Mids<B> md = load_mids<B>(a.lut);
+  const bool by_cells = build_code_cells<B>(cells, md, tid);
   ExactSums qs;
   exact_zero(qs);
   if (a.qnorm)
@@ -480,9 +529,11 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         tiebits |= (uint32_t)(mag == cT) << jj;
         outbits |= (uint32_t)out << jj;
         // an outlier's position stores code 0 (its exact value replaces the dequantized one)
-        const uint32_t c = (out || cinv == 0.0f)
-                               ? 0u
-                               : nuq_code<B>((f16_bits_to_f32((uint16_t)x) - cmn) * cinv, md);
+        uint32_t c = 0u;
+        if (!out && cinv != 0.0f) {
+          const float xn = (f16_bits_to_f32((uint16_t)x) - cmn) * cinv;
+          c = by_cells ? nuq_code_cells<B>(xn, cells) : nuq_code<B>(xn, md);
+        }
         cb[jj >> 2] |= c << (8 * (jj & 3));
       }
       if (__any(tiebits != 0u)) {
@@ -726,12 +777,14 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
   __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
   __shared__ float2 st[kGroup];
   __shared__ uint32_t qh[kGroup][16];       // Q-Norm: dense code counts per token
+  __shared__ CodeCells<B> cells;
   const int64_t job = blockIdx.x;
   const int blk = (int)(job % a.n_blocks);
   const int64_t bh = job / a.n_blocks;
   const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
   const int tid = threadIdx.x;
   const Mids<B> md = load_mids<B>(a.lut);
+  const bool by_cells = build_code_cells<B>(cells, md, tid);
   {
     const int t = tid >> 3, c = (tid & 7) * 16;
     const uint4* p = reinterpret_cast<const uint4*>(a.v + b * a.sb + h * a.sh +
@@ -810,7 +863,11 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       // an outlier channel stores code 0 (its exact value replaces the dequantized one)
-      code[j] = (((outm >> j) & 1u) || g.y == 0.0f) ? 0u : nuq_code<B>((xv(j) - g.x) * g.y, md);
+      code[j] = 0u;
+      if (!((outm >> j) & 1u) && g.y != 0.0f) {
+        const float xn = (xv(j) - g.x) * g.y;
+        code[j] = by_cells ? nuq_code_cells<B>(xn, cells) : nuq_code<B>(xn, md);
+      }
       cw[j >> 2] |= code[j] << (8 * (j & 3));
     }
     *reinterpret_cast<uint4*>(&ct[t][c0]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);

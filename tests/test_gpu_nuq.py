@@ -93,6 +93,55 @@ def test_nuq_quantize_bit_exact(B, H, n, bp, lut, v_bp):
             _check_head(c, b, h, ref, n, bp)
 
 
+@pytest.mark.parametrize("lut", ["ident", "close"])
+def test_nuq_quantize_exact_midpoint_ties(lut):
+    """Keys and values on the half-integer grid of [0, 7] (fp16 exact): with the identity
+    code book every half-integer is a midpoint, and min 0 / max 7 give scale 1, so many
+    normalized values land exactly on a midpoint (ties go to the even level).  "close"
+    has levels a quarter apart, so the quantizers cannot use their one-comparison cell
+    table and fall back to the counting search."""
+    B, H, n = 1, 2, 256
+    rng = np.random.default_rng(17)
+    grid = rng.integers(0, 15, size=(B, H, n, 128)).astype(np.float32) * np.float32(0.5)
+    grid[..., 0, :] = 0.0
+    grid[..., 1, :] = 7.0                             # every channel spans [0, 7]
+    grid[..., :, 0] = 0.0
+    grid[..., :, 1] = 7.0                             # every token spans [0, 7]
+    k = grid.astype(np.float16).view(np.uint16)
+    v = k.copy()
+    if lut == "ident":
+        L = np.arange(8).astype(np.float16).view(np.uint16)
+    else:
+        L = np.array([0.0, 0.25, 0.5, 1.0, 3.0, 5.0, 6.75, 7.0], np.float16).view(np.uint16)
+    c = _nuq_cache(B, H, n + 64, 0, 0, L, L)
+    _quantize(c, k, v, n)
+    for h in range(H):
+        ref = O.nuq_head(k[0, h], v[0, h], L, L, 0, n, 0, 0.0)
+        _check_head(c, 0, h, ref, n, 0)
+
+
+def test_nuq_keys_and_values_quantized_on_two_streams():
+    """The key and value quantizers write disjoint buffers: issued on two streams at once
+    they leave the same bytes as one after the other."""
+    B, H, n = 1, 2, 4096 + 128
+    k, v = _kv(41, B, H, n)
+    L = S.nuq3_lut()
+    ref = _nuq_cache(B, H, n, 0, 100, L, L, 100)
+    _quantize(ref, k, v, n)
+    c = _nuq_cache(B, H, n, 0, 100, L, L, 100)
+    kd, vd = dev(k), dev(v)
+    wsb = K.kvq_workspace_bytes(c.c, 0, K.KVQ_OP_QUANTIZE_KEYS)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    K.kvq_quantize_keys(c.c, kd, H * n * 128, n * 128, 128, 0, n, ws, wsb, stream=main)
+    K.kvq_quantize_values(c.c, vd, H * n * 128, n * 128, 128, 0, n, stream=side)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_meta", "v_codes", "v_meta", "k_csr_rowptr", "k_csr_ent", "v_out"):
+        assert torch.equal(c.buf(name), ref.buf(name)), name
+
+
 def test_nuq_keys_many_ties_at_the_threshold():
     """Values drawn from a few levels so that the k-th largest magnitude is shared by
     many tokens: the earliest ones must become the outliers."""
