@@ -429,37 +429,39 @@ __global__ void nuq_finalize_kernel(NuqKeysArgs a) {
   a.norm[i * 2 + 1] = inv;
 }
 
-// Word w of one channel's B code words of a block from the codes ct[token][channel]:
-// token j in byte j % 4 of its words (B = 2: words 0/1 hold tokens 0..15 / 16..31 at
-// 8*(j%4) + 2*(j%16/4); B = 4: word w holds tokens 8w..8w+7 at 8*(j%4) + 4*(j%8/4);
-// B = 3, m = j / 4: for m < 6 the code at 8*(j%4) + 3*(m%2) of word m/2, for m = 6, 7
-// the low two bits at 8*(j%4) + 6 of word m - 6 and the high bit at 8*(j%4) + m of
-// word 2).
-__device__ __forceinline__ uint32_t pack_nuq_word(const uint8_t (*ct)[kHeadDim], int d, int w,
-                                                  int bits_per_code) {
-  uint32_t bits = 0;
-  if (bits_per_code == 4) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bits |= (uint32_t)(ct[8 * w + j][d] & 15u) << (8 * (j & 3) + 4 * (j >> 2));
-  } else if (bits_per_code == 2) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      bits |= (uint32_t)(ct[16 * w + j][d] & 3u) << (8 * (j & 3) + 2 * (j >> 2));
+
+// The B code words of a channel's 32-token block from its codes one per byte: this lane
+// holds tokens 16 * half + 4mm + k in byte k of cb[mm], its partner lane (lane ^ 1) the
+// other half (the layout of nuq_code_fields).  Both lanes of the pair must call it.
+template <int B>
+__device__ __forceinline__ void store_code_words(uint32_t* kw, const uint32_t (&cb)[4],
+                                                 int half) {
+  if constexpr (B == 4) {
+    // word 2 half + i holds tokens 8i..8i+7 of the half, token 4mm + k at 8k + 4(mm % 2)
+    kw[2 * half] = cb[0] | (cb[1] << 4);
+    kw[2 * half + 1] = cb[2] | (cb[3] << 4);
+  } else if constexpr (B == 2) {
+    kw[half] = cb[0] | (cb[1] << 2) | (cb[2] << 4) | (cb[3] << 6);
   } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // whole codes of m = 2w, 2w + 1
-      bits |= (uint32_t)(ct[8 * w + k][d] & 7u) << (8 * k);
-      bits |= (uint32_t)(ct[8 * w + 4 + k][d] & 7u) << (8 * k + 3);
-      if (w < 2) bits |= (uint32_t)(ct[24 + 4 * w + k][d] & 3u) << (8 * k + 6);   // m = 6 + w
-      else {
-        bits |= (uint32_t)(ct[24 + k][d] >> 2) << (8 * k + 6);                     // m = 6
-        bits |= (uint32_t)(ct[28 + k][d] >> 2) << (8 * k + 7);                     // m = 7
-      }
+    // half 0: m = mm, words 0 and 1 (m = 0..3).  Half 1: m = 4 + mm, word 2 (m = 4, 5) and
+    // the m = 6, 7 fields split over words 0 / 1 (low bits at 8k + 6) and word 2 (high bit
+    // at 8k + m).  The halves' fields are disjoint: OR them.
+    const uint32_t p01 = cb[0] | (cb[1] << 3), p23 = cb[2] | (cb[3] << 3);
+    const uint32_t h6 = ((cb[2] >> 2) & 0x01010101u) << 6;
+    const uint32_t h7 = ((cb[3] >> 2) & 0x01010101u) << 7;
+    const uint32_t w0 = half ? (cb[2] & 0x03030303u) << 6 : p01;
+    const uint32_t w1 = half ? (cb[3] & 0x03030303u) << 6 : p23;
+    const uint32_t w2 = half ? p01 | h6 | h7 : 0u;
+    const uint32_t x0 = w0 | __shfl_xor(w0, 1);
+    const uint32_t x1 = w1 | __shfl_xor(w1, 1);
+    const uint32_t x2 = w2 | __shfl_xor(w2, 1);
+    if (half == 0) {
+      kw[0] = x0;
+      kw[1] = x1;
+    } else {
+      kw[2] = x2;
     }
   }
-  return bits;
 }
 
 // ---- 7: codes and CSR rows ---------------------------------------------------------
@@ -566,32 +568,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         }
       }
       uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
-      if constexpr (B == 4) {
-        // word 2 half + i holds tokens 8i..8i+7 of the half, token 4mm + k at 8k + 4(mm % 2)
-        kw[2 * half] = cb[0] | (cb[1] << 4);
-        kw[2 * half + 1] = cb[2] | (cb[3] << 4);
-      } else if constexpr (B == 2) {
-        kw[half] = cb[0] | (cb[1] << 2) | (cb[2] << 4) | (cb[3] << 6);
-      } else {
-        // half 0: m = mm, words 0 and 1 (m = 0..3).  Half 1: m = 4 + mm, word 2 (m = 4, 5)
-        // and the m = 6, 7 fields split over words 0 / 1 (low bits at 8k + 6) and word 2
-        // (high bit at 8k + m).  The halves' fields are disjoint: OR them.
-        const uint32_t p01 = cb[0] | (cb[1] << 3), p23 = cb[2] | (cb[3] << 3);
-        const uint32_t h6 = ((cb[2] >> 2) & 0x01010101u) << 6;
-        const uint32_t h7 = ((cb[3] >> 2) & 0x01010101u) << 7;
-        const uint32_t w0 = half ? (cb[2] & 0x03030303u) << 6 : p01;
-        const uint32_t w1 = half ? (cb[3] & 0x03030303u) << 6 : p23;
-        const uint32_t w2 = half ? p01 | h6 | h7 : 0u;
-        const uint32_t x0 = w0 | __shfl_xor(w0, 1);
-        const uint32_t x1 = w1 | __shfl_xor(w1, 1);
-        const uint32_t x2 = w2 | __shfl_xor(w2, 1);
-        if (half == 0) {
-          kw[0] = x0;
-          kw[1] = x1;
-        } else {
-          kw[2] = x2;
-        }
-      }
+      store_code_words<B>(kw, cb, half);
     }
     __syncthreads();
     if (a.rowptr != nullptr) {
@@ -771,53 +748,54 @@ __device__ uint32_t value_outliers(const uint32_t (&xw)[8], int part, int kv) {
 // ---- values: per token over all channels --------------------------------------------
 // VOUT: the cache keeps per-token value outliers (an instance of its own, so that the
 // search's registers do not lower the occupancy of the plain case).
+// Values: per token over its D channels (with VOUT, dense-and-sparse: the token's kv
+// largest magnitudes kept exactly).  A workgroup takes kValueTiles consecutive 32-token
+// blocks of one head.  Per block, first eight threads per token (16 channels each)
+// gather the token's outliers, dense min / max and metadata, then two threads per
+// channel (16 tokens each) code the block and write the channel's code words.  Tiles,
+// statistics and outlier masks are double-buffered, so one barrier per block separates
+// the two roles.
+constexpr int kValueTiles = 16;
+
 template <int B, bool VOUT>
 __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArgs a) {
-  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
-  __shared__ __align__(16) uint8_t ct[kGroup][kHeadDim];
-  __shared__ float2 st[kGroup];
+  __shared__ __align__(16) uint16_t tiles[2][kGroup][kHeadDim];
+  __shared__ float2 sts[2][kGroup];         // per token: min, 1 / scale (0: all codes 0)
+  __shared__ uint16_t oms[2][kGroup][8];    // per token: outlier channels, 16 per word
   __shared__ uint32_t qh[kGroup][16];       // Q-Norm: dense code counts per token
   __shared__ CodeCells<B> cells;
-  const int64_t job = blockIdx.x;
-  const int blk = (int)(job % a.n_blocks);
-  const int64_t bh = job / a.n_blocks;
+  const int groups = (a.n_blocks + kValueTiles - 1) / kValueTiles;
+  const int64_t bh = blockIdx.x / groups;
+  const int grp = (int)(blockIdx.x % groups);
   const int64_t b = bh / a.kv_heads, h = bh % a.kv_heads;
   const int tid = threadIdx.x;
   const Mids<B> md = load_mids<B>(a.lut);
   const bool by_cells = build_code_cells<B>(cells, md, tid);
-  {
-    const int t = tid >> 3, c = (tid & 7) * 16;
-    const uint4* p = reinterpret_cast<const uint4*>(a.v + b * a.sb + h * a.sh +
-                                                    ((int64_t)blk * kGroup + t) * a.st + c);
-    const uint4 u0 = p[0], u1 = p[1];
-    uint4* dd = reinterpret_cast<uint4*>(&tile[t][c]);
-    dd[0] = u0;
-    dd[1] = u1;
-  }
-  uint32_t outm = 0;                        // this thread's outlier channels (bits)
-  if (a.qnorm)
-    for (int i = tid; i < kGroup * 16; i += kThreads) (&qh[0][0])[i] = 0u;
-  __syncthreads();
-  // 8 threads per token (same wave), 16 channels each; the thread's 16 fp16 values are
-  // read from LDS once, as two 16-byte vectors (two values per word)
-  const int t = tid >> 3, part = tid & 7, c0 = part * 16;
-  uint32_t xw[8];
-  {
-    const uint4* rp = reinterpret_cast<const uint4*>(&tile[t][c0]);
-    const uint4 r0 = rp[0], r1 = rp[1];
-    xw[0] = r0.x; xw[1] = r0.y; xw[2] = r0.z; xw[3] = r0.w;
-    xw[4] = r1.x; xw[5] = r1.y; xw[6] = r1.z; xw[7] = r1.w;
-  }
-  const auto xv = [&](int j) -> float { return (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]); };
-  {
-    const uint16_t* row = &tile[t][c0];
-    outm = VOUT ? value_outliers(xw, part, a.kv) : 0u;
-    // min / max of the dense channels, then combine
+  const int t = tid >> 3, part = tid & 7;   // token role
+  const int ch = tid >> 1, half = tid & 1;  // channel role
+  const int blk0 = grp * kValueTiles, blk1 = min(a.n_blocks, blk0 + kValueTiles);
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int buf = (blk - blk0) & 1;
+    const int64_t tok = a.tok0 + (int64_t)blk * kGroup + t;
+    // ---- token role: this thread's 16 channels, straight from HBM into registers (and
+    // the tile for the channel role)
+    uint32_t xw[8];
+    {
+      const uint4* p = reinterpret_cast<const uint4*>(
+          a.v + b * a.sb + h * a.sh + ((int64_t)blk * kGroup + t) * a.st + part * 16);
+      const uint4 u0 = p[0], u1 = p[1];
+      uint4* d = reinterpret_cast<uint4*>(&tiles[buf][t][part * 16]);
+      d[0] = u0;
+      d[1] = u1;
+      xw[0] = u0.x; xw[1] = u0.y; xw[2] = u0.z; xw[3] = u0.w;
+      xw[4] = u1.x; xw[5] = u1.y; xw[6] = u1.z; xw[7] = u1.w;
+    }
+    const uint32_t outm = VOUT ? value_outliers(xw, part, a.kv) : 0u;
     float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (!((outm >> j) & 1u)) {
-        const float x = xv(j);
+        const float x = (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
       }
@@ -827,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
       mn = fminf(mn, __shfl_xor(mn, o));
       mx = fmaxf(mx, __shfl_xor(mx, o));
     }
-    if (mn > mx) mn = mx = 0.0f;          // every channel an outlier
+    if (mn > mx) mn = mx = 0.0f;            // every channel an outlier
     if (VOUT) {
       // this thread's outliers, channels ascending, after those of the lower parts
       const uint32_t mine = (uint32_t)__builtin_popcount(outm);
@@ -838,68 +816,66 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
         if (part >= o) before += x;
       }
       before -= mine;
-      const int64_t tok = a.tok0 + (int64_t)blk * kGroup + t;
       uint32_t* dst = a.v_out + (bh * a.cap_tokens + tok) * a.kv + before;
       uint32_t m = outm;
       for (int i = 0; m != 0u; ++i) {
         const int j = __builtin_ctz(m);
         m &= m - 1u;
-        dst[i] = (uint32_t)(part * 16 + j) | ((uint32_t)row[j] << 16);
+        dst[i] = (uint32_t)(part * 16 + j) | (((xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
       }
     }
+    oms[buf][t][part] = (uint16_t)outm;
+    uint32_t meta;
+    float m0, inv;
+    params_nuq(mn, mx, a.bits, &meta, &m0, &inv);
     if (part == 0) {
-      uint32_t meta;
-      float m0, inv;
-      params_nuq(mn, mx, a.bits, &meta, &m0, &inv);
-      a.v_meta[bh * a.cap_tokens + a.tok0 + (int64_t)blk * kGroup + t] = meta;
-      st[t] = make_float2(m0, inv);
+      a.v_meta[bh * a.cap_tokens + tok] = meta;
+      sts[buf][t] = make_float2(m0, inv);
     }
-  }
-  __syncthreads();
-  uint32_t code[16];
-  {
-    const float2 g = st[t];
-    uint32_t cw[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      // an outlier channel stores code 0 (its exact value replaces the dequantized one)
-      code[j] = 0u;
-      if (!((outm >> j) & 1u) && g.y != 0.0f) {
-        const float xn = (xv(j) - g.x) * g.y;
-        code[j] = by_cells ? nuq_code_cells<B>(xn, cells) : nuq_code<B>(xn, md);
-      }
-      cw[j >> 2] |= code[j] << (8 * (j & 3));
-    }
-    *reinterpret_cast<uint4*>(&ct[t][c0]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-  }
-  __syncthreads();
-  if (a.qnorm) {
-    // Q-Norm: the token's dense sums and code counts, then its metadata again
     ExactSums es;
-    exact_zero(es);
+    if (a.qnorm) {
+      exact_zero(es);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (!((outm >> j) & 1u)) {
-        exact_add(es, (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-        atomicAdd(&qh[t][code[j]], 1u);
+      for (int j = 0; j < 16; ++j)
+        if (!((outm >> j) & 1u)) exact_add(es, (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) exact_merge_xor(es, o);
+      qh[t][2 * part] = qh[t][2 * part + 1] = 0u;
+    }
+    __syncthreads();
+    // ---- channel role: channel ch of tokens 16 half .. 16 half + 15, codes one per byte
+    {
+      uint32_t cb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int tt = 16 * half + jj;
+        const float2 g = sts[buf][tt];
+        const bool out = VOUT && ((oms[buf][tt][ch >> 4] >> (ch & 15)) & 1u);
+        uint32_t c = 0u;
+        if (!out && g.y != 0.0f) {
+          const float xn = (f16_bits_to_f32(tiles[buf][tt][ch]) - g.x) * g.y;
+          c = by_cells ? nuq_code_cells<B>(xn, cells) : nuq_code<B>(xn, md);
+        }
+        cb[jj >> 2] |= c << (8 * (jj & 3));
+        if (a.qnorm && !out) atomicAdd(&qh[tt][c], 1u);
+      }
+      uint32_t* kw = a.v_codes + (bh * a.cap_blocks + a.tok0 / kGroup + blk) * (kHeadDim * B) +
+                     ch * B;
+      store_code_words<B>(kw, cb, half);
+    }
+    if (a.qnorm) {
+      // Q-Norm: the token's dense sums and code counts, then its metadata again
+      __syncthreads();
+      if (part == 0) {
+        double sx, sxx;
+        exact_to_f64(es, &sx, &sxx);
+        uint32_t n = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) n += qh[t][c];
+        a.v_meta[bh * a.cap_tokens + tok] = qnorm_meta(meta, sx, sxx, qh[t], n, a.lut, a.bits);
       }
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) exact_merge_xor(es, o);
-    double sx, sxx;
-    exact_to_f64(es, &sx, &sxx);
-    __syncthreads();
-    if ((tid & 7) == 0) {
-      uint32_t n = 0;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) n += qh[t][c];
-      uint32_t* meta = a.v_meta + bh * a.cap_tokens + a.tok0 + (int64_t)blk * kGroup + t;
-      *meta = qnorm_meta(*meta, sx, sxx, qh[t], n, a.lut, a.bits);
-    }
   }
-  const int64_t dst = bh * a.cap_blocks + a.tok0 / kGroup + blk;
-  for (int wi = tid; wi < kHeadDim * a.bits; wi += kThreads)
-    a.v_codes[dst * (kHeadDim * a.bits) + wi] = pack_nuq_word(ct, wi / a.bits, wi % a.bits, a.bits);
 }
 
 inline unsigned grid1(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
@@ -929,7 +905,7 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s) {
-  const int64_t jobs = (int64_t)a.bh_count * a.n_blocks;
+  const int64_t jobs = (int64_t)a.bh_count * ((a.n_blocks + kValueTiles - 1) / kValueTiles);
   if (jobs == 0) return hipSuccess;
   const dim3 grid((unsigned)jobs), block(kThreads);
   const bool vout = a.kv > 0;
