@@ -241,25 +241,33 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 }
 
 // ---- 1/3: magnitude histograms (LDS counts are u16 pairs packed in u32) ------------
-// A lane owns channels 2l, 2l+1 (one 4-byte load per token); the four waves take every
-// fourth token.  Each channel's row of counters is padded by one word so that the rows
-// of different channels start on different LDS banks: key magnitudes crowd into a few
-// bins, and unpadded rows put a wave's 128 atomics on the same few banks.  Sixteen
-// tokens' loads are issued before their atomics.
+// A lane owns two adjacent channels (one 4-byte load per token).  The high-bin pass keeps
+// 256 bins per channel, so a workgroup takes half of the channels (64): its LDS (33 KB)
+// then lets four workgroups share a CU, where 128 channels (66 KB) allowed two; half-wave
+// lane groups take different tokens.  The low-bin pass (128 bins) takes all 128.  Each
+// channel's row of counters is padded by one word so that the rows of different channels
+// start on different LDS banks: key magnitudes crowd into a few bins, and unpadded rows
+// put a wave's atomics on the same few banks.  Sixteen tokens' loads are issued before
+// their atomics.
 template <bool LOW>
 __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
   constexpr int NB = LOW ? 128 : 256;
+  constexpr int CH = LOW ? kHeadDim : kHeadDim / 2;       // channels per workgroup
+  constexpr int LPT = CH / 2;                             // lanes per token
   constexpr int RW = NB / 2 + 1;                          // words per channel row
-  __shared__ uint32_t h[kHeadDim][RW];
-  const int64_t bh = blockIdx.x / a.nchunks;
-  const int chunk = blockIdx.x % a.nchunks;
+  __shared__ uint32_t h[CH][RW];
+  constexpr int PARTS = kHeadDim / CH;
+  const int64_t job = blockIdx.x / PARTS;
+  const int c0 = (int)(blockIdx.x % PARTS) * CH;          // first channel of this group
+  const int64_t bh = job / a.nchunks;
+  const int chunk = (int)(job % a.nchunks);
   const int tid = threadIdx.x;
-  for (int i = tid; i < kHeadDim * RW; i += kThreads) (&h[0][0])[i] = 0;
+  for (int i = tid; i < CH * RW; i += kThreads) (&h[0][0])[i] = 0;
   int sel0 = -1, sel1 = -1;
-  const int cp = tid & 63;
+  const int cp = tid % LPT;                               // channels c0 + 2cp, c0 + 2cp + 1
   if (LOW) {
-    sel0 = a.thr[(bh * kHeadDim + 2 * cp) * 4 + 2];
-    sel1 = a.thr[(bh * kHeadDim + 2 * cp + 1) * 4 + 2];
+    sel0 = a.thr[(bh * kHeadDim + c0 + 2 * cp) * 4 + 2];
+    sel1 = a.thr[(bh * kHeadDim + c0 + 2 * cp + 1) * 4 + 2];
   }
   __syncthreads();
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
@@ -275,24 +283,25 @@ __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
     }
   };
   constexpr int U = 16;                                   // tokens in flight per lane
-  constexpr int STEP = kThreads / 64;                     // tokens per pass of the block
-  int64_t t = t0 + (tid >> 6);
+  constexpr int STEP = kThreads / LPT;                    // tokens per pass of the block
+  int64_t t = t0 + tid / LPT;
   for (; t + (int64_t)(U - 1) * STEP < t1; t += (int64_t)U * STEP) {
     uint32_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * STEP) + 2 * cp);
+      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * STEP) + c0 + 2 * cp);
 #pragma unroll
     for (int u = 0; u < U; ++u) count(w[u]);
   }
-  for (; t < t1; t += STEP) count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + 2 * cp));
+  for (; t < t1; t += STEP)
+    count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + c0 + 2 * cp));
   __syncthreads();
   uint32_t* g = LOW ? a.hist_lo : a.hist_hi;
-  for (int i = tid; i < kHeadDim * NB / 2; i += kThreads) {
+  for (int i = tid; i < CH * NB / 2; i += kThreads) {
     const int d = i / (NB / 2), b2 = i % (NB / 2);
     const uint32_t v = h[d][b2];
     if (v == 0) continue;
-    uint32_t* row = g + (bh * kHeadDim + d) * NB;
+    uint32_t* row = g + (bh * kHeadDim + c0 + d) * NB;
     if (v & 0xFFFFu) atomicAdd(&row[2 * b2], v & 0xFFFFu);
     if (v >> 16) atomicAdd(&row[2 * b2 + 1], v >> 16);
   }
@@ -345,42 +354,79 @@ __device__ __forceinline__ void load_key_tile(uint16_t (*tile)[kHeadDim], const 
 }
 
 // ---- 4: per chunk: ties, last positive / negative tie, dense min / max ----------------
+// Two threads per channel (tokens 0..15 and 16..31 of each 32-token tile); a chunk's ties
+// are numbered in token order, the second half's after the first half's of the same
+// tile.  Tiles are double-buffered in LDS and each is requested into registers while the
+// one before it is read.
 __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a) {
-  __shared__ __align__(16) uint16_t tile[kGroup][kHeadDim];
+  __shared__ __align__(16) uint16_t tiles[2][kGroup][kHeadDim];
   const int64_t bh = blockIdx.x / a.nchunks;
   const int chunk = blockIdx.x % a.nchunks;
-  const int d = threadIdx.x;
-  int T = 0x8000;
-  if (d < kHeadDim) T = a.thr[(bh * kHeadDim + d) * 4];
-  uint32_t ties = 0, above = 0;
+  const int tid = threadIdx.x;
+  const int ch = tid >> 1, half = tid & 1;
+  const int T = a.thr[(bh * kHeadDim + ch) * 4];
+  uint32_t run = 0, above = 0;              // ties so far in the chunk; values above T
   int32_t last_pos = -1, last_neg = -1;
   float dmin = __builtin_inff(), dmax = -__builtin_inff();
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
   const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
+  const int lt = tid >> 3, lc = (tid & 7) * 16;           // loader: token row, 16 channels
+  uint4 u0 = make_uint4(0u, 0u, 0u, 0u), u1 = u0;
+  if (t0 < t1) {
+    const uint4* p = reinterpret_cast<const uint4*>(key_row(a, bh, t0 + lt) + lc);
+    u0 = p[0];
+    u1 = p[1];
+  }
   for (int64_t tb = t0; tb < t1; tb += kGroup) {
-    load_key_tile(tile, a, bh, tb);
-    __syncthreads();
-    if (d < kHeadDim) {
-      for (int j = 0; j < kGroup; ++j) {
-        const uint16_t x = tile[j][d];
-        const int mag = x & 0x7FFF;
-        if (mag < T) {
-          const float v = f16_bits_to_f32(x);
-          dmin = fminf(dmin, v);
-          dmax = fmaxf(dmax, v);
-        } else if (mag == T) {
-          if (x & 0x8000u) last_neg = (int32_t)ties; else last_pos = (int32_t)ties;
-          ++ties;
-        } else {
-          ++above;
-        }
-      }
+    const int buf = (int)(((tb - t0) / kGroup) & 1);
+    uint4* d = reinterpret_cast<uint4*>(&tiles[buf][lt][lc]);
+    d[0] = u0;
+    d[1] = u1;
+    if (tb + kGroup < t1) {
+      const uint4* p = reinterpret_cast<const uint4*>(key_row(a, bh, tb + kGroup + lt) + lc);
+      u0 = p[0];
+      u1 = p[1];
     }
     __syncthreads();
+    uint32_t tiebits = 0u, posbits = 0u;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const uint32_t x = tiles[buf][16 * half + jj][ch];
+      const int mag = (int)(x & 0x7FFFu);
+      const float v = f16_bits_to_f32((uint16_t)x);
+      const bool dense = mag < T;
+      dmin = dense ? fminf(dmin, v) : dmin;
+      dmax = dense ? fmaxf(dmax, v) : dmax;
+      above += mag > T ? 1u : 0u;
+      const uint32_t eq = mag == T ? 1u : 0u;
+      tiebits |= eq << jj;
+      posbits |= (eq & ((x >> 15) ^ 1u)) << jj;
+    }
+    const uint32_t my = (uint32_t)__builtin_popcount(tiebits);
+    const uint32_t other = __shfl_xor(my, 1);
+    if (tiebits) {
+      // chunk-level number of this half's first tie, then of its last positive / negative
+      const uint32_t base = run + (half ? other : 0u);
+      const uint32_t negbits = tiebits & ~posbits;
+      if (posbits) {
+        const int j = 31 - __builtin_clz(posbits);
+        last_pos = (int32_t)(base + __builtin_popcount(tiebits & ((2u << j) - 1u)) - 1u);
+      }
+      if (negbits) {
+        const int j = 31 - __builtin_clz(negbits);
+        last_neg = (int32_t)(base + __builtin_popcount(tiebits & ((2u << j) - 1u)) - 1u);
+      }
+    }
+    run += my + other;
   }
-  if (d < kHeadDim) {
-    uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + d) * 8;
-    cs[0] = ties;
+  dmin = fminf(dmin, __shfl_xor(dmin, 1));
+  dmax = fmaxf(dmax, __shfl_xor(dmax, 1));
+  above += __shfl_xor(above, 1);
+  last_pos = max(last_pos, __shfl_xor(last_pos, 1));
+  last_neg = max(last_neg, __shfl_xor(last_neg, 1));
+  if (half == 0) {
+    uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + ch) * 8;
+    cs[0] = run;
     cs[1] = (uint32_t)last_pos;
     cs[2] = (uint32_t)last_neg;
     cs[3] = __builtin_bit_cast(uint32_t, dmin);
@@ -887,7 +933,7 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
   const unsigned jobs = (unsigned)((int64_t)a.bh_count * a.nchunks);
   fill_u32_kernel<<<dim3(1024), dim3(kThreads), 0, s>>>(a.hist_hi, bhd * 256, 0u);
   fill_u32_kernel<<<dim3(1024), dim3(kThreads), 0, s>>>(a.hist_lo, bhd * 128, 0u);
-  nuq_hist_kernel<false><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+  nuq_hist_kernel<false><<<dim3(2 * jobs), dim3(kThreads), 0, s>>>(a);   // two channel halves
   nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 0);
   nuq_hist_kernel<true><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
   nuq_select_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a, 1);
