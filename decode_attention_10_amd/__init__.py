@@ -11,7 +11,9 @@ import ctypes as C
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# KVQ_LIBRARY selects another build of the same C ABI, e.g. libkvq_debug.so (device-side
+# bounds checks, synchronous entry points)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python decode_attention_10_amd/build.py`")

@@ -3,6 +3,7 @@
     python decode_attention_10_amd/build.py        (or build_all() from Python)
 
 libkvq.so       <- decode_attention_10_amd/csrc/*.hip   (the C ABI of include/kvq.h)
+libkvq_debug.so <- the same sources with -DKVQ_DEBUG (device-side bounds checks)
 libkvq_synth.so <- kvq_synth/synth.hip                 (seeded input generator)
 
 Flags: contraction off (the quantizer's fp32 arithmetic must be one rounding per
@@ -36,14 +37,14 @@ def _run(cmd):
     return r
 
 
-def _build_lib(sources, out, includes, objdir):
+def _build_lib(sources, out, includes, objdir, extra=()):
     os.makedirs(objdir, exist_ok=True)
     objs = []
     cmds = []
     for src in sources:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *CFLAGS, *[f"-I{i}" for i in includes], "-c", src, "-o", obj])
+        cmds.append([HIPCC, *CFLAGS, *extra, *[f"-I{i}" for i in includes], "-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = out + ".tmp"
@@ -52,11 +53,16 @@ def _build_lib(sources, out, includes, objdir):
     return out
 
 
-def build_kvq() -> str:
+def build_kvq(debug: bool = False) -> str:
+    """libkvq.so, or with debug=True libkvq_debug.so: the same library compiled with
+    -DKVQ_DEBUG (device-side bounds checks that set flags instead of trapping; every entry
+    point then waits for its launches and reports a failed check as KVQ_ERR_HIP).  Select
+    it at run time with KVQ_LIBRARY=<path>."""
     csrc = os.path.join(PKG, "csrc")
     srcs = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith(".hip"))
-    return _build_lib(srcs, os.path.join(PKG, "libkvq.so"),
-                      [os.path.join(ROOT, "include"), csrc], os.path.join(ROOT, "_build", "kvq"))
+    name, sub = ("libkvq_debug.so", "kvq_debug") if debug else ("libkvq.so", "kvq")
+    return _build_lib(srcs, os.path.join(PKG, name), [os.path.join(ROOT, "include"), csrc],
+                      os.path.join(ROOT, "_build", sub), ["-DKVQ_DEBUG"] if debug else [])
 
 
 def build_synth() -> str:
@@ -66,7 +72,7 @@ def build_synth() -> str:
 
 
 def build_all() -> list[str]:
-    return [build_kvq(), build_synth()]
+    return [build_kvq(), build_kvq(debug=True), build_synth()]
 
 
 if __name__ == "__main__":

@@ -414,6 +414,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gqa_kernel(DecodeArgs a) {
   const int s0 = (int)((int64_t)units * split / a.splits);
   const int s1 = (int)((int64_t)units * (split + 1) / a.splits);
   const int bend = min(s1, a.n_blocks);
+  KVQ_CHECK(a.n_blocks <= a.cap_blocks && s1 <= units, kDbgSplit);
   const int first = s0 + wave;
   const int cnt = first < bend ? (bend - first + NW - 1) / NW : 0;
 
@@ -518,5 +519,7 @@ const void* decode_gqa_fn(int k_bits, int v_bits, int gq, int nw) {
 #undef KVQ_GF
   return nullptr;
 }
+
+uint32_t debug_take_decode_gqa() { return debug_take_local(); }
 
 }  // namespace kvq

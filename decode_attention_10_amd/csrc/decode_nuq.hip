@@ -440,6 +440,7 @@ __device__ __forceinline__ NuqBlockEntries load_block_entries(const NuqStreams& 
   NuqBlockEntries e;
   e.e_begin = e.n = 0;
   if (S.rp_step) {
+    KVQ_CHECK(r.r0 >= 0 && r.r0 <= r.r1 && r.r1 <= S.csr_cap, kDbgCsr);
     const int32_t b0 = max(__builtin_amdgcn_readlane(r.r0, 0), 0);
     const int32_t b1 = min(__builtin_amdgcn_readlane(r.r1, 63), S.csr_cap);
     e.e_begin = b0;
@@ -568,6 +569,8 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     const int rhi = (int)((uint32_t)r.r1 - (uint32_t)e_begin);
     auto window = [&](int off, uint32_t ent) {
       if (off + lane < n_ent) {
+        KVQ_CHECK(((ent >> 8) & 0xFFu) < (uint32_t)kGroup && (ent & 0xFFu) < (uint32_t)kHeadDim,
+                  kDbgEntry);
         const int te = (int)((ent >> 8) & (kGroup - 1));
         const int col = (int)(ent & (kHeadDim - 1));
         const int pr = col >> 1;
@@ -694,6 +697,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
       if (e < v_ne) {
         const uint32_t ent = e0 == 0 ? be.vent : S.vout[vbase + e];
         const int te = (e / S.v_kv) & (kGroup - 1);
+        KVQ_CHECK((ent & 0xFFFFu) < (uint32_t)kHeadDim, kDbgEntry);
         const int d = (int)(ent & (kHeadDim - 1));
         const float x = f16_bits_to_f32((uint16_t)(ent >> 16));
         const uint32_t vmw = ws.vmeta[te];
@@ -841,6 +845,7 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel
     if (u >= w0 && u < w1) process_nuq_window<GQ>(a, bh, c, pc, st, wsc[wave].ps, lane);
   }
   const int b0 = w0, b1 = min(w1, a.n_blocks);
+  KVQ_CHECK(a.n_blocks <= a.cap_blocks && s1 <= units, kDbgSplit);
   if (b0 < b1) {
     // One block in flight ahead of the one being processed (clamped index, unrolled by
     // two so no register copy waits on the loads just issued).
@@ -950,5 +955,7 @@ const void* decode_nuq_fn(int gq, int nw, int bits) {
 #undef KVQ_DF
   return nullptr;
 }
+
+uint32_t debug_take_decode_nuq() { return debug_take_local(); }
 
 }  // namespace kvq

@@ -208,6 +208,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   const int nb = max(bend - s0, 0);
   const int c_first = max(s0 - a.n_blocks + kWindowUnits - 1, 0) / kWindowUnits;
   const int c_end = min(nchunks, max(s1 - a.n_blocks + kWindowUnits - 1, 0) / kWindowUnits);
+  KVQ_CHECK(a.n_blocks <= a.cap_blocks && s1 <= units && c_end <= nchunks, kDbgSplit);
   const Deal deal = deal_blocks(nb, max(c_end - c_first, 0), NW);
   const int cnt = __builtin_amdgcn_readfirstlane(deal.count(wave));
 
@@ -265,6 +266,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(const float
   __shared__ float po[kMergeParts][kHeadDim];
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x & (kHeadDim - 1), part = threadIdx.x >> 7;
+  KVQ_CHECK(splits >= 1 && splits <= kMaxSplits, kDbgSplit);
   const float* P = partials + row * splits * kPartialStride;
   float M = kNegInf, L = 0.f, O = 0.f;
   for (int s0 = part; s0 < splits; s0 += kMergeParts * kMergeChunk) {
@@ -371,5 +373,7 @@ hipError_t launch_merge_splits(const DecodeArgs& a, hipStream_t s) {
                                                                            a.splits);
   return hipGetLastError();
 }
+
+uint32_t debug_take_decode_uniform() { return debug_take_local(); }
 
 }  // namespace kvq

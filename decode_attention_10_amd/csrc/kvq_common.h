@@ -25,6 +25,43 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// ---- debug builds (compiled with -DKVQ_DEBUG) -------------------------------------------
+// Device-side bounds checks.  A failed check does not trap: it sets a bit in its
+// translation unit's flag word (a global atomic), the kernel goes on (every checked access
+// is also guarded or clamped), and the host entry point, which in these builds waits for
+// its stream after launching, reads and clears the words of all translation units and
+// returns KVQ_ERR_HIP naming the bits.  Release builds compile the checks away.
+enum DebugBit : uint32_t {
+  kDbgBlock = 1u << 0,    // a packed block or window chunk beyond the cache
+  kDbgCsr = 1u << 1,      // a CSR row range or entry index beyond csr_capacity
+  kDbgEntry = 1u << 2,    // a CSR or value-outlier entry with a field out of range
+  kDbgWrite = 1u << 3,    // a quantizer write beyond the buffers' capacity
+  kDbgSplit = 1u << 4,    // a split's unit range or a merge index beyond the plan
+};
+#ifdef KVQ_DEBUG
+static __device__ uint32_t kvq_debug_word;
+#define KVQ_CHECK(cond, bit)                                                    \
+  do {                                                                          \
+    if (!(cond)) atomicOr(&::kvq::kvq_debug_word, (uint32_t)(bit));             \
+  } while (0)
+// This translation unit's flag word, read and cleared (host; the caller synchronized).
+static inline uint32_t debug_take_local() {
+  uint32_t v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kvq_debug_word), sizeof v) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(kvq_debug_word), &z, sizeof z) != hipSuccess) return ~0u;
+  return v;
+}
+#else
+#define KVQ_CHECK(cond, bit) ((void)0)
+static inline uint32_t debug_take_local() { return 0u; }
+#endif
+// Each kernel translation unit defines one: its flag word (0 in release builds).
+uint32_t debug_take_decode_uniform();
+uint32_t debug_take_decode_gqa();
+uint32_t debug_take_decode_nuq();
+uint32_t debug_take_quant_uniform();
+uint32_t debug_take_quant_nuq();
+
 // Streaming loads: global loads with the nontemporal hint, for data read once per decode
 // (packed codes, metadata, fp16 windows).  Measured on a 117 MB read by one workgroup
 // per CU: 6.5 TB/s with the hint against 5.8 TB/s without.  Pointers must be aligned to
@@ -136,12 +173,14 @@ __device__ __forceinline__ Fp16Chunk fp16_chunk(const DecodeArgs& a, int64_t bh,
     r.v = a.v_sink + (bh * a.sink_len + tok0) * kHeadDim;
     r.nvalid = min(kGroup, a.n_sink - tok0);
     r.pos0 = tok0;
+    KVQ_CHECK(r.nvalid >= 1 && a.n_sink <= a.sink_len, kDbgBlock);
   } else {
     const int tok0 = (c - sink_chunks) * kGroup;
     r.k = a.k_resid + (bh * a.residual_len + tok0) * kHeadDim;
     r.v = a.v_resid + (bh * a.residual_len + tok0) * kHeadDim;
     r.nvalid = min(kGroup, a.n_resid - tok0);
     r.pos0 = a.n_sink + (int64_t)a.n_blocks * kGroup + tok0;
+    KVQ_CHECK(r.nvalid >= 1 && a.n_resid <= a.residual_len, kDbgBlock);
   }
   return r;
 }

@@ -613,6 +613,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
           }
         }
       }
+      KVQ_CHECK(tb / kGroup < a.cap_blocks, kDbgWrite);
       uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
       store_code_words<B>(kw, cb, half);
     }
@@ -647,6 +648,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_keys_kernel(NuqKeysArgs a)
         while (bits) {
           const int d = 32 * w + __builtin_ctz(bits);
           bits &= bits - 1;
+          KVQ_CHECK(pos < a.csr_capacity, kDbgCsr);
           if (pos < a.csr_capacity)
             ent[pos] = (uint32_t)d | ((uint32_t)j << 8) | ((uint32_t)tile[j][d] << 16);
           ++pos;
@@ -905,6 +907,7 @@ __global__ __launch_bounds__(kThreads) void nuq_quant_values_kernel(NuqValuesArg
         cb[jj >> 2] |= c << (8 * (jj & 3));
         if (a.qnorm && !out) atomicAdd(&qh[tt][c], 1u);
       }
+      KVQ_CHECK(a.tok0 / kGroup + blk < a.cap_blocks, kDbgWrite);
       uint32_t* kw = a.v_codes + (bh * a.cap_blocks + a.tok0 / kGroup + blk) * (kHeadDim * B) +
                      ch * B;
       store_code_words<B>(kw, cb, half);
@@ -963,5 +966,7 @@ hipError_t launch_nuq_values(const NuqValuesArgs& a, hipStream_t s) {
   else nuq_quant_values_kernel<4, false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
+
+uint32_t debug_take_quant_nuq() { return debug_take_local(); }
 
 }  // namespace kvq

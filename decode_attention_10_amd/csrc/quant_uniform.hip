@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kThreads) void quant_uniform_kernel(QuantArgs a) {
   const int h = (int)(bh % a.kv_heads);
   const int64_t dst = bh * a.cap_blocks + a.blk0 + blk;   // [B][H][cap_blocks]
   const int tid = threadIdx.x;
+  KVQ_CHECK(a.blk0 + blk < a.cap_blocks, kDbgWrite);
 
   if constexpr (KB != 0) {
    if (a.k != nullptr) {
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int64_t row = j / (kHeadDim / 8);
   const int c = (int)(j % (kHeadDim / 8));
   const uint16_t* src = (is_v ? a.v_new : a.k_new) + row * kHeadDim + c * 8;
+  KVQ_CHECK(a.slot >= 0 && a.slot < a.residual_len, kDbgWrite);
   uint16_t* dst = (is_v ? a.v_resid : a.k_resid) +
                   (row * a.residual_len + a.slot) * kHeadDim + c * 8;
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
@@ -242,5 +244,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
+
+uint32_t debug_take_quant_uniform() { return debug_take_local(); }
 
 }  // namespace kvq

@@ -120,6 +120,12 @@
  *    they can be captured into a HIP graph.  A captured call keeps the pointers
  *    and the counters (n_packed, n_resid, n_sink) it saw at capture: each replay
  *    repeats that step on the buffers' current contents.
+ *  - Debug build (libkvq_debug.so, compiled with -DKVQ_DEBUG; same ABI): the
+ *    kernels also check every block index, CSR row range, outlier entry, append
+ *    slot and split range they derive, setting a flag instead of trapping, and
+ *    every call then waits for the device and returns KVQ_ERR_HIP, naming the
+ *    flags, if a check failed.  Those calls synchronize, so they cannot be
+ *    captured into a graph.
  */
 #ifndef KVQ_H
 #define KVQ_H

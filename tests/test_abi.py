@@ -277,3 +277,13 @@ def test_capacity_and_csr_limits():
         K.kvq_quantize_keys(c, FAKE, 0, 0, 128, 0, 1 << 28, FAKE, 1 << 40, stream=0)
     assert e.value.status == K.KVQ_ERR_CAPACITY
     assert "int32" in K.kvq_last_error()
+
+
+def test_debug_build_exports_the_same_functions():
+    """libkvq_debug.so (built with -DKVQ_DEBUG: device-side bounds checks) keeps the ABI."""
+    path = os.path.join(os.path.dirname(K.LIB_PATH), "libkvq_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("libkvq_debug.so is not built")
+    lib = C.CDLL(path)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
