@@ -9,10 +9,11 @@
 // so one lane owns a channel pair i.  Each block starts from a_i(t0) = q e^(-i t0 th_i),
 // where e^(-i t0 th_i) is carried from block to block in fp64 (one complex product by
 // e^(-i 32 th_i) per block, started from an angle reduced modulo 2 pi at the wave's
-// first block).  Inside the block two chains (tokens 0 and 16 on) advance by the
-// three-term recurrence x(t+1) = 2 cos(th_i) x(t) - x(t-1), which every real-linear
-// function of a_i(t) obeys; with one query head the chains carry s_2i Re(a), s_2i+1 Im(a)
-// and m_2i Re(a) + m_2i+1 Im(a) (key scales and minima folded in), so a token costs three
+// first block).  Inside the block chains advance by the three-term recurrence
+// x(t+1) = 2 cos(th_i) x(t) - x(t-1), which every real-linear function of a_i(t) obeys
+// (one chain over the 32 tokens for nuq3 with one query head, two chains from tokens 0
+// and 16 otherwise); with one query head the chains carry s_2i Re(a), s_2i+1 Im(a) and
+// m_2i Re(a) + m_2i+1 Im(a) (key scales and minima folded in), so a token costs three
 // fmas of recurrence and two of score.  Per-pair partial scores of the block's 32 tokens
 // are then summed across lanes (lanes 2t and 2t+1 end with token t).
 // Outliers: the dense pass uses the stored code everywhere; one lane per CSR entry
@@ -291,8 +292,8 @@ struct PairConsts {
 // Any real-linear function x(t) of q e^(-i t theta) (its real part, its imaginary part,
 // a combination of both) satisfies x(t+1) = 2 cos(theta) x(t) - x(t-1): one fma per
 // token instead of a complex product.  An error made at token s reaches token t scaled
-// by sin((t-s) theta) / sin(theta), at most t - s, so over the 16 tokens of a chain the
-// recurrence keeps a relative error of ~1e-5 even where theta is tiny.
+// by sin((t-s) theta) / sin(theta), at most t - s, so over the (at most) 32 tokens of a
+// chain the recurrence keeps a relative error of ~2e-5 even where theta is tiny.
 __device__ __forceinline__ float cheb_next(float tc, float cur, float prev) {
   return fmaf(tc, cur, -prev);
 }
@@ -375,16 +376,16 @@ template <int B>
 struct NuqBlockRegs {
   uint32_t kw[2 * B], vw[2 * B];   // key / value code words of channels 2l, 2l+1
   uint32_t vmeta;            // value scale / min of token lane >> 1
-  int32_t r0, r1;            // CSR row of token lane >> 1
 };
 
-// The block's outlier entries: key CSR entries [e_begin, e_begin + n) and the first 64 of
-// them (one per lane), the first 64 value-outlier entries.  They are loaded once the
-// block's row pointers are in and before the next block's loads are issued, so that
-// waiting for them never waits for the prefetch.
+// The block's outlier entries: key CSR entries [e_begin, e_begin + n), the first 64 of
+// them (one per lane), the first 64 value-outlier entries, and this lane's token row.
+// The block loop requests them one block ahead of their use, from row pointers loaded
+// two blocks ahead, so that neither dependent load makes a wave wait.
 struct NuqBlockEntries {
   int32_t e_begin, n;        // n entries from e_begin (at most one per code of the block)
   uint32_t ent, vent;
+  uint32_t rows;             // row of token lane >> 1 relative to e_begin: lo | hi << 16
 };
 
 // A wave's (batch, kv head) streams, uniform: resolved once so that the block loop
@@ -421,30 +422,36 @@ __device__ __forceinline__ void load_words(uint32_t* dst, const uint32_t* p) {
 template <int B>
 __device__ __forceinline__ void load_nuq_block(NuqBlockRegs<B>& r, const NuqStreams& S,
                                                int64_t blk, int lane) {
-  const int t = lane >> 1;
-  const int64_t t0 = blk * kGroup;
   load_words<B>(r.kw, S.kc + blk * (kHeadDim * B) + 2 * lane * B);
   load_words<B>(r.vw, S.vc + blk * (kHeadDim * B) + 2 * lane * B);
-  r.vmeta = S.vm[t0 + t];
-  // Unconditional (without key outliers both read a value-metadata word, ignored by
-  // load_block_entries), so that no register copy of a conditionally loaded value makes
-  // the wave wait for the loads just issued.
-  r.r0 = S.rp[t0 + t];
-  r.r1 = S.rp[t0 + t + S.rp_step];
+  r.vmeta = S.vm[blk * kGroup + (lane >> 1)];
 }
 
-template <int B>
+// Row pointers of the block: the even lane of token t loads the start of its row, the odd
+// lane the end.  Unconditional (without key outliers it reads a value-metadata word,
+// ignored by load_block_entries), so that no register copy of a conditionally loaded
+// value makes the wave wait for the loads just issued.
+__device__ __forceinline__ int32_t load_rows(const NuqStreams& S, int64_t blk, int lane) {
+  return S.rp[blk * kGroup + (lane >> 1) + (lane & 1) * S.rp_step];
+}
+
 __device__ __forceinline__ NuqBlockEntries load_block_entries(const NuqStreams& S, int64_t blk,
-                                                              const NuqBlockRegs<B>& r,
-                                                              int lane) {
+                                                              int32_t rp, int lane) {
   NuqBlockEntries e;
   e.e_begin = e.n = 0;
+  e.rows = 0;
   if (S.rp_step) {
-    KVQ_CHECK(r.r0 >= 0 && r.r0 <= r.r1 && r.r1 <= S.csr_cap, kDbgCsr);
-    const int32_t b0 = max(__builtin_amdgcn_readlane(r.r0, 0), 0);
-    const int32_t b1 = min(__builtin_amdgcn_readlane(r.r1, 63), S.csr_cap);
+    const int32_t other = __builtin_amdgcn_update_dpp(0, rp, 0xB1, 0xF, 0xF, false);
+    const int32_t r0 = (lane & 1) ? other : rp, r1 = (lane & 1) ? rp : other;
+    KVQ_CHECK(r0 >= 0 && r0 <= r1 && r1 <= S.csr_cap, kDbgCsr);
+    const int32_t b0 = max(__builtin_amdgcn_readlane(rp, 0), 0);
+    const int32_t b1 = min(__builtin_amdgcn_readlane(rp, 63), S.csr_cap);
     e.e_begin = b0;
     e.n = min(max(b1 - b0, 0), kGroup * kHeadDim);
+    // relative to b0 in unsigned arithmetic (wraps, never traps), clamped to [0, n]
+    const int lo = min(max((int)((uint32_t)r0 - (uint32_t)b0), 0), e.n);
+    const int hi = min(max((int)((uint32_t)r1 - (uint32_t)b0), 0), e.n);
+    e.rows = (uint32_t)lo | ((uint32_t)hi << 16);
   }
   e.ent = 0;
   if (lane < e.n) e.ent = (S.ent + e.e_begin)[lane];
@@ -480,48 +487,66 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     // chain step are used at once
     float part[32];
     qb[0] = base;                                    // q e^(-i t0 theta), see the caller
-    const float2 c16 = cmul(qb[0], pc.r16);
-    Uvw ca[2] = {uvw_of(qb[0], pc), uvw_of(c16, pc)};                    // token k
-    Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
+    if constexpr (B == 3) {
+      // one chain over the 32 tokens; the pair-table entries of tokens 4 m4 .. 4 m4 + 3
+      // are requested one group ahead of their use
+      Uvw c0 = uvw_of(qb[0], pc), c1 = uvw_of(cmul(qb[0], pc.step), pc);   // tokens k, k + 1
+      uint32_t eb[2][4];
+      auto fetch = [&](uint32_t (&e)[4], int m4) {
+        const uint32_t x = key_pair_index4(kw0, kw1, m4);
+        e[0] = pair_entry<0>(sh.tk, x);
+        e[1] = pair_entry<1>(sh.tk, x);
+        e[2] = pair_entry<2>(sh.tk, x);
+        e[3] = pair_entry<3>(sh.tk, x);
+      };
+      fetch(eb[0], 0);
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {                 // tokens 4 m4 .. 4 m4 + 3 of each chain
-      uint32_t a[2][2], b[2][2], ix[2];
+      for (int m4 = 0; m4 < 8; ++m4) {
+        if (m4 < 7) fetch(eb[(m4 + 1) & 1], m4 + 1);
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        if constexpr (B == 3) {
-          ix[ch] = key_pair_index4(kw0, kw1, m4 + 4 * ch);
-        } else {
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k = 4 * m4 + kk;
+          const uint32_t e = eb[m4 & 1][kk];
+          part[k] = fmaf(c0.u, lo_f16(e), fmaf(c0.v, hi_f16(e), c0.w));
+          if (k < 31) {
+            Uvw n = c1;
+            if (k < 30) n = cheb_next(pc.tc, c1, c0);
+            c0 = c1;
+            c1 = n;
+          }
+        }
+      }
+    } else {
+      // two chains (tokens 0..15 and 16..31), four codes per table lookup
+      const float2 c16 = cmul(qb[0], pc.r16);
+      Uvw ca[2] = {uvw_of(qb[0], pc), uvw_of(c16, pc)};                    // token k
+      Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {               // tokens 4 m4 .. 4 m4 + 3 of each chain
+        uint32_t a[2][2], b[2][2];
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
           lut4<B>(lk, codes_of<B>(kw0, m4 + 4 * ch), a[ch][0], a[ch][1]);
           lut4<B>(lk, codes_of<B>(kw1, m4 + 4 * ch), b[ch][0], b[ch][1]);
         }
-      }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = 4 * m4 + kk;
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          float l0, l1;
-          if constexpr (B == 3) {
-            const uint32_t e = kk == 0   ? pair_entry<0>(sh.tk, ix[ch])
-                               : kk == 1 ? pair_entry<1>(sh.tk, ix[ch])
-                               : kk == 2 ? pair_entry<2>(sh.tk, ix[ch])
-                                         : pair_entry<3>(sh.tk, ix[ch]);
-            l0 = lo_f16(e);
-            l1 = hi_f16(e);
-          } else {
-            const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
-            l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
-            l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
-          }
-          part[16 * ch + k] = fmaf(ca[ch].u, l0, fmaf(ca[ch].v, l1, ca[ch].w));
-        }
-        if (k < 15) {
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k = 4 * m4 + kk;
 #pragma unroll
           for (int ch = 0; ch < 2; ++ch) {
-            Uvw n = cb[ch];
-            if (k < 14) n = cheb_next(pc.tc, cb[ch], ca[ch]);
-            ca[ch] = cb[ch];
-            cb[ch] = n;
+            const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
+            const float l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
+            const float l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
+            part[16 * ch + k] = fmaf(ca[ch].u, l0, fmaf(ca[ch].v, l1, ca[ch].w));
+          }
+          if (k < 15) {
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+              Uvw n = cb[ch];
+              if (k < 14) n = cheb_next(pc.tc, cb[ch], ca[ch]);
+              ca[ch] = cb[ch];
+              cb[ch] = n;
+            }
           }
         }
       }
@@ -563,10 +588,10 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
 #pragma unroll
     for (int j = 0; j < GQ; ++j) ws.qb[j][lane] = qb[j];
     __builtin_amdgcn_wave_barrier();
-    // this lane's token row relative to e_begin (unsigned: wraps, never traps; the
-    // clamps below keep every LDS index inside the window)
-    const int rlo = (int)((uint32_t)r.r0 - (uint32_t)e_begin);
-    const int rhi = (int)((uint32_t)r.r1 - (uint32_t)e_begin);
+    // this lane's token row relative to e_begin (within [0, n_ent]; the clamps below
+    // keep every LDS index inside the window)
+    const int rlo = (int)(be.rows & 0xFFFFu);
+    const int rhi = (int)(be.rows >> 16);
     auto window = [&](int off, uint32_t ent) {
       if (off + lane < n_ent) {
         KVQ_CHECK(((ent >> 8) & 0xFFu) < (uint32_t)kGroup && (ent & 0xFFu) < (uint32_t)kHeadDim,
@@ -863,19 +888,28 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel
     S.vout = a.v_out ? a.v_out + bt * a.v_kv : nullptr;
     S.v_kv = a.v_kv;
     S.scale_log2 = a.scale_log2;
+    // Code words one block ahead of their use; row pointers two blocks ahead, so that the
+    // entries they locate can be requested one block ahead.
     NuqBlockRegs<B> r0, r1;
+    int32_t rp0 = load_rows(S, b0, lane);
+    int32_t rp1 = load_rows(S, min(b0 + 1, last), lane);
     load_nuq_block<B>(r0, S, b0, lane);
+    NuqBlockEntries e0 = load_block_entries(S, b0, rp0, lane), e1;
     // e^(-i t0 theta) of the current block, in fp64 from block to block; with one query
     // head the query is folded in (the block then starts from q e^(-i t0 theta) itself)
     double2 base = rot_at64(a.n_sink + (int64_t)b0 * kGroup, pc.theta);
     if constexpr (GQ == 1) base = cmul64(base, make_double2(pc.q[0].x, pc.q[0].y));
     for (int i = b0; i < b1; i += 2) {
-      const NuqBlockEntries e0 = load_block_entries<B>(S, i, r0, lane);
+      // block i: entries e0 and codes r0 requested one block ago; now the entries of block
+      // i + 1 (its rows arrived), the rows of block i + 2, the codes of block i + 1
+      e1 = load_block_entries(S, min(i + 1, last), rp1, lane);
+      rp0 = load_rows(S, min(i + 2, last), lane);
       load_nuq_block<B>(r1, S, min(i + 1, last), lane);
       process_nuq_block<GQ, B>(S, i, r0, e0, pc, to_f32(base), lk, lv, st, sh, wsc[wave], lane);
       base = cmul64(base, pc.step32);
       if (i + 1 >= b1) break;
-      const NuqBlockEntries e1 = load_block_entries<B>(S, i + 1, r1, lane);
+      e0 = load_block_entries(S, min(i + 2, last), rp0, lane);
+      rp1 = load_rows(S, min(i + 3, last), lane);
       load_nuq_block<B>(r0, S, min(i + 2, last), lane);
       process_nuq_block<GQ, B>(S, i + 1, r1, e1, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
                                lane);
