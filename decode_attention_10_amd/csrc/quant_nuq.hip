@@ -628,111 +628,111 @@ __global__ __launch_bounds__(kThreads, 4) void nuq_quant_keys_kernel(NuqKeysArgs
   // CSR: this chunk's first entry (the scan of the per-chunk counts), kept by every wave
   int64_t run = a.rowptr != nullptr ? (int64_t)a.chunk_off[bh * a.nchunks + chunk] : 0;
   auto tile_loop = [&](auto cells_tag) {
-  constexpr bool CELLS = decltype(cells_tag)::value;
-  KeyPieces kp = t0 < t1 ? fetch_key_tile(a, bh, t0) : KeyPieces{};
-  for (int64_t tb = t0; tb < t1; tb += kGroup) {
-    const int buf = (int)(((tb - t0) / kGroup) & 1);
-    uint16_t (*tile)[kHeadDim] = tiles[buf];
-    uint32_t (*om)[4] = oms[buf];
-    store_key_tile(tile, kp);
-    if (tb + kGroup < t1) kp = fetch_key_tile(a, bh, tb + kGroup);
-    if (tid < kGroup * 4) om[tid >> 2][tid & 3] = 0;
-    __syncthreads();
-    {
-      // Two lanes of one wave per channel, tokens 0..15 and 16..31.  The outlier rank of
-      // ties at the threshold runs in token order: the second half's continues from the
-      // first half's count.  Codes are gathered one per byte (token 4mm + k of the half
-      // in byte k of cb[mm]) and turned into the channel's B code words at the end.
-      const int ch = tid >> 1, half = tid & 1;
-      uint32_t xs[16];
-      float xn2[16];
-      uint32_t outbits = 0u, my_ties = 0u;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const uint32_t x = tile[16 * half + jj][ch];
-        xs[jj] = x;
-        const int mag = (int)(x & 0x7FFFu);
-        const bool out = mag > cT;                 // ties at cT: below
-        my_ties += mag == cT ? 1u : 0u;
-        outbits |= (uint32_t)out << jj;
-        // an outlier's position stores code 0 (its exact value replaces the dequantized
-        // one), and so does every position of a channel without a dense range
-        xn2[jj] = out || cinv2 == 0.0f ? -__builtin_inff()
-                                       : (f16_bits_to_f32((uint16_t)x) - cmn) * cinv2;
-      }
-      const uint32_t other_ties = __shfl_xor(my_ties, 1);
-      uint32_t cb[4] = {0u, 0u, 0u, 0u};
-      nuq_code16<B, B == 4 ? 4 : 8, CELLS>(cb, [&](int jj) { return xn2[jj]; }, cells, md);
-      if (__any(my_ties != 0u)) {
-        // ties at the threshold, in token order: the first cneed of the channel's ties
-        // (counted from crank, the ties of the earlier chunks) are outliers
-        uint32_t r = crank + (half ? other_ties : 0u);
-        uint32_t tbits = 0u;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) tbits |= (uint32_t)((int)(xs[jj] & 0x7FFFu) == cT) << jj;
-        while (tbits) {
-          const int jj = __builtin_ctz(tbits);
-          tbits &= tbits - 1u;
-          if (r < (uint32_t)cneed) {
-            outbits |= 1u << jj;
-            cb[jj >> 2] &= ~(0xFFu << (8 * (jj & 3)));
-          }
-          ++r;
-        }
-      }
-      crank += my_ties + other_ties;
-      for (uint32_t ob = outbits; ob != 0u; ob &= ob - 1u) {
-        const int jj = __builtin_ctz(ob);
-        atomicOr(&om[16 * half + jj][ch >> 5], 1u << (ch & 31));
-      }
-      if (a.qnorm) {
+    constexpr bool CELLS = decltype(cells_tag)::value;
+    KeyPieces kp = t0 < t1 ? fetch_key_tile(a, bh, t0) : KeyPieces{};
+    for (int64_t tb = t0; tb < t1; tb += kGroup) {
+      const int buf = (int)(((tb - t0) / kGroup) & 1);
+      uint16_t (*tile)[kHeadDim] = tiles[buf];
+      uint32_t (*om)[4] = oms[buf];
+      store_key_tile(tile, kp);
+      if (tb + kGroup < t1) kp = fetch_key_tile(a, bh, tb + kGroup);
+      if (tid < kGroup * 4) om[tid >> 2][tid & 3] = 0;
+      __syncthreads();
+      {
+        // Two lanes of one wave per channel, tokens 0..15 and 16..31.  The outlier rank of
+        // ties at the threshold runs in token order: the second half's continues from the
+        // first half's count.  Codes are gathered one per byte (token 4mm + k of the half
+        // in byte k of cb[mm]) and turned into the channel's B code words at the end.
+        const int ch = tid >> 1, half = tid & 1;
+        uint32_t xs[16];
+        float xn2[16];
+        uint32_t outbits = 0u, my_ties = 0u;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          if (!((outbits >> jj) & 1u)) {
-            exact_add(qs, xs[jj]);
-            atomicAdd(&qh[ch][(cb[jj >> 2] >> (8 * (jj & 3))) & 0xFFu], 1u);
+          const uint32_t x = tile[16 * half + jj][ch];
+          xs[jj] = x;
+          const int mag = (int)(x & 0x7FFFu);
+          const bool out = mag > cT;                 // ties at cT: below
+          my_ties += mag == cT ? 1u : 0u;
+          outbits |= (uint32_t)out << jj;
+          // an outlier's position stores code 0 (its exact value replaces the dequantized
+          // one), and so does every position of a channel without a dense range
+          xn2[jj] = out || cinv2 == 0.0f ? -__builtin_inff()
+                                         : (f16_bits_to_f32((uint16_t)x) - cmn) * cinv2;
+        }
+        const uint32_t other_ties = __shfl_xor(my_ties, 1);
+        uint32_t cb[4] = {0u, 0u, 0u, 0u};
+        nuq_code16<B, B == 4 ? 4 : 8, CELLS>(cb, [&](int jj) { return xn2[jj]; }, cells, md);
+        if (__any(my_ties != 0u)) {
+          // ties at the threshold, in token order: the first cneed of the channel's ties
+          // (counted from crank, the ties of the earlier chunks) are outliers
+          uint32_t r = crank + (half ? other_ties : 0u);
+          uint32_t tbits = 0u;
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) tbits |= (uint32_t)((int)(xs[jj] & 0x7FFFu) == cT) << jj;
+          while (tbits) {
+            const int jj = __builtin_ctz(tbits);
+            tbits &= tbits - 1u;
+            if (r < (uint32_t)cneed) {
+              outbits |= 1u << jj;
+              cb[jj >> 2] &= ~(0xFFu << (8 * (jj & 3)));
+            }
+            ++r;
           }
         }
-      }
-      KVQ_CHECK(tb / kGroup < a.cap_blocks, kDbgWrite);
-      uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
-      store_code_words<B>(kw, cb, half);
-    }
-    __syncthreads();
-    if (a.rowptr != nullptr) {
-      // each token's first entry: every wave scans the 32 row lengths itself (lane j: token
-      // j), so no barrier separates the scan from the writes; then thread (token j,
-      // sixteenth e) writes the entries of channels 16e..16e+15 (ascending, the exact fp16
-      // value from the tile) and e = 0 the row pointer.  No barrier after: the next tile
-      // goes to the other buffers.
-      const int l = tid & (kWave - 1);
-      const uint32_t cnt = l < kGroup ? (uint32_t)(__popc(om[l][0]) + __popc(om[l][1]) +
-                                                   __popc(om[l][2]) + __popc(om[l][3]))
-                                      : 0u;
-      uint32_t incl = cnt;
+        crank += my_ties + other_ties;
+        for (uint32_t ob = outbits; ob != 0u; ob &= ob - 1u) {
+          const int jj = __builtin_ctz(ob);
+          atomicOr(&om[16 * half + jj][ch >> 5], 1u << (ch & 31));
+        }
+        if (a.qnorm) {
 #pragma unroll
-      for (int o = 1; o < kGroup; o <<= 1) {
-        const uint32_t x = __shfl_up(incl, o);
-        if (l >= o) incl += x;
+          for (int jj = 0; jj < 16; ++jj) {
+            if (!((outbits >> jj) & 1u)) {
+              exact_add(qs, xs[jj]);
+              atomicAdd(&qh[ch][(cb[jj >> 2] >> (8 * (jj & 3))) & 0xFFu], 1u);
+            }
+          }
+        }
+        KVQ_CHECK(tb / kGroup < a.cap_blocks, kDbgWrite);
+        uint32_t* kw = a.k_codes + (bh * a.cap_blocks + tb / kGroup) * (kHeadDim * B) + ch * B;
+        store_code_words<B>(kw, cb, half);
       }
-      const int j = tid >> 3, e = tid & 7, w = e >> 1;
-      const uint32_t word = om[j][w];
-      const uint32_t bits0 = (e & 1) ? word >> 16 : word & 0xFFFFu;
-      int64_t pos = run + (int64_t)__shfl(incl - cnt, j);
-      for (int i = 0; i < w; ++i) pos += __popc(om[j][i]);
-      if (e & 1) pos += __popc(word & 0xFFFFu);
-      if (e == 0) a.rowptr[bh * (a.cap_tokens + 1) + tb + j] = (int32_t)pos;
-      uint32_t* ent = a.ent + bh * a.csr_capacity;
-      for (uint32_t bits = bits0; bits != 0u; bits &= bits - 1u) {
-        const int d = 16 * e + __builtin_ctz(bits);
-        KVQ_CHECK(pos < a.csr_capacity, kDbgCsr);
-        if (pos < a.csr_capacity)
-          ent[pos] = (uint32_t)d | ((uint32_t)j << 8) | ((uint32_t)tile[j][d] << 16);
-        ++pos;
+      __syncthreads();
+      if (a.rowptr != nullptr) {
+        // each token's first entry: every wave scans the 32 row lengths itself (lane j: token
+        // j), so no barrier separates the scan from the writes; then thread (token j,
+        // sixteenth e) writes the entries of channels 16e..16e+15 (ascending, the exact fp16
+        // value from the tile) and e = 0 the row pointer.  No barrier after: the next tile
+        // goes to the other buffers.
+        const int l = tid & (kWave - 1);
+        const uint32_t cnt = l < kGroup ? (uint32_t)(__popc(om[l][0]) + __popc(om[l][1]) +
+                                                     __popc(om[l][2]) + __popc(om[l][3]))
+                                        : 0u;
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kGroup; o <<= 1) {
+          const uint32_t x = __shfl_up(incl, o);
+          if (l >= o) incl += x;
+        }
+        const int j = tid >> 3, e = tid & 7, w = e >> 1;
+        const uint32_t word = om[j][w];
+        const uint32_t bits0 = (e & 1) ? word >> 16 : word & 0xFFFFu;
+        int64_t pos = run + (int64_t)__shfl(incl - cnt, j);
+        for (int i = 0; i < w; ++i) pos += __popc(om[j][i]);
+        if (e & 1) pos += __popc(word & 0xFFFFu);
+        if (e == 0) a.rowptr[bh * (a.cap_tokens + 1) + tb + j] = (int32_t)pos;
+        uint32_t* ent = a.ent + bh * a.csr_capacity;
+        for (uint32_t bits = bits0; bits != 0u; bits &= bits - 1u) {
+          const int d = 16 * e + __builtin_ctz(bits);
+          KVQ_CHECK(pos < a.csr_capacity, kDbgCsr);
+          if (pos < a.csr_capacity)
+            ent[pos] = (uint32_t)d | ((uint32_t)j << 8) | ((uint32_t)tile[j][d] << 16);
+          ++pos;
+        }
+        run += __shfl(incl, kGroup - 1);
       }
-      run += __shfl(incl, kGroup - 1);
     }
-  }
   };
   if (by_cells) tile_loop(CellsTag<true>{});
   else tile_loop(CellsTag<false>{});
@@ -904,109 +904,109 @@ __global__ __launch_bounds__(kThreads, 4) void nuq_quant_values_kernel(NuqValues
   const int ch = tid >> 1, half = tid & 1;  // channel role
   const int blk0 = grp * kValueTiles, blk1 = min(a.n_blocks, blk0 + kValueTiles);
   auto block_loop = [&](auto cells_tag) {
-  constexpr bool CELLS = decltype(cells_tag)::value;
-  for (int blk = blk0; blk < blk1; ++blk) {
-    const int buf = (blk - blk0) & 1;
-    const int64_t tok = a.tok0 + (int64_t)blk * kGroup + t;
-    // ---- token role: this thread's 16 channels, straight from HBM into registers
-    uint32_t xw[8];
-    {
-      const uint4* p = reinterpret_cast<const uint4*>(
-          a.v + b * a.sb + h * a.sh + ((int64_t)blk * kGroup + t) * a.st + part * 16);
-      const uint4 u0 = p[0], u1 = p[1];
-      xw[0] = u0.x; xw[1] = u0.y; xw[2] = u0.z; xw[3] = u0.w;
-      xw[4] = u1.x; xw[5] = u1.y; xw[6] = u1.z; xw[7] = u1.w;
-    }
-    const uint32_t outm = VOUT ? value_outliers(xw, part, a.kv) : 0u;
-    float mn = __builtin_inff(), mx = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (!((outm >> j) & 1u)) {
-        const float x = (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
+    constexpr bool CELLS = decltype(cells_tag)::value;
+    for (int blk = blk0; blk < blk1; ++blk) {
+      const int buf = (blk - blk0) & 1;
+      const int64_t tok = a.tok0 + (int64_t)blk * kGroup + t;
+      // ---- token role: this thread's 16 channels, straight from HBM into registers
+      uint32_t xw[8];
+      {
+        const uint4* p = reinterpret_cast<const uint4*>(
+            a.v + b * a.sb + h * a.sh + ((int64_t)blk * kGroup + t) * a.st + part * 16);
+        const uint4 u0 = p[0], u1 = p[1];
+        xw[0] = u0.x; xw[1] = u0.y; xw[2] = u0.z; xw[3] = u0.w;
+        xw[4] = u1.x; xw[5] = u1.y; xw[6] = u1.z; xw[7] = u1.w;
       }
-    }
+      const uint32_t outm = VOUT ? value_outliers(xw, part, a.kv) : 0u;
+      float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o));
-      mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
-    if (mn > mx) mn = mx = 0.0f;            // every channel an outlier
-    if (VOUT) {
-      // this thread's outliers, channels ascending, after those of the lower parts
-      const uint32_t mine = (uint32_t)__builtin_popcount(outm);
-      uint32_t before = mine;
+      for (int j = 0; j < 16; ++j) {
+        if (!((outm >> j) & 1u)) {
+          const float x = (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+      }
 #pragma unroll
       for (int o = 1; o < 8; o <<= 1) {
-        const uint32_t x = __shfl_up(before, o, 8);
-        if (part >= o) before += x;
+        mn = fminf(mn, __shfl_xor(mn, o));
+        mx = fmaxf(mx, __shfl_xor(mx, o));
       }
-      before -= mine;
-      uint32_t* dst = a.v_out + (bh * a.cap_tokens + tok) * a.kv + before;
-      uint32_t m = outm;
-      for (int i = 0; m != 0u; ++i) {
-        const int j = __builtin_ctz(m);
-        m &= m - 1u;
-        dst[i] = (uint32_t)(part * 16 + j) | (((xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
+      if (mn > mx) mn = mx = 0.0f;            // every channel an outlier
+      if (VOUT) {
+        // this thread's outliers, channels ascending, after those of the lower parts
+        const uint32_t mine = (uint32_t)__builtin_popcount(outm);
+        uint32_t before = mine;
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          const uint32_t x = __shfl_up(before, o, 8);
+          if (part >= o) before += x;
+        }
+        before -= mine;
+        uint32_t* dst = a.v_out + (bh * a.cap_tokens + tok) * a.kv + before;
+        uint32_t m = outm;
+        for (int i = 0; m != 0u; ++i) {
+          const int j = __builtin_ctz(m);
+          m &= m - 1u;
+          dst[i] = (uint32_t)(part * 16 + j) | (((xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
+        }
+      }
+      uint32_t meta;
+      float m0, inv;
+      params_nuq(mn, mx, a.bits, &meta, &m0, &inv);
+      // codes of the 16 channels (an outlier's position, and every position of a token
+      // without a dense range, takes code 0), into the token's row of the code tile
+      const float inv2 = 2.0f * inv;
+      uint32_t cw[4] = {0u, 0u, 0u, 0u};
+      nuq_code16<B, 16, CELLS>(
+          cw,
+          [&](int j) {
+            const float x = (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]);
+            return ((outm >> j) & 1u) || inv2 == 0.0f ? -__builtin_inff() : (x - m0) * inv2;
+          },
+          cells, md);
+      *reinterpret_cast<uint4*>(&codes[buf][t][part * 16]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      if (!a.qnorm) {
+        if (part == 0) a.v_meta[bh * a.cap_tokens + tok] = meta;
+      } else {
+        // Q-Norm: the token's dense sums and code counts (the token's eight threads share a
+        // wave, whose LDS operations run in order), then its metadata
+        ExactSums es;
+        exact_zero(es);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (!((outm >> j) & 1u)) exact_add(es, (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) exact_merge_xor(es, o);
+        qh[t][2 * part] = qh[t][2 * part + 1] = 0u;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (!((outm >> j) & 1u)) atomicAdd(&qh[t][(cw[j >> 2] >> (8 * (j & 3))) & 0xFFu], 1u);
+        __builtin_amdgcn_wave_barrier();
+        if (part == 0) {
+          double sx, sxx;
+          exact_to_f64(es, &sx, &sxx);
+          uint32_t n = 0;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) n += qh[t][c];
+          a.v_meta[bh * a.cap_tokens + tok] = qnorm_meta(meta, sx, sxx, qh[t], n, a.lut, a.bits);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      __syncthreads();
+      // ---- channel role: channel ch of tokens 16 half .. 16 half + 15, codes one per byte
+      {
+        uint32_t cb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+          cb[jj >> 2] |= (uint32_t)codes[buf][16 * half + jj][ch] << (8 * (jj & 3));
+        KVQ_CHECK(a.tok0 / kGroup + blk < a.cap_blocks, kDbgWrite);
+        uint32_t* kw = a.v_codes + (bh * a.cap_blocks + a.tok0 / kGroup + blk) * (kHeadDim * B) +
+                       ch * B;
+        store_code_words<B>(kw, cb, half);
       }
     }
-    uint32_t meta;
-    float m0, inv;
-    params_nuq(mn, mx, a.bits, &meta, &m0, &inv);
-    // codes of the 16 channels (an outlier's position, and every position of a token
-    // without a dense range, takes code 0), into the token's row of the code tile
-    const float inv2 = 2.0f * inv;
-    uint32_t cw[4] = {0u, 0u, 0u, 0u};
-    nuq_code16<B, 16, CELLS>(
-        cw,
-        [&](int j) {
-          const float x = (j & 1) ? hi_f16(xw[j >> 1]) : lo_f16(xw[j >> 1]);
-          return ((outm >> j) & 1u) || inv2 == 0.0f ? -__builtin_inff() : (x - m0) * inv2;
-        },
-        cells, md);
-    *reinterpret_cast<uint4*>(&codes[buf][t][part * 16]) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    if (!a.qnorm) {
-      if (part == 0) a.v_meta[bh * a.cap_tokens + tok] = meta;
-    } else {
-      // Q-Norm: the token's dense sums and code counts (the token's eight threads share a
-      // wave, whose LDS operations run in order), then its metadata
-      ExactSums es;
-      exact_zero(es);
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (!((outm >> j) & 1u)) exact_add(es, (xw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) exact_merge_xor(es, o);
-      qh[t][2 * part] = qh[t][2 * part + 1] = 0u;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (!((outm >> j) & 1u)) atomicAdd(&qh[t][(cw[j >> 2] >> (8 * (j & 3))) & 0xFFu], 1u);
-      __builtin_amdgcn_wave_barrier();
-      if (part == 0) {
-        double sx, sxx;
-        exact_to_f64(es, &sx, &sxx);
-        uint32_t n = 0;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) n += qh[t][c];
-        a.v_meta[bh * a.cap_tokens + tok] = qnorm_meta(meta, sx, sxx, qh[t], n, a.lut, a.bits);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    __syncthreads();
-    // ---- channel role: channel ch of tokens 16 half .. 16 half + 15, codes one per byte
-    {
-      uint32_t cb[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj)
-        cb[jj >> 2] |= (uint32_t)codes[buf][16 * half + jj][ch] << (8 * (jj & 3));
-      KVQ_CHECK(a.tok0 / kGroup + blk < a.cap_blocks, kDbgWrite);
-      uint32_t* kw = a.v_codes + (bh * a.cap_blocks + a.tok0 / kGroup + blk) * (kHeadDim * B) +
-                     ch * B;
-      store_code_words<B>(kw, cb, half);
-    }
-  }
   };
   if (by_cells) block_loop(CellsTag<true>{});
   else block_loop(CellsTag<false>{});
