@@ -5,18 +5,21 @@
 // O = P V_hat are small dense products (g rows against the block's 32 tokens and 128
 // channels) - the case where the dequantized dot products stop being HBM-bound and the
 // vector ALUs become the limit ("The KV cache has a geometry problem", section on
-// grouped-query attention; KIVI post, "Experiments").  Both products run on
-// v_mfma_f32_16x16x32_bf16; the codes never leave their packed form except for one
-// AND-OR per pair:
+// grouped-query attention; KIVI post, "Experiments").  The scores run on
+// v_mfma_f32_16x16x32_bf16 and the value products on v_mfma_f32_16x16x32_f16; the codes
+// never leave their packed form except for one AND-OR per pair:
 //
-//   * a 2-bit (4-bit) code field masked into the low mantissa bits of a bf16 with
-//     exponent 0 is the exact value 1 + c * 2^(p - 7) (p = the field's bit position),
-//     so one v_and_or_b32 turns two codes into two bf16 matrix elements;
-//   * the per-block weights (q * key scale, p * value scale) are fp32; each is split
-//     into bf16 hi + lo (about 16 significant bits) and both go in as matrix rows or
-//     columns, the factor 2^(7 - p) folded into them;
+//   * a 2-bit (4-bit) code field masked into the low mantissa bits of a bf16 (fp16) 1.0
+//     is the exact value 1 + c * 2^(p - 7) (1 + c * 2^(p - 10)), p = the field's bit
+//     position, so one v_and_or_b32 turns two codes into two matrix elements;
+//   * the key weights q * scale are fp32, each split into bf16 hi + lo (about 16
+//     significant bits), both rows of the A operand, the factor 2^(7 - p) folded in;
+//   * the value weights p * scale enter as fp16, scaled by 2^-e with e the wave's
+//     exponent, raised (and the sums rescaled by an exact power of two) whenever a weight
+//     would reach 2^15; one rounding per weight, at most 2^-11 relative;
 //   * the constant 1 of every element is removed with one more product against a
-//     constant matrix (-1 for the scores, +1 for the value weights' column sums).
+//     constant matrix (-1 for the scores, +1 for the value weights' column sums), with
+//     the same rounded weights, so it cancels exactly.
 //
 // Keys: rows = (head, hi/lo), K = channels (4 steps of 32), columns = 16 tokens; the
 // weights reach the A operand through LDS in matrix order.  Values: rows = 16 channel
@@ -51,6 +54,7 @@ constexpr int kPRow = 36;                      // floats per p / value-meta row 
 // literals the compiler would emit a separate AND and OR.
 struct Unpack {
   uint32_t one;                 // (1.0, 1.0) bf16, VGPR
+  uint32_t one_h;               // (1.0, 1.0) fp16, VGPR
   uint32_t m2[3];               // 2-bit field masks at positions 0, 2, 4 of each half
   uint32_t m4;                  // 4-bit field mask at position 0 of each half
 };
@@ -62,6 +66,7 @@ __device__ __forceinline__ uint32_t opaque_sgpr(uint32_t x) {
 __device__ __forceinline__ Unpack make_unpack() {
   Unpack u;
   u.one = __builtin_amdgcn_mov_dpp(kOne2, 0xE4, 0xF, 0xF, true);
+  u.one_h = __builtin_amdgcn_mov_dpp(0x3C003C00u, 0xE4, 0xF, 0xF, true);
   u.m2[0] = opaque_sgpr(0x00030003u);
   u.m2[1] = opaque_sgpr(0x000C000Cu);
   u.m2[2] = opaque_sgpr(0x00300030u);
@@ -76,6 +81,15 @@ __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t o
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16h(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16(float x0, float x1) {
+  const h2_t v = {(_Float16)x0, (_Float16)x1};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
@@ -118,17 +132,17 @@ __device__ __forceinline__ u32x4 key_step_pairs(const uint32_t* k, int ks, const
 
 // Pair T (tile T: channel T of the octet) of the four token-pair words of a value tile.
 template <int VB>
-__device__ __forceinline__ u32x4 value_tile_pairs(const uint32_t* vc, int t, const Unpack& u) {
+__device__ __forceinline__ u32x4 value_tile_pairs(const uint32_t* vc, int t, const Unpack& u,
+                                                  uint32_t one) {
   if constexpr (VB == 2) {
     const int sh = t < 3 ? 0 : t < 6 ? 6 : 12;
     const uint32_t m = u.m2[t % 3];
-    return u32x4{and_or(vc[0] >> sh, m, u.one), and_or(vc[1] >> sh, m, u.one),
-                 and_or(vc[2] >> sh, m, u.one), and_or(vc[3] >> sh, m, u.one)};
+    return u32x4{and_or(vc[0] >> sh, m, one), and_or(vc[1] >> sh, m, one),
+                 and_or(vc[2] >> sh, m, one), and_or(vc[3] >> sh, m, one)};
   } else {
     const int base = 4 * (t >> 2), sh = 4 * (t & 3);
-    return u32x4{and_or(vc[base] >> sh, u.m4, u.one), and_or(vc[base + 1] >> sh, u.m4, u.one),
-                 and_or(vc[base + 2] >> sh, u.m4, u.one),
-                 and_or(vc[base + 3] >> sh, u.m4, u.one)};
+    return u32x4{and_or(vc[base] >> sh, u.m4, one), and_or(vc[base + 1] >> sh, u.m4, one),
+                 and_or(vc[base + 2] >> sh, u.m4, one), and_or(vc[base + 3] >> sh, u.m4, one)};
   }
 }
 
@@ -243,6 +257,7 @@ struct GqState {
   float mv;            // p * min over this lane's tokens, column (head, group)
   f32x4 acc[8];        // value products: tile T, rows = channel octets, cols = (head, group)
   f32x4 corr;          // column sums of the value weights (the constant-1 part)
+  int e;               // fp16 value weights: acc and corr are kept scaled by 2^-e
 };
 
 template <int KB, int VB, int GQ>
@@ -345,28 +360,39 @@ __device__ __forceinline__ void gq_block(const GqRegs<KB, VB>& r, GqState<GQ>& s
     vw[0] = b0.x; vw[1] = b0.y; vw[2] = b0.z; vw[3] = b0.w;
     vw[4] = b1.x; vw[5] = b1.y; vw[6] = b1.z; vw[7] = b1.w;
   }
-  u32x4 bhi, blo;
+  // fp16 weights p * scale * 2^-e, e the wave's exponent: raised (and the sums rescaled
+  // by an exact power of two) whenever a weight would reach 2^15
+  float w8[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t h, l;
-    split_bf16(pw[2 * i] * lo_f16(vw[2 * i]), pw[2 * i + 1] * lo_f16(vw[2 * i + 1]), h, l);
-    bhi[i] = h;
-    blo[i] = l;
+  for (int i = 0; i < 8; ++i) w8[i] = pw[i] * lo_f16(vw[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
     st.mv = fmaf(pw[2 * i], hi_f16(vw[2 * i]), fmaf(pw[2 * i + 1], hi_f16(vw[2 * i + 1]), st.mv));
-  }
-  const u32x4 ones = {up.one, up.one, up.one, up.one};
-  st.corr = mfma16(ones, bhi, st.corr);
-  st.corr = mfma16(ones, blo, st.corr);
-
-  // ---- values: A = codes of channel octet n (tile T: channel 8n + T), tokens 8u..8u+7
-  u32x4 at[8];
+  float wmax = w8[0];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    at[t] = value_tile_pairs<VB>(r.vc, t, up);
-    st.acc[t] = mfma16(at[t], bhi, st.acc[t]);
-  }
+  for (int i = 1; i < 8; ++i) wmax = fmaxf(wmax, w8[i]);
+  if (__any(ldexpf(wmax, -st.e) >= 32768.0f)) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) st.acc[t] = mfma16(at[t], blo, st.acc[t]);
+    for (int o = 1; o < kWave; o <<= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, o));
+    int x;
+    (void)frexpf(wmax, &x);
+    const int e1 = __builtin_amdgcn_readfirstlane(x - 15);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) st.acc[t][rr] = ldexpf(st.acc[t][rr], st.e - e1);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) st.corr[rr] = ldexpf(st.corr[rr], st.e - e1);
+    st.e = e1;
+  }
+  u32x4 bw;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bw[i] = pack_f16(ldexpf(w8[2 * i], -st.e), ldexpf(w8[2 * i + 1], -st.e));
+  const u32x4 ones = {up.one_h, up.one_h, up.one_h, up.one_h};
+  st.corr = mfma16h(ones, bw, st.corr);
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    st.acc[t] = mfma16h(value_tile_pairs<VB>(r.vc, t, up, up.one_h), bw, st.acc[t]);
 }
 
 template <int KB, int VB, int GQ, int NW>
@@ -439,6 +465,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) st.acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.corr = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.e = -24;
   if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
     const uint32_t* kc = a.k_codes + seg * (kGroup * kHeadDim * KB / 32);
@@ -475,7 +502,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_gqa_kernel(DecodeArgs a) {
     if (j < GQ && g == u) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float f = VB == 2 ? pair_factor(2, t) : 128.0f;
+        // fp16 elements 1 + c 2^(p - 10), sums scaled by 2^-e
+        const float f = ldexpf(VB == 2 ? pair_factor(2, t) * 8.0f : 1024.0f, st.e);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           wo[wave][j][8 * (4 * u + rr) + t] = (st.acc[t][rr] - st.corr[rr]) * f + mv;
