@@ -188,6 +188,7 @@ __device__ __forceinline__ Fp16Chunk fp16_chunk(const DecodeArgs& a, int64_t bh,
 constexpr int kPartialStride = kHeadDim + 4;   // o[128], m, l, pad
 constexpr int kMaxSplits = 2048;               // workgroups per (batch, kv head) at most
 constexpr int kNuqChunk = 2048;                // tokens per chunk in the nuq key passes
+constexpr int kNuqListCap = 32;                // threshold-bin entries kept per chunk and channel
 constexpr int64_t kMaxCapacityTokens = (int64_t)1 << 28;   // packed tokens per (batch, head)
 
 struct NuqKeysArgs {
@@ -212,6 +213,7 @@ struct NuqKeysArgs {
   int32_t* thr;             // [bh][D][4]: T, need, high bin, count above
   float* norm;              // [bh][D][2]: min, 1/scale
   uint32_t* chunk_stats;    // [bh][nchunks][D][8]
+  uint32_t* lists;          // [bh][nchunks][D][kNuqListCap]: threshold-bin entries
   uint32_t* tie_prefix;     // [bh][nchunks][D]
   uint32_t* chunk_cnt;      // [bh][nchunks]
   uint32_t* chunk_off;      // [bh][nchunks]

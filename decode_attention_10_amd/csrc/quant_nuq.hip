@@ -284,6 +284,28 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
     p[i] = v;
 }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Per-half fp16 max / min of two pairs (finite inputs), without the canonicalizing
+// multiplies the compiler would add around the generic min / max.
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t x, uint32_t y) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t x, uint32_t y) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+// Bits of a where mask is set, of b elsewhere (one v_bfi_b32; written out, the compiler
+// turns a per-half mask back into compares and selects).
+__device__ __forceinline__ uint32_t bitsel(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+  return r;
+}
+
 // ---- 1/3: magnitude histograms (LDS counts are u16 pairs packed in u32) ------------
 // A lane owns two adjacent channels (one 4-byte load per token).  The high-bin pass keeps
 // 256 bins per channel, so a workgroup takes half of the channels (64): its LDS (33 KB)
@@ -293,13 +315,26 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 // start on different LDS banks: key magnitudes crowd into a few bins, and unpadded rows
 // put a wave's atomics on the same few banks.  Sixteen tokens' loads are issued before
 // their atomics.
+//
+// The low-bin pass also gathers what the chunk statistics need once the threshold T
+// inside the high bin is known: per chunk and channel the min / max of the entries below
+// the high bin (dense whatever T is), the count of those above it (outliers whatever T
+// is), and the entries of the high bin itself, as (fp16 bits << 16 | token in the
+// chunk), at most kNuqListCap per channel.  The count is stored even when it exceeds the
+// list; such a chunk is read again by the statistics pass.  (Lists per token row with
+// counters in registers instead of one LDS counter per channel measured slower: 2.46 ms
+// against 2.37 ms on the 1M-token keys.)
 template <bool LOW>
 __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
   constexpr int NB = LOW ? 128 : 256;
   constexpr int CH = LOW ? kHeadDim : kHeadDim / 2;       // channels per workgroup
   constexpr int LPT = CH / 2;                             // lanes per token
   constexpr int RW = NB / 2 + 1;                          // words per channel row
+  constexpr int TW = kThreads / LPT;                      // token rows of a pass
   __shared__ uint32_t h[CH][RW];
+  __shared__ uint32_t lcnt[LOW ? kHeadDim : 1];
+  __shared__ float rmin[LOW ? TW : 1][LOW ? kHeadDim : 1], rmax[LOW ? TW : 1][LOW ? kHeadDim : 1];
+  __shared__ uint32_t rab[LOW ? TW : 1][LOW ? kHeadDim : 1];
   constexpr int PARTS = kHeadDim / CH;
   const int64_t job = blockIdx.x / PARTS;
   const int c0 = (int)(blockIdx.x % PARTS) * CH;          // first channel of this group
@@ -307,39 +342,102 @@ __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
   const int chunk = (int)(job % a.nchunks);
   const int tid = threadIdx.x;
   for (int i = tid; i < CH * RW; i += kThreads) (&h[0][0])[i] = 0;
-  int sel0 = -1, sel1 = -1;
+  if (LOW && tid < kHeadDim) lcnt[tid] = 0;
   const int cp = tid % LPT;                               // channels c0 + 2cp, c0 + 2cp + 1
+  // low pass: magnitudes below lo are dense, from hi on outliers, in between the high
+  // bin; without a high bin (no outliers, or all) lo = hi = T.  A lane tests its two
+  // channels at once on 16-bit halves: lo - 1 - m and hi - 1 - m lie in [-2^15, 2^15)
+  // and are negative exactly where m >= lo (not dense) and m >= hi (above).
+  s16x2 lom1 = {0, 0}, him1 = {0, 0};
   if (LOW) {
-    sel0 = a.thr[(bh * kHeadDim + c0 + 2 * cp) * 4 + 2];
-    sel1 = a.thr[(bh * kHeadDim + c0 + 2 * cp + 1) * 4 + 2];
+    auto bounds = [&](int ch, int& lo, int& hi) {
+      const int32_t* th = a.thr + (bh * kHeadDim + ch) * 4;
+      const int hb = th[2];
+      if (hb >= 0) {
+        lo = hb << 7;
+        hi = (hb + 1) << 7;
+      } else {
+        lo = hi = th[0] < 0 ? 0 : 0x8000;
+      }
+    };
+    int lo0, hi0, lo1, hi1;
+    bounds(c0 + 2 * cp, lo0, hi0);
+    bounds(c0 + 2 * cp + 1, lo1, hi1);
+    lom1 = s16x2{(short)(lo0 - 1), (short)(lo1 - 1)};
+    him1 = s16x2{(short)(hi0 - 1), (short)(hi1 - 1)};
   }
+  uint32_t amin = 0x7C007C00u, amax = 0xFC00FC00u;        // fp16 pairs: dense min / max
+  s16x2 nabove = {0, 0};                                  // minus the counts above
   __syncthreads();
   const int64_t t0 = (int64_t)chunk * kNuqChunk;
   const int64_t t1 = min((int64_t)a.n_tokens, t0 + kNuqChunk);
-  auto count = [&](uint32_t w) {
-    const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
+  // this lane's lists: channels 2cp and 2cp + 1
+  uint32_t* list0 = LOW ? a.lists + ((bh * a.nchunks + chunk) * kHeadDim + 2 * cp) * kNuqListCap
+                        : nullptr;
+  // x: the entry's fp16 bits in the high half, m: its magnitude
+  auto in_bin = [&](int k, uint32_t x, uint32_t m, int64_t t) {
+    atomicAdd(&h[2 * cp + k][(m & 127u) >> 1], m & 1u ? 0x10000u : 1u);
+    const uint32_t slot = atomicAdd(&lcnt[2 * cp + k], 1u);
+    if (slot < (uint32_t)kNuqListCap)
+      list0[k * kNuqListCap + slot] = x | (uint32_t)(t - t0);
+  };
+  auto count = [&](uint32_t w, int64_t t) {
     if (!LOW) {
+      const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
       atomicAdd(&h[2 * cp][(m0 >> 7) >> 1], (m0 >> 7) & 1u ? 0x10000u : 1u);
       atomicAdd(&h[2 * cp + 1][(m1 >> 7) >> 1], (m1 >> 7) & 1u ? 0x10000u : 1u);
     } else {
-      if ((int)(m0 >> 7) == sel0) atomicAdd(&h[2 * cp][(m0 & 127u) >> 1], m0 & 1u ? 0x10000u : 1u);
-      if ((int)(m1 >> 7) == sel1) atomicAdd(&h[2 * cp + 1][(m1 & 127u) >> 1], m1 & 1u ? 0x10000u : 1u);
+      const uint32_t m = w & 0x7FFF7FFFu;
+      const s16x2 ms = __builtin_bit_cast(s16x2, m);
+      const uint32_t nd = __builtin_bit_cast(uint32_t, (s16x2)((lom1 - ms) >> 15));
+      const s16x2 abm = (him1 - ms) >> 15;
+      nabove += abm;
+      amax = pk_max_f16(amax, bitsel(nd, 0xFC00FC00u, w));
+      amin = pk_min_f16(amin, bitsel(nd, 0x7C007C00u, w));
+      const uint32_t mid = nd & ~__builtin_bit_cast(uint32_t, abm);
+      if (mid) {
+        if (mid & 0xFFFFu) in_bin(0, w << 16, m & 0xFFFFu, t);
+        if (mid >> 16) in_bin(1, w & 0xFFFF0000u, m >> 16, t);
+      }
     }
   };
   constexpr int U = 16;                                   // tokens in flight per lane
-  constexpr int STEP = kThreads / LPT;                    // tokens per pass of the block
   int64_t t = t0 + tid / LPT;
-  for (; t + (int64_t)(U - 1) * STEP < t1; t += (int64_t)U * STEP) {
+  for (; t + (int64_t)(U - 1) * TW < t1; t += (int64_t)U * TW) {
     uint32_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * STEP) + c0 + 2 * cp);
+      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * TW) + c0 + 2 * cp);
 #pragma unroll
-    for (int u = 0; u < U; ++u) count(w[u]);
+    for (int u = 0; u < U; ++u) count(w[u], t + u * TW);
   }
-  for (; t < t1; t += STEP)
-    count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + c0 + 2 * cp));
+  for (; t < t1; t += TW)
+    count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + c0 + 2 * cp), t);
+  if (LOW) {
+    const int r = tid / LPT;
+    rmin[r][2 * cp] = f16_bits_to_f32((uint16_t)amin);
+    rmin[r][2 * cp + 1] = f16_bits_to_f32((uint16_t)(amin >> 16));
+    rmax[r][2 * cp] = f16_bits_to_f32((uint16_t)amax);
+    rmax[r][2 * cp + 1] = f16_bits_to_f32((uint16_t)(amax >> 16));
+    rab[r][2 * cp] = (uint32_t)(uint16_t)(-nabove[0]);
+    rab[r][2 * cp + 1] = (uint32_t)(uint16_t)(-nabove[1]);
+  }
   __syncthreads();
+  if (LOW && tid < kHeadDim) {
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    uint32_t ab = 0u;
+#pragma unroll
+    for (int r = 0; r < TW; ++r) {
+      mn = fminf(mn, rmin[r][tid]);
+      mx = fmaxf(mx, rmax[r][tid]);
+      ab += rab[r][tid];
+    }
+    uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + tid) * 8;
+    cs[3] = __builtin_bit_cast(uint32_t, mn);
+    cs[4] = __builtin_bit_cast(uint32_t, mx);
+    cs[5] = ab;
+    cs[7] = lcnt[tid];
+  }
   uint32_t* g = LOW ? a.hist_lo : a.hist_hi;
   for (int i = tid; i < CH * NB / 2; i += kThreads) {
     const int d = i / (NB / 2), b2 = i % (NB / 2);
@@ -405,10 +503,13 @@ __device__ __forceinline__ void store_key_tile(uint16_t (*tile)[kHeadDim], const
 }
 
 // ---- 4: per chunk: ties, last positive / negative tie, dense min / max ----------------
-// Two threads per channel (tokens 0..15 and 16..31 of each 32-token tile); a chunk's ties
-// are numbered in token order, the second half's after the first half's of the same
-// tile.  Tiles are double-buffered in LDS and each is requested into registers while the
-// one before it is read.
+// From the low-bin pass's gathering when every channel's high-bin entries of the chunk
+// fit its list: the entries below T add to the dense min / max, those above to the count
+// above T, and the ties are ranked in token order by their token offsets.  Otherwise the
+// chunk is read again: two threads per channel (tokens 0..15 and 16..31 of each 32-token
+// tile); a chunk's ties are numbered in token order, the second half's after the first
+// half's of the same tile.  Tiles are double-buffered in LDS and each is requested into
+// registers while the one before it is read.
 __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a) {
   __shared__ __align__(16) uint16_t tiles[2][kGroup][kHeadDim];
   const int64_t bh = blockIdx.x / a.nchunks;
@@ -416,6 +517,70 @@ __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a
   const int tid = threadIdx.x;
   const int ch = tid >> 1, half = tid & 1;
   const int T = a.thr[(bh * kHeadDim + ch) * 4];
+  uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + ch) * 8;
+  const uint32_t n_list = cs[7];
+  if (!__syncthreads_or(n_list > (uint32_t)kNuqListCap)) {
+    // every listed entry lies in T's high bin (none without one); this thread takes
+    // entries 16 half .. 16 half + 15, all requested at once
+    const uint4* lp = reinterpret_cast<const uint4*>(
+        a.lists + ((bh * a.nchunks + chunk) * kHeadDim + ch) * kNuqListCap + 16 * half);
+    uint32_t ent[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = lp[q];
+      ent[4 * q] = u.x; ent[4 * q + 1] = u.y; ent[4 * q + 2] = u.z; ent[4 * q + 3] = u.w;
+    }
+    const int nmine = min(max((int)n_list - 16 * half, 0), 16);
+    const uint32_t tbits = (uint32_t)T;                   // T's magnitude bits
+    uint32_t run = 0u, above = 0u;
+    int32_t pos_tok = -1, neg_tok = -1;
+    float dmin = __builtin_inff(), dmax = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nmine) {
+        const uint32_t x = ent[i] >> 16, mag = x & 0x7FFFu;
+        const int tok = (int)(ent[i] & 2047u);
+        if (mag < tbits) {
+          const float v = f16_bits_to_f32((uint16_t)x);
+          dmin = fminf(dmin, v);
+          dmax = fmaxf(dmax, v);
+        } else if (mag > tbits) {
+          above += 1u;
+        } else {
+          run += 1u;
+          if (x >> 15) neg_tok = max(neg_tok, tok);
+          else pos_tok = max(pos_tok, tok);
+        }
+      }
+    }
+    pos_tok = max(pos_tok, __shfl_xor(pos_tok, 1));
+    neg_tok = max(neg_tok, __shfl_xor(neg_tok, 1));
+    // rank of the last positive (negative) tie: the ties at earlier tokens
+    uint32_t rp = 0u, rn = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < nmine && ((ent[i] >> 16) & 0x7FFFu) == tbits) {
+        const int tok = (int)(ent[i] & 2047u);
+        rp += tok < pos_tok ? 1u : 0u;
+        rn += tok < neg_tok ? 1u : 0u;
+      }
+    }
+    run += __shfl_xor(run, 1);
+    above += __shfl_xor(above, 1);
+    rp += __shfl_xor(rp, 1);
+    rn += __shfl_xor(rn, 1);
+    dmin = fminf(dmin, __shfl_xor(dmin, 1));
+    dmax = fmaxf(dmax, __shfl_xor(dmax, 1));
+    if (half == 0) {
+      cs[0] = run;
+      cs[1] = pos_tok >= 0 ? rp : 0xFFFFFFFFu;
+      cs[2] = neg_tok >= 0 ? rn : 0xFFFFFFFFu;
+      cs[3] = __builtin_bit_cast(uint32_t, fminf(__builtin_bit_cast(float, cs[3]), dmin));
+      cs[4] = __builtin_bit_cast(uint32_t, fmaxf(__builtin_bit_cast(float, cs[4]), dmax));
+      cs[5] += above;
+    }
+    return;
+  }
   uint32_t run = 0, above = 0;              // ties so far in the chunk; values above T
   int32_t last_pos = -1, last_neg = -1;
   float dmin = __builtin_inff(), dmax = -__builtin_inff();
@@ -476,7 +641,6 @@ __global__ __launch_bounds__(kThreads) void nuq_chunk_stats_kernel(NuqKeysArgs a
   last_pos = max(last_pos, __shfl_xor(last_pos, 1));
   last_neg = max(last_neg, __shfl_xor(last_neg, 1));
   if (half == 0) {
-    uint32_t* cs = a.chunk_stats + ((bh * a.nchunks + chunk) * kHeadDim + ch) * 8;
     cs[0] = run;
     cs[1] = (uint32_t)last_pos;
     cs[2] = (uint32_t)last_neg;

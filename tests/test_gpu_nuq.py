@@ -157,6 +157,37 @@ def test_nuq_keys_many_ties_at_the_threshold():
         _check_head(c, 0, h, O.nuq_head(k[0, h], v[0, h], L, L, 150, n, 0, 0.0), n, 150)
 
 
+
+def test_nuq_threshold_bin_lists_and_rereads():
+    """The low-histogram pass lists each chunk's entries of the threshold's high bin, at
+    most 32 per chunk and channel; a chunk with more is read again.  Head 0: the first
+    2048-token chunk on the integer grid -3..3 (hundreds of entries at the threshold 3.0:
+    read again), the rest N(0,1) (listed).  Head 1: 0.3 N(0,1) plus, in every chunk and
+    channel, 25 entries of +-3.0 and d % 11 of +-4.0 at random tokens, positive with
+    probability (d % 8) / 7: the threshold is 3.0, every list holds ties of one or both
+    signs, and the earliest ties in token order become the outliers."""
+    B, H, n = 1, 2, 3 * 2048 + 64
+    bp = 96                                               # k = 60 per channel
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((B, H, n, 128))
+    x[0, 0, :2048] = rng.integers(-3, 4, size=(2048, 128))
+    x[0, 1] *= 0.3
+    for c0 in range(0, n, 2048):
+        c1 = min(n, c0 + 2048)
+        for d in range(128):
+            n4 = d % 11
+            toks = rng.choice(np.arange(c0, c1), size=25 + n4, replace=False)
+            mag = np.where(np.arange(25 + n4) < 25, 3.0, 4.0)
+            sign = np.where(rng.random(25 + n4) < (d % 8) / 7.0, 1.0, -1.0)
+            x[0, 1, toks, d] = sign * mag
+    k = x.astype(np.float16).view(np.uint16)
+    v = S.gen_tensor(23, S.TID_V, B, H, n, 128)
+    L = S.nuq3_lut()
+    c = _nuq_cache(B, H, n, 0, bp, L, L)
+    _quantize(c, k, v, n)
+    for h in range(H):
+        _check_head(c, 0, h, O.nuq_head(k[0, h], v[0, h], L, L, bp, n, 0, 0.0), n, bp)
+
 DECODE = [
     # B, Hkv, GQ, n_packed, n_resid, R, bp, theta
     (1, 1, 1, 512, 0, 0, 100, 1e4),
