@@ -381,35 +381,59 @@ __global__ __launch_bounds__(kThreads) void nuq_hist_kernel(NuqKeysArgs a) {
     if (slot < (uint32_t)kNuqListCap)
       list0[k * kNuqListCap + slot] = x | (uint32_t)(t - t0);
   };
+  // low pass, every word: dense min / max and the count above; returns the word's
+  // high-bin mask (0xFFFF in each half that holds an entry of the high bin)
+  auto classify = [&](uint32_t w) -> uint32_t {
+    const uint32_t m = w & 0x7FFF7FFFu;
+    const s16x2 ms = __builtin_bit_cast(s16x2, m);
+    const uint32_t nd = __builtin_bit_cast(uint32_t, (s16x2)((lom1 - ms) >> 15));
+    const s16x2 abm = (him1 - ms) >> 15;
+    nabove += abm;
+    amax = pk_max_f16(amax, bitsel(nd, 0xFC00FC00u, w));
+    amin = pk_min_f16(amin, bitsel(nd, 0x7C007C00u, w));
+    return nd & ~__builtin_bit_cast(uint32_t, abm);
+  };
   auto count = [&](uint32_t w, int64_t t) {
     if (!LOW) {
       const uint32_t m0 = w & 0x7FFFu, m1 = (w >> 16) & 0x7FFFu;
       atomicAdd(&h[2 * cp][(m0 >> 7) >> 1], (m0 >> 7) & 1u ? 0x10000u : 1u);
       atomicAdd(&h[2 * cp + 1][(m1 >> 7) >> 1], (m1 >> 7) & 1u ? 0x10000u : 1u);
     } else {
-      const uint32_t m = w & 0x7FFF7FFFu;
-      const s16x2 ms = __builtin_bit_cast(s16x2, m);
-      const uint32_t nd = __builtin_bit_cast(uint32_t, (s16x2)((lom1 - ms) >> 15));
-      const s16x2 abm = (him1 - ms) >> 15;
-      nabove += abm;
-      amax = pk_max_f16(amax, bitsel(nd, 0xFC00FC00u, w));
-      amin = pk_min_f16(amin, bitsel(nd, 0x7C007C00u, w));
-      const uint32_t mid = nd & ~__builtin_bit_cast(uint32_t, abm);
+      const uint32_t mid = classify(w);
       if (mid) {
-        if (mid & 0xFFFFu) in_bin(0, w << 16, m & 0xFFFFu, t);
-        if (mid >> 16) in_bin(1, w & 0xFFFF0000u, m >> 16, t);
+        if (mid & 0xFFFFu) in_bin(0, w << 16, w & 0x7FFFu, t);
+        if (mid >> 16) in_bin(1, w & 0xFFFF0000u, (w >> 16) & 0x7FFFu, t);
       }
     }
   };
   constexpr int U = 16;                                   // tokens in flight per lane
   int64_t t = t0 + tid / LPT;
   for (; t + (int64_t)(U - 1) * TW < t1; t += (int64_t)U * TW) {
+    const uint16_t* p0 = key_row(a, bh, t) + c0 + 2 * cp;
     uint32_t w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      w[u] = *reinterpret_cast<const uint32_t*>(key_row(a, bh, t + u * TW) + c0 + 2 * cp);
+      w[u] = *reinterpret_cast<const uint32_t*>(p0 + (int64_t)u * TW * a.st);
+    if (!LOW) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) count(w[u], t + u * TW);
+      for (int u = 0; u < U; ++u) count(w[u], t + u * TW);
+    } else {
+      // A wave holds a high-bin entry in about half of its words, so a branch per word
+      // would run on half of them.  Instead the words' high-bin halves are marked (bit
+      // 2u + k: half k of word u) and taken afterwards one per round, each word requested
+      // again (it has just been read: the request is served from the cache).
+      uint32_t midm = 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u) midm |= ((classify(w[u]) >> 15) & 3u) << (2 * u);
+      while (midm) {
+        const int j = __builtin_ctz(midm);
+        midm &= midm - 1u;
+        const int u = j >> 1, k = j & 1;
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(p0 + (int64_t)u * TW * a.st);
+        const uint32_t xh = k ? x & 0xFFFF0000u : x << 16;
+        in_bin(k, xh, (xh >> 16) & 0x7FFFu, t + u * TW);
+      }
+    }
   }
   for (; t < t1; t += TW)
     count(*reinterpret_cast<const uint32_t*>(key_row(a, bh, t) + c0 + 2 * cp), t);
