@@ -13,15 +13,18 @@
 //   1. magnitude histogram of the top 8 of the 15 magnitude bits, per channel
 //   2. the bin that holds the k-th largest magnitude
 //   3. histogram of the low 7 bits inside that bin  ->  exact threshold T and the
-//      number of elements equal to T that are outliers (the earliest tokens)
+//      number of elements equal to T that are outliers (the earliest tokens); the same
+//      read gathers, per chunk of tokens, the dense min/max below that bin, the count
+//      above it, and a list of the bin's own entries
 //   4. per chunk of tokens: ties to T, magnitudes above T, the last positive/negative
-//      tie, dense min/max
+//      tie, dense min/max (from the lists of step 3; a chunk whose list overflowed is
+//      read again)
 //   5. per channel: tie prefix of every chunk, dense min/max -> (scale, min), and each
 //      chunk's outlier count (above T plus the ties ranked below the tie quota)
 //   6. per (batch, head): scan of the chunk counts -> each chunk's first CSR entry
 //   7. codes for every element; the rows of the CSR (row pointers and entries, exact
 //      values from the tile) written in token order by the same pass
-// Every pass reads the keys with coalesced rows; histograms live in LDS and only
+// Steps 1, 3 and 7 read the keys with coalesced rows; histograms live in LDS and only
 // their non-zero bins reach global memory.
 #include "kvq_common.h"
 
