@@ -797,8 +797,12 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
   }
 }
 
+// One query head: 4 waves per SIMD (at most 128 VGPRs) for nuq2 and nuq3; nuq4, whose
+// 16-entry lookups need more registers, spills at that bound and runs at 3 (150 VGPRs:
+// 386 against 438 us on a 256K-token context; nuq2 at 3 waves measured 2 % slower).
 template <int GQ, int NW, int B>
-__global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void decode_nuq_kernel(
+    DecodeArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ NuqShared<GQ> sh;
   __shared__ __align__(16) NuqWaveScratch<GQ, B> wsc[NW];
