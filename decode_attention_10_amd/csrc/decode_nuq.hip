@@ -137,6 +137,31 @@ __device__ __forceinline__ uint32_t value_pair_index4(const uint32_t* w, int q) 
   return x | ((w[2] >> 2) & 0x20202020u);                                  // 28 + k, high
 }
 
+// nuq2 pair-table indices, one per byte (16-entry tables: code of the first element plus
+// 4 times that of the second).  Keys: channel 2i and 2i+1 of tokens 4m..4m+3, both at
+// bits 8k + 2(m % 4) of word m / 4.  Values: tokens 8q + k and 8q + 4 + k of one channel,
+// the adjacent fields at bits 8k + 4(q % 2) of word q / 2, so one shift and one mask.
+__device__ __forceinline__ uint32_t key_pair_index4_2(const uint32_t* w0, const uint32_t* w1,
+                                                      int m) {
+  const int s = 2 * (m & 3);
+  return ((w0[m >> 2] >> s) & 0x03030303u) | (((w1[m >> 2] >> s) << 2) & 0x0C0C0C0Cu);
+}
+__device__ __forceinline__ uint32_t value_pair_index4_2(const uint32_t* w, int q) {
+  return (w[q >> 1] >> (4 * (q & 1))) & 0x0F0F0F0Fu;
+}
+
+// Pair-table indices of either width with tables (nuq2, nuq3).
+template <int B>
+__device__ __forceinline__ uint32_t key_pair_idx(const uint32_t* w0, const uint32_t* w1, int m) {
+  if constexpr (B == 2) return key_pair_index4_2(w0, w1, m);
+  else return key_pair_index4(w0, w1, m);
+}
+template <int B>
+__device__ __forceinline__ uint32_t value_pair_idx(const uint32_t* w, int q) {
+  if constexpr (B == 2) return value_pair_index4_2(w, q);
+  else return value_pair_index4(w, q);
+}
+
 // 4 * (byte k of x): one v_lshlrev_b32 with a byte-select operand (SDWA).  Written out
 // because the compiler, knowing the top bits of each index byte are clear, otherwise
 // prefers a shift and a mask.  Arithmetic only, no memory access.
@@ -355,8 +380,9 @@ struct NuqShared {
   float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
   float lutk[16], lutv[16];
-  // nuq3 code-book pairs: entry a + 8 b holds (lut[a], lut[b]) as fp16 halves.  Keys look
-  // up the two channels of a lane's pair at one token, values two tokens of one channel.
+  // Code-book pairs: entry a + 8 b (nuq3; nuq2: a + 4 b, the first 16) holds
+  // (lut[a], lut[b]) as fp16 halves.  Keys look up the two channels of a lane's pair at
+  // one token, values two tokens of one channel.
   uint32_t tk[64], tv[64];
 };
 
@@ -487,13 +513,13 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     // chain step are used at once
     float part[32];
     qb[0] = base;                                    // q e^(-i t0 theta), see the caller
-    if constexpr (B == 3) {
+    if constexpr (B == 2 || B == 3) {
       // one chain over the 32 tokens; the pair-table entries of tokens 4 m4 .. 4 m4 + 3
       // are requested one group ahead of their use
       Uvw c0 = uvw_of(qb[0], pc), c1 = uvw_of(cmul(qb[0], pc.step), pc);   // tokens k, k + 1
       uint32_t eb[2][4];
       auto fetch = [&](uint32_t (&e)[4], int m4) {
-        const uint32_t x = key_pair_index4(kw0, kw1, m4);
+        const uint32_t x = key_pair_idx<B>(kw0, kw1, m4);
         e[0] = pair_entry<0>(sh.tk, x);
         e[1] = pair_entry<1>(sh.tk, x);
         e[2] = pair_entry<2>(sh.tk, x);
@@ -656,9 +682,9 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
       st.e[j] = e1;
       wsc = ldexpf(w, -e1);
     }
-    // nuq3 pairs tokens 8q + k and 8q + 4 + k (the value pair-table order): token
-    // t = 8q + 4h + k goes to half h of pair 4q + k
-    const int slot = B == 3 ? ((t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1)) : t;
+    // nuq2 and nuq3 pair tokens 8q + k and 8q + 4 + k (the value pair-table order):
+    // token t = 8q + 4h + k goes to half h of pair 4q + k
+    const int slot = B != 4 ? ((t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1)) : t;
     ws.psh[j][slot] = __builtin_bit_cast(uint16_t, (_Float16)wsc);
     st.mv[j] = fmaf(p[j], vm, st.mv[j] * alpha[j]);     // every token counted twice
     st.o[j][0] = o0;
@@ -671,8 +697,8 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                // tokens 8i..8i+7
       const uint4 w8 = pp[i];
-      if constexpr (B == 3) {
-        const uint32_t x0 = value_pair_index4(vw0, i), x1 = value_pair_index4(vw1, i);
+      if constexpr (B == 2 || B == 3) {
+        const uint32_t x0 = value_pair_idx<B>(vw0, i), x1 = value_pair_idx<B>(vw1, i);
         const uint32_t wk[4] = {w8.x, w8.y, w8.z, w8.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {            // tokens 8i + k, 8i + 4 + k
@@ -848,6 +874,11 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void de
     if constexpr (B == 3) {
       sh.tk[lane] = a.lut_k[lane & 7] | ((uint32_t)a.lut_k[lane >> 3] << 16);
       sh.tv[lane] = a.lut_v[lane & 7] | ((uint32_t)a.lut_v[lane >> 3] << 16);
+    } else if constexpr (B == 2) {
+      if (lane < 16) {
+        sh.tk[lane] = a.lut_k[lane & 3] | ((uint32_t)a.lut_k[lane >> 2] << 16);
+        sh.tv[lane] = a.lut_v[lane & 3] | ((uint32_t)a.lut_v[lane >> 2] << 16);
+      }
     }
   }
   __syncthreads();
