@@ -11,8 +11,8 @@
 // e^(-i 32 th_i) per block, started from an angle reduced modulo 2 pi at the wave's
 // first block).  Inside the block chains advance by the three-term recurrence
 // x(t+1) = 2 cos(th_i) x(t) - x(t-1), which every real-linear function of a_i(t) obeys
-// (one chain over the 32 tokens for nuq3 with one query head, two chains from tokens 0
-// and 16 otherwise); with one query head the chains carry s_2i Re(a), s_2i+1 Im(a) and
+// (one chain over the 32 tokens with one query head, two chains from tokens 0 and 16
+// otherwise); with one query head the chains carry s_2i Re(a), s_2i+1 Im(a) and
 // m_2i Re(a) + m_2i+1 Im(a) (key scales and minima folded in), so a token costs three
 // fmas of recurrence and two of score.  Per-pair partial scores of the block's 32 tokens
 // are then summed across lanes (lanes 2t and 2t+1 end with token t).
@@ -26,8 +26,11 @@
 // value outliers (if any) add p_t * (x - dequant(code)) to their channels.  The weights
 // p_t * s_t enter as fp16 (scaled by a per-wave power of two that keeps them below 2^15)
 // in fp16 dot products with fp32 accumulation, two tokens per instruction.
-// Code-book lookups: four codes in the four bytes of a word select bytes of the fp16
-// table with v_perm_b32 (4 or 8 entries in one source pair; 16 entries in two).
+// Code-book lookups: tables in LDS of code-book pairs (entry a + 2^B b = (lut[a],
+// lut[b]) as fp16 halves), indexed per token by the two channels of a lane's key pair
+// and per channel by two tokens of the values; four indices per word, one per byte.
+// With several query heads the keys are dequantized through v_perm_b32 selections from
+// the code book in registers (four codes in the four bytes of a word).
 // Code widths B = 2, 3, 4 (kernel template); sink and window tokens are fp16 chunks.
 #include "kvq_common.h"
 
@@ -150,15 +153,27 @@ __device__ __forceinline__ uint32_t value_pair_index4_2(const uint32_t* w, int q
   return (w[q >> 1] >> (4 * (q & 1))) & 0x0F0F0F0Fu;
 }
 
-// Pair-table indices of either width with tables (nuq2, nuq3).
+// nuq4 pair-table indices (256-entry tables: code of the first element plus 16 times
+// that of the second).  Keys: tokens 4m..4m+3 at bits 8k + 4(m % 2) of word m / 2.
+// Values: tokens 8q + k and 8q + 4 + k are the low and high nibble of byte k of word q,
+// so the code word is the index word.
+__device__ __forceinline__ uint32_t key_pair_index4_4(const uint32_t* w0, const uint32_t* w1,
+                                                      int m) {
+  const int s = 4 * (m & 1);
+  return ((w0[m >> 1] >> s) & 0x0F0F0F0Fu) | (((w1[m >> 1] >> s) << 4) & 0xF0F0F0F0u);
+}
+
+// Pair-table indices of any width.
 template <int B>
 __device__ __forceinline__ uint32_t key_pair_idx(const uint32_t* w0, const uint32_t* w1, int m) {
   if constexpr (B == 2) return key_pair_index4_2(w0, w1, m);
+  else if constexpr (B == 4) return key_pair_index4_4(w0, w1, m);
   else return key_pair_index4(w0, w1, m);
 }
 template <int B>
 __device__ __forceinline__ uint32_t value_pair_idx(const uint32_t* w, int q) {
   if constexpr (B == 2) return value_pair_index4_2(w, q);
+  else if constexpr (B == 4) return w[q];
   else return value_pair_index4(w, q);
 }
 
@@ -183,7 +198,7 @@ __device__ __forceinline__ uint32_t byte_times4(uint32_t x) {
   return r;
 }
 
-// The table entry selected by byte K of a word of table indices (< 64 each).
+// The table entry selected by byte K of a word of table indices (< 256 each).
 template <int K>
 __device__ __forceinline__ uint32_t pair_entry(const uint32_t* table, uint32_t idx4) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) +
@@ -380,10 +395,10 @@ struct NuqShared {
   float2 rot[kGroup][64];    // e^(-i j theta_i) for token j of a block, pair i
   float ks[kHeadDim], km[kHeadDim];
   float lutk[16], lutv[16];
-  // Code-book pairs: entry a + 8 b (nuq3; nuq2: a + 4 b, the first 16) holds
-  // (lut[a], lut[b]) as fp16 halves.  Keys look up the two channels of a lane's pair at
-  // one token, values two tokens of one channel.
-  uint32_t tk[64], tv[64];
+  // Code-book pairs: entry a + 2^B b (the first 4^B entries) holds (lut[a], lut[b]) as
+  // fp16 halves.  Keys look up the two channels of a lane's pair at one token, values two
+  // tokens of one channel.
+  uint32_t tk[256], tv[256];
 };
 
 // Per-wave scratch (LDS).
@@ -490,7 +505,7 @@ template <int GQ, int B>
 __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlockRegs<B>& r, const NuqBlockEntries& be,
                                   const PairConsts& pc,
                                   float2 base,   // e^(-i t0 theta); q e^(-i t0 theta) if GQ == 1
-                                  const Lut<B>& lk, const Lut<B>& lv, NuqState<GQ>& st,
+                                  const Lut<B>& lk, NuqState<GQ>& st,
                                   const NuqShared<GQ>& sh, NuqWaveScratch<GQ, B>& ws, int lane) {
   const int t = lane >> 1;                  // this lane's token after the reduction
   const uint32_t* kw0 = r.kw;
@@ -513,7 +528,7 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
     // chain step are used at once
     float part[32];
     qb[0] = base;                                    // q e^(-i t0 theta), see the caller
-    if constexpr (B == 2 || B == 3) {
+    {
       // one chain over the 32 tokens; the pair-table entries of tokens 4 m4 .. 4 m4 + 3
       // are requested one group ahead of their use
       Uvw c0 = uvw_of(qb[0], pc), c1 = uvw_of(cmul(qb[0], pc.step), pc);   // tokens k, k + 1
@@ -539,40 +554,6 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
             if (k < 30) n = cheb_next(pc.tc, c1, c0);
             c0 = c1;
             c1 = n;
-          }
-        }
-      }
-    } else {
-      // two chains (tokens 0..15 and 16..31), four codes per table lookup
-      const float2 c16 = cmul(qb[0], pc.r16);
-      Uvw ca[2] = {uvw_of(qb[0], pc), uvw_of(c16, pc)};                    // token k
-      Uvw cb[2] = {uvw_of(cmul(qb[0], pc.step), pc), uvw_of(cmul(c16, pc.step), pc)};  // k + 1
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) {               // tokens 4 m4 .. 4 m4 + 3 of each chain
-        uint32_t a[2][2], b[2][2];
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          lut4<B>(lk, codes_of<B>(kw0, m4 + 4 * ch), a[ch][0], a[ch][1]);
-          lut4<B>(lk, codes_of<B>(kw1, m4 + 4 * ch), b[ch][0], b[ch][1]);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int k = 4 * m4 + kk;
-#pragma unroll
-          for (int ch = 0; ch < 2; ++ch) {
-            const uint32_t wa = a[ch][kk >> 1], wb = b[ch][kk >> 1];
-            const float l0 = (kk & 1) ? hi_f16(wa) : lo_f16(wa);
-            const float l1 = (kk & 1) ? hi_f16(wb) : lo_f16(wb);
-            part[16 * ch + k] = fmaf(ca[ch].u, l0, fmaf(ca[ch].v, l1, ca[ch].w));
-          }
-          if (k < 15) {
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-              Uvw n = cb[ch];
-              if (k < 14) n = cheb_next(pc.tc, cb[ch], ca[ch]);
-              ca[ch] = cb[ch];
-              cb[ch] = n;
-            }
           }
         }
       }
@@ -682,9 +663,9 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
       st.e[j] = e1;
       wsc = ldexpf(w, -e1);
     }
-    // nuq2 and nuq3 pair tokens 8q + k and 8q + 4 + k (the value pair-table order):
-    // token t = 8q + 4h + k goes to half h of pair 4q + k
-    const int slot = B != 4 ? ((t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1)) : t;
+    // the value pair tables pair tokens 8q + k and 8q + 4 + k: token t = 8q + 4h + k
+    // goes to half h of pair 4q + k
+    const int slot = (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1);
     ws.psh[j][slot] = __builtin_bit_cast(uint16_t, (_Float16)wsc);
     st.mv[j] = fmaf(p[j], vm, st.mv[j] * alpha[j]);     // every token counted twice
     st.o[j][0] = o0;
@@ -697,35 +678,20 @@ __device__ void process_nuq_block(const NuqStreams& S, int64_t blk, const NuqBlo
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                // tokens 8i..8i+7
       const uint4 w8 = pp[i];
-      if constexpr (B == 2 || B == 3) {
-        const uint32_t x0 = value_pair_idx<B>(vw0, i), x1 = value_pair_idx<B>(vw1, i);
-        const uint32_t wk[4] = {w8.x, w8.y, w8.z, w8.w};
+      const uint32_t x0 = value_pair_idx<B>(vw0, i), x1 = value_pair_idx<B>(vw1, i);
+      const uint32_t wk[4] = {w8.x, w8.y, w8.z, w8.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {            // tokens 8i + k, 8i + 4 + k
-          const uint32_t e0 = k == 0   ? pair_entry<0>(sh.tv, x0)
-                              : k == 1 ? pair_entry<1>(sh.tv, x0)
-                              : k == 2 ? pair_entry<2>(sh.tv, x0)
-                                       : pair_entry<3>(sh.tv, x0);
-          const uint32_t e1 = k == 0   ? pair_entry<0>(sh.tv, x1)
-                              : k == 1 ? pair_entry<1>(sh.tv, x1)
-                              : k == 2 ? pair_entry<2>(sh.tv, x1)
-                                       : pair_entry<3>(sh.tv, x1);
-          o0 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e0), o0, false);
-          o1 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e1), o1, false);
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {            // tokens 4m4..4m4+3, m4 = 2i + h
-          const int m4 = 2 * i + h;
-          const uint32_t w01 = h ? w8.z : w8.x, w23 = h ? w8.w : w8.y;
-          uint32_t a01, a23, b01, b23;
-          lut4<B>(lv, codes_of<B>(vw0, m4), a01, a23);
-          lut4<B>(lv, codes_of<B>(vw1, m4), b01, b23);
-          o0 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(a01), o0, false);
-          o0 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(a23), o0, false);
-          o1 = __builtin_amdgcn_fdot2(as_h2(w01), as_h2(b01), o1, false);
-          o1 = __builtin_amdgcn_fdot2(as_h2(w23), as_h2(b23), o1, false);
-        }
+      for (int k = 0; k < 4; ++k) {              // tokens 8i + k, 8i + 4 + k
+        const uint32_t e0 = k == 0   ? pair_entry<0>(sh.tv, x0)
+                            : k == 1 ? pair_entry<1>(sh.tv, x0)
+                            : k == 2 ? pair_entry<2>(sh.tv, x0)
+                                     : pair_entry<3>(sh.tv, x0);
+        const uint32_t e1 = k == 0   ? pair_entry<0>(sh.tv, x1)
+                            : k == 1 ? pair_entry<1>(sh.tv, x1)
+                            : k == 2 ? pair_entry<2>(sh.tv, x1)
+                                     : pair_entry<3>(sh.tv, x1);
+        o0 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e0), o0, false);
+        o1 = __builtin_amdgcn_fdot2(as_h2(wk[k]), as_h2(e1), o1, false);
       }
     }
     st.o[j][0] = o0;
@@ -827,7 +793,7 @@ __device__ void process_nuq_window(const DecodeArgs& a, int64_t bh, int c,
 // 16-entry lookups need more registers, spills at that bound and runs at 3 (150 VGPRs:
 // 386 against 438 us on a 256K-token context; nuq2 at 3 waves measured 2 % slower).
 template <int GQ, int NW, int B>
-__global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void decode_nuq_kernel(
+__global__ __launch_bounds__(NW * kWave, GQ == 1 ? 4 : 1) void decode_nuq_kernel(
     DecodeArgs a) {
   constexpr int NT = NW * kWave;
   __shared__ NuqShared<GQ> sh;
@@ -864,7 +830,6 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void de
     pc.ks0 = pc.km0 = pc.ks1 = pc.km1 = 0.f;
   }
   const Lut<B> lk = load_lut<B>(a.lut_k);
-  const Lut<B> lv = load_lut<B>(a.lut_v);
   for (int j = wave; j < kGroup; j += NW) sh.rot[j][lane] = to_f32(rot_at64(j, pc.theta));
   if (wave == 0) {
     sh.ks[2 * lane] = pc.ks0; sh.km[2 * lane] = pc.km0;
@@ -878,6 +843,11 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void de
       if (lane < 16) {
         sh.tk[lane] = a.lut_k[lane & 3] | ((uint32_t)a.lut_k[lane >> 2] << 16);
         sh.tv[lane] = a.lut_v[lane & 3] | ((uint32_t)a.lut_v[lane >> 2] << 16);
+      }
+    } else {
+      for (int i = lane; i < 256; i += kWave) {
+        sh.tk[i] = a.lut_k[i & 15] | ((uint32_t)a.lut_k[i >> 4] << 16);
+        sh.tv[i] = a.lut_v[i & 15] | ((uint32_t)a.lut_v[i >> 4] << 16);
       }
     }
   }
@@ -940,13 +910,13 @@ __global__ __launch_bounds__(NW * kWave, GQ == 1 ? (B == 4 ? 3 : 4) : 1) void de
       e1 = load_block_entries(S, min(i + 1, last), rp1, lane);
       rp0 = load_rows(S, min(i + 2, last), lane);
       load_nuq_block<B>(r1, S, min(i + 1, last), lane);
-      process_nuq_block<GQ, B>(S, i, r0, e0, pc, to_f32(base), lk, lv, st, sh, wsc[wave], lane);
+      process_nuq_block<GQ, B>(S, i, r0, e0, pc, to_f32(base), lk, st, sh, wsc[wave], lane);
       base = cmul64(base, pc.step32);
       if (i + 1 >= b1) break;
       e0 = load_block_entries(S, min(i + 2, last), rp0, lane);
       rp1 = load_rows(S, min(i + 3, last), lane);
       load_nuq_block<B>(r0, S, min(i + 2, last), lane);
-      process_nuq_block<GQ, B>(S, i + 1, r1, e1, pc, to_f32(base), lk, lv, st, sh, wsc[wave],
+      process_nuq_block<GQ, B>(S, i + 1, r1, e1, pc, to_f32(base), lk, st, sh, wsc[wave],
                                lane);
       base = cmul64(base, pc.step32);
     }
