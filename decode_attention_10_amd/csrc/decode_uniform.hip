@@ -160,8 +160,6 @@ __device__ __forceinline__ void process_block(const BlockRegs<KB, VB>& r, WaveSt
 // tokens) is units [n_blocks + kWindowUnits*c, n_blocks + kWindowUnits*(c+1)), weighted
 // by its larger byte count.  A split covers a contiguous unit range: the packed blocks
 // in it and every window chunk whose first unit falls in it.
-constexpr int kPullMinBlocks = 8;      // packed blocks per wave from which waves pull them
-
 template <int KB, int VB, int GQ, int NW, bool NT>
 __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a) {
   constexpr int CPW = 32 / KB;
@@ -170,7 +168,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   __shared__ __align__(16) float psL[NW][GQ][4][kRow];
   __shared__ float wm[NW][GQ], wl[NW][GQ];
   __shared__ __align__(16) float wo[NW][GQ][kHeadDim];
-  __shared__ int next_blk;                  // packed blocks pulled so far (pulled deal)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -193,7 +190,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
     qf[j][1] = hi_f16(qreg[j]) * f1 * a.scale_log2;
     if (wave == 0) qh[j][lane] = qreg[j];
   }
-  if (threadIdx.x == 0) next_blk = 0;
   __syncthreads();
 
   const float cscale = a.scale_log2;
@@ -220,39 +216,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_uniform_kernel(DecodeArgs a
   for (int c = c_first; c < c_end; ++c)
     if (NW - 1 - ((c - c_first) % NW) == wave)
       process_window<GQ, VB>(a, bh, c, st, qh, reinterpret_cast<float(*)[kGroup]>(psL[wave]), lane);
-  if (NT && nb >= kPullMinBlocks * NW) {
-    // Pulled deal: each wave takes the split's next packed block from a workgroup
-    // counter in LDS, one block ahead of its use.  A SIMD holds several waves of the
-    // workgroup and issues for the older ones first, so with fixed shares the younger
-    // waves finished last, alone on their SIMDs (llama2_7b, 8-wave groups: waves 4-7
-    // about 5 us after waves 0-3).  Pulling: llama2_13b 115.0-115.6 -> 112.9-113.4 us, llama2_7b within
-    // the noise (same box, four runs each); short splits keep the fixed deal (tiny, two
-    // blocks per wave: 6.35 us fixed, 6.81 us pulled).
-    const int64_t seg = bh * a.cap_blocks;
-    const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
-                         a.k_meta + seg * kHeadDim, a.v_codes + seg * (kHeadDim * VB),
-                         a.v_meta + seg * (kGroup * 4)};
-    auto pull = [&]() -> int {
-      int g = 0;
-      if (lane == 0) g = atomicAdd(&next_blk, 1);
-      return __builtin_amdgcn_readfirstlane(g);
-    };
-    auto blk = [&](int g) { return s0 + min(g, nb - 1); };     // clamped past the end
-    BlockRegs<KB, VB> r0, r1;
-    int g0 = pull(), g1 = pull();
-    load_block<KB, VB, NT>(r0, hp, blk(g0), lane);
-    while (g0 < nb) {
-      load_block<KB, VB, NT>(r1, hp, blk(g1), lane);
-      const int g2 = pull();
-      process_block<KB, VB, GQ>(r0, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
-      if (g1 >= nb) break;
-      load_block<KB, VB, NT>(r0, hp, blk(g2), lane);
-      const int g3 = pull();
-      process_block<KB, VB, GQ>(r1, st, qreg, qf, cscale, qsL[wave], psL[wave], lane);
-      g0 = g2;
-      g1 = g3;
-    }
-  } else if (cnt > 0) {
+  if (cnt > 0) {
     const int64_t seg = bh * a.cap_blocks;
     const HeadPtrs hp = {a.k_codes + seg * (kGroup * kHeadDim * KB / 32),
                          a.k_meta + seg * kHeadDim, a.v_codes + seg * (kHeadDim * VB),
