@@ -255,6 +255,30 @@ def test_nuq_decode_matches_oracle(B, Hkv, GQ, N, r, R, bp, theta):
     _nuq_decode_case(B, Hkv, GQ, N, r, R, bp, theta)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nuq_decode_repeats_bit_for_bit(bits):
+    """Two calls over the same cache, the workspace filled with garbage in between, give
+    the same bytes: the split plan fixes which wave sums which block."""
+    B, H, N = 1, 2, 16384
+    k, v = _kv(91, B, H, N)
+    L = S.nuq_lut(bits)
+    c = _nuq_cache(B, H, N, 0, 100, L, L)
+    _quantize(c, k, v, N)
+    c.c.n_packed, c.c.n_resid = N, 0
+    q = dev(S.gen_tensor(91, S.TID_Q, B, H, 1, 128)[:, :, 0])
+    wsb = K.kvq_workspace_bytes(c.c, H, K.KVQ_OP_DECODE_ATTN)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        out = torch.full((B, H, 128), float("nan"), device="cuda")
+        K.kvq_decode_attn(c.c, q, H, O.default_sm_scale(128), 1e4, out, ws, wsb)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        ws.fill_(0xFF)
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("B,Hkv,GQ,ns,S_len,N,r,R,bp,theta", [
     (1, 2, 1, 4, 4, 2048, 0, 0, 100, 1e4),
     (2, 2, 2, 40, 64, 1024, 37, 64, 100, 1e4),

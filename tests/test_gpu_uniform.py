@@ -158,8 +158,12 @@ def test_decode_empty_cache_is_zero():
     assert not out.any()
 
 
-def test_decode_workspace_needs_no_initialization_and_repeats():
-    B, Hkv, GQ, N, r = 2, 2, 2, 4096, 64
+@pytest.mark.parametrize("B,Hkv,GQ,N,r", [(2, 2, 2, 4096, 64), (1, 4, 1, 16384, 64),
+                                          (8, 32, 1, 2048, 128)])
+def test_decode_workspace_needs_no_initialization_and_repeats(B, Hkv, GQ, N, r):
+    """Repeated calls give the same bytes: every plan fixes which wave sums which block,
+    so the fp32 sums run in the same order (split plans with one and two query heads per
+    kv head, and one workgroup per head with 8 blocks per wave)."""
     k, v = _kv(77, B, Hkv, N + r)
     q = S.gen_tensor(77, S.TID_Q, B, Hkv * GQ, 1, 128)[:, :, 0]
     cache = build_uniform_cache(K, k, v, N, r, 2, 2, 128, cap=N)
