@@ -783,8 +783,10 @@ __device__ __forceinline__ void store_code_words(uint32_t* kw, const uint32_t (&
 // ---- 7: codes and CSR rows ---------------------------------------------------------
 // Four waves per SIMD (at most 128 registers, cell reads in groups of eight): 3.22 ms on
 // the 1M-token keys against 3.68 ms at the three the compiler picks by itself with groups
-// of sixteen.
-template <int B>
+// of sixteen.  Compiled apart with and without Q-Norm (QN): without it the exact moment
+// sums and the per-channel code counts are not kept across the tile loop (105 registers
+// for nuq3 against 128).
+template <int B, bool QN>
 __global__ __launch_bounds__(kThreads, 4) void nuq_quant_keys_kernel(NuqKeysArgs a) {
   // two tiles and outlier masks: the CSR rows of one tile are written while the next is
   // loaded and coded
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 4) void nuq_quant_keys_kernel(NuqKeysArgs
   const bool by_cells = build_code_cells<B>(cells, md, tid);
   ExactSums qs;
   exact_zero(qs);
-  if (a.qnorm)
+  if constexpr (QN)
     for (int i = tid; i < kHeadDim * 16; i += kThreads) (&qh[0][0])[i] = 0u;
   // per-channel state of this lane's channel (two lanes per channel)
   int cT, cneed;
@@ -876,7 +878,7 @@ __global__ __launch_bounds__(kThreads, 4) void nuq_quant_keys_kernel(NuqKeysArgs
           const int jj = __builtin_ctz(ob);
           atomicOr(&om[16 * half + jj][ch >> 5], 1u << (ch & 31));
         }
-        if (a.qnorm) {
+        if constexpr (QN) {
 #pragma unroll
           for (int jj = 0; jj < 16; ++jj) {
             if (!((outbits >> jj) & 1u)) {
@@ -927,7 +929,7 @@ __global__ __launch_bounds__(kThreads, 4) void nuq_quant_keys_kernel(NuqKeysArgs
   };
   if (by_cells) tile_loop(CellsTag<true>{});
   else tile_loop(CellsTag<false>{});
-  if (a.qnorm) {
+  if constexpr (QN) {
     // the two lanes of a channel combine their sums; the block's atomics on qh are done
     exact_merge_xor(qs, 1);
     __syncthreads();
@@ -1222,9 +1224,13 @@ hipError_t launch_nuq_keys(const NuqKeysArgs& a, hipStream_t s) {
     csr_chunk_count_kernel<<<dim3(jobs), dim3(kHeadDim), 0, s>>>(a);
     csr_scan_kernel<<<dim3((unsigned)a.bh_count), dim3(kThreads), 0, s>>>(a);
   }
-  if (a.bits == 2) nuq_quant_keys_kernel<2><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
-  else if (a.bits == 3) nuq_quant_keys_kernel<3><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
-  else nuq_quant_keys_kernel<4><<<dim3(jobs), dim3(kThreads), 0, s>>>(a);
+#define KVQ_QK(B_)                                                                   \
+  (a.qnorm ? nuq_quant_keys_kernel<B_, true><<<dim3(jobs), dim3(kThreads), 0, s>>>(a)      \
+           : nuq_quant_keys_kernel<B_, false><<<dim3(jobs), dim3(kThreads), 0, s>>>(a))
+  if (a.bits == 2) KVQ_QK(2);
+  else if (a.bits == 3) KVQ_QK(3);
+  else KVQ_QK(4);
+#undef KVQ_QK
   if (a.qnorm) nuq_qnorm_keys_kernel<<<dim3(grid1(bhd)), dim3(kThreads), 0, s>>>(a);
   return hipGetLastError();
 }
